@@ -1,0 +1,197 @@
+"""Float64 CPU oracle for paged MLA decode — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module. The product path (the C-ABI library and
+its Python binding) never calls it, and this module calls nothing of theirs.
+
+What it computes (plain reading of the pages):
+  * "[WIP][Attention] FlashAttn MLA", description: MLA's decode step is
+    computed as multi-query attention (MQA) — all query heads attend to a
+    single shared KV head.
+  * "[Attention] Blackwell FP8 MLA support with CUTLASS_MLA backend", review
+    thread (the failing kernel test): h_kv = 1, d = 576 (query/key width),
+    dv = 512 (value width), paged cache with page size 64, ``causal`` and
+    ``varlen`` options, cache dtype bf16 or ``torch.float8_e4m3fn``.
+  * Readings where the pages are silent (each listed in the design notes):
+    the 512 latent columns come first and the 64 rotary columns last; V is the
+    first 512 columns of the same cached row; k = decode(code) * kv_scale;
+    scores = softmax_scale * (q . k); lse is the natural log of the softmax
+    denominator including both scales; with s_q > 1 query tokens the causal
+    mask is bottom-right aligned (query token i sees keys [0, L - s_q + 1 + i));
+    a row that sees no key gets out = 0, lse = -inf.
+
+Everything is float64 and unblocked: one numpy matmul per (sequence, query
+token) for the scores and one for the weighted sum of values.
+Parity status: pinned (see tests/test_oracle.py) — brute force, closed forms,
+invariants and the OCP fp8 special values.
+"""
+from __future__ import annotations
+
+import math
+from typing import Tuple
+
+import numpy as np
+
+D_QK = 576
+D_V = 512
+
+
+# ---------------------------------------------------------------------------
+# element decoding
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 is the top half of an IEEE float32: widen exactly."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_value(code: int) -> float:
+    """Value of one OCP OFP8 E4M3 ("fn": finite, no infinities) code.
+
+    OCP 8-bit Floating Point Specification v1.0, E4M3: 1 sign bit, 4 exponent
+    bits with bias 7, 3 mantissa bits; exponent field 0 encodes subnormals
+    (2^-6 * m/8); S.1111.111 is NaN; there is no infinity, so S.1111.110 = 448
+    is the largest finite magnitude. (The pages name the dtype
+    ``torch.float8_e4m3fn`` for the cache.)
+    """
+    s = (code >> 7) & 1
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        mag = math.ldexp(m / 8.0, -6)
+    else:
+        mag = math.ldexp(1.0 + m / 8.0, e - 7)
+    return -mag if s else mag
+
+
+E4M3FN_TABLE = np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
+    return E4M3FN_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def decode_rows(raw: np.ndarray, kv_dtype: str) -> np.ndarray:
+    if kv_dtype == "bf16":
+        return bf16_bits_to_f64(raw)
+    if kv_dtype == "fp8":
+        return e4m3fn_to_f64(raw)
+    raise ValueError(kv_dtype)
+
+
+# ---------------------------------------------------------------------------
+# paging
+# ---------------------------------------------------------------------------
+
+def gather_keys(kv: np.ndarray, block_table_row: np.ndarray, seq_len: int,
+                kv_dtype: str, kv_scale: float) -> np.ndarray:
+    """Rows 0..seq_len-1 of one sequence, in token order, as float64.
+
+    Token t lives at page ``block_table_row[t // bs]``, slot ``t % bs``
+    (paged cache of the kernel test in the CUTLASS_MLA fp8 review thread).
+    """
+    bs = kv.shape[1]
+    out = np.empty((seq_len, D_QK), dtype=np.float64)
+    for t in range(0, seq_len, bs):
+        page = int(block_table_row[t // bs])
+        n = min(bs, seq_len - t)
+        out[t:t + n] = decode_rows(kv[page, :n], kv_dtype)
+    return out * np.float64(kv_scale)
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def attend(qrows: np.ndarray, keys: np.ndarray, softmax_scale: float
+           ) -> Tuple[np.ndarray, np.ndarray]:
+    """Softmax attention of query rows [n, 576] over keys [T, 576]; the value
+    of key t is keys[t, :512]. Returns (out [n, 512], lse [n]), natural log."""
+    n = qrows.shape[0]
+    T = keys.shape[0]
+    if T == 0:
+        return np.zeros((n, D_V)), np.full(n, -np.inf)
+    s = np.float64(softmax_scale) * (qrows @ keys.T)          # [n, T]
+    m = s.max(axis=1, keepdims=True)
+    w = np.exp(s - m)
+    den = w.sum(axis=1, keepdims=True)
+    out = (w @ keys[:, :D_V]) / den
+    lse = (m + np.log(den))[:, 0]
+    return out, lse
+
+
+def visible_keys(seq_len: int, s_q: int, i: int, causal: bool) -> int:
+    """Number of keys query token i (0-based among the s_q new tokens) sees.
+    The new tokens are the last s_q of the sequence (they are already in the
+    cache), so causal attention lets token i see keys [0, L - s_q + 1 + i)."""
+    if not causal:
+        return seq_len
+    return max(0, seq_len - s_q + 1 + i)
+
+
+def mla_decode(q_bits: np.ndarray, kv: np.ndarray, block_table: np.ndarray,
+               seq_lens: np.ndarray, s_q: int, softmax_scale: float,
+               kv_scale: float, kv_dtype: str, causal: bool = True
+               ) -> Tuple[np.ndarray, np.ndarray]:
+    """Paged MLA decode in its weight-absorbed MQA form.
+
+    q_bits: uint16 bf16 bits [B, s_q, H, 576]; kv: uint16 bf16 bits or uint8
+    e4m3fn codes [num_blocks, bs, 576]; block_table int32 [B, max_blocks];
+    seq_lens int32 [B]. Returns float64 out [B, s_q, H, 512], lse [B, s_q, H].
+    """
+    B, sq, H, d = q_bits.shape
+    assert sq == s_q and d == D_QK and kv.shape[2] == D_QK
+    out = np.zeros((B, s_q, H, D_V), dtype=np.float64)
+    lse = np.full((B, s_q, H), -np.inf, dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        keys = gather_keys(kv, block_table[b], L, kv_dtype, kv_scale)
+        for i in range(s_q):
+            n_vis = visible_keys(L, s_q, i, causal)
+            qrows = bf16_bits_to_f64(q_bits[b, i])
+            o, l = attend(qrows, keys[:n_vis], softmax_scale)
+            out[b, i] = o
+            lse[b, i] = l
+    return out, lse
+
+
+def combine_partials(o_parts: np.ndarray, lse_parts: np.ndarray
+                     ) -> Tuple[np.ndarray, np.ndarray]:
+    """Merge attention results computed over disjoint key chunks.
+
+    o_parts [S, ..., 512] are each chunk's normalised outputs and lse_parts
+    [S, ...] their log-sum-exps; a chunk that saw no key has lse = -inf and
+    weight 0. The merged lse is log(sum_s exp(lse_s)) and the merged output is
+    sum_s exp(lse_s - lse) * o_s (flash-decoding's split-KV reduction).
+    """
+    m = np.max(lse_parts, axis=0)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(lse_parts - m_safe)                            # [S, ...]
+    den = w.sum(axis=0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lse = np.where(den > 0, m_safe + np.log(den), -np.inf)
+        o = np.where((den > 0)[..., None],
+                     (w[..., None] * o_parts).sum(axis=0) / den[..., None], 0.0)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# comparison metrics
+# ---------------------------------------------------------------------------
+
+def cos_diff(x: np.ndarray, y: np.ndarray) -> float:
+    """The parity metric of the kernel test in the CUTLASS_MLA fp8 review
+    thread: 1 - 2*sum(x*y) / max(sum(x*x + y*y), 1e-12)."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    return float(1.0 - 2.0 * (x * y).sum() / max(float((x * x + y * y).sum()), 1e-12))
+
+
+def rel_fro(x: np.ndarray, ref: np.ndarray) -> float:
+    """Relative Frobenius error ||x - ref|| / ||ref||."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))

@@ -1,0 +1,375 @@
+"""Pins for the float64 oracle (CPU only).
+
+Each test checks the oracle against something other than itself: pure-Python
+brute force with an independent element decoder, closed forms, invariants of
+softmax attention, spec values of the fp8 format, torch's own fp8 cast, and
+the numbers the pages print for the kernel test. The last block plants
+plausible mistakes in copies of the oracle and checks that these pins fail.
+"""
+import json
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+from oracle import mla_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# helpers: tiny workloads and an independent brute force
+# ---------------------------------------------------------------------------
+
+def tiny(B=2, s_q=1, H=3, bs=8, dtype="bf16", lens=(5, 21), seed=11, causal=True, q_zero=False):
+    wl = mi.Workload("t", B, s_q, H, bs, dtype, "fixed", tuple(lens), causal=causal, seed=seed,
+                     spare_pages=3)
+    return mi.make_inputs(wl, q_zero=q_zero)
+
+
+def run_oracle(inp, **kw):
+    wl = inp.wl
+    args = dict(s_q=wl.s_q, softmax_scale=wl.softmax_scale, kv_scale=inp.kv_scale,
+                kv_dtype=wl.kv_dtype, causal=wl.causal)
+    args.update(kw)
+    return orc.mla_decode(inp.q_bits, inp.kv, inp.block_table, inp.seq_lens, **args)
+
+
+def _bf16_scalar(bits):
+    return struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
+
+
+_TORCH_FP8 = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn) \
+    .to(torch.float64).numpy()
+
+
+def brute_force(inp, softmax_scale=None, kv_scale=None):
+    """Dense attention with Python loops: gathers each key through the block
+    table, decodes elements with struct (bf16) or torch's fp8 cast, and takes
+    lse = log(sum(exp(s))) with no max shift."""
+    wl = inp.wl
+    sc = wl.softmax_scale if softmax_scale is None else softmax_scale
+    ks = inp.kv_scale if kv_scale is None else kv_scale
+    B, s_q, H = wl.batch, wl.s_q, wl.heads
+    bs = wl.block_size
+    out = np.zeros((B, s_q, H, 512))
+    lse = np.zeros((B, s_q, H))
+
+    def dec(x):
+        return _bf16_scalar(x) if wl.kv_dtype == "bf16" else float(_TORCH_FP8[int(x)])
+
+    for b in range(B):
+        L = int(inp.seq_lens[b])
+        keys = []
+        for t in range(L):
+            page = int(inp.block_table[b][t // bs])
+            keys.append([dec(x) * ks for x in inp.kv[page][t % bs]])
+        for i in range(s_q):
+            n = (L - s_q + 1 + i) if wl.causal else L
+            for h in range(H):
+                q = [_bf16_scalar(x) for x in inp.q_bits[b][i][h]]
+                ex = []
+                for t in range(n):
+                    s = 0.0
+                    for j in range(576):
+                        s += q[j] * keys[t][j]
+                    ex.append(math.exp(sc * s))
+                den = sum(ex)
+                lse[b, i, h] = math.log(den) if n > 0 else -math.inf
+                for d in range(512):
+                    acc = 0.0
+                    for t in range(n):
+                        acc += ex[t] * keys[t][d]
+                    out[b, i, h, d] = acc / den if n > 0 else 0.0
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# element decoding
+# ---------------------------------------------------------------------------
+
+def test_bf16_widening_matches_torch():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 1 << 16, size=20000, dtype=np.uint32).astype(np.uint16)
+    exp_field = (bits >> 7) & 0xFF
+    bits = bits[exp_field != 0xFF]                     # drop inf/NaN
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(orc.bf16_bits_to_f64(bits), ref)
+
+
+def test_e4m3fn_all_codes_match_torch_cast():
+    tab = orc.E4M3FN_TABLE
+    nan = np.isnan(tab)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.isnan(_TORCH_FP8[0x7F]) and np.isnan(_TORCH_FP8[0xFF])
+    np.testing.assert_array_equal(tab[~nan], _TORCH_FP8[~nan])
+    assert np.isfinite(tab[~nan]).all()           # e4m3fn has no infinities
+
+
+def test_e4m3fn_spec_special_values():
+    with open(os.path.join(GOLDEN, "ocp_e4m3fn_special_values.json")) as f:
+        g = json.load(f)
+    for code, val in g["values"].items():
+        got = orc.e4m3fn_value(int(code, 16))
+        assert got == val and math.copysign(1.0, got) == math.copysign(1.0, val), code
+    for code in g["nan_codes"]:
+        assert math.isnan(orc.e4m3fn_value(int(code, 16)))
+
+
+# ---------------------------------------------------------------------------
+# oracle vs brute force
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,s_q,causal,lens", [
+    ("bf16", 1, True, (5, 21)),
+    ("fp8", 1, True, (1, 17)),
+    ("bf16", 3, True, (4, 19)),
+    ("fp8", 2, False, (9, 3)),
+])
+def test_oracle_matches_brute_force(dtype, s_q, causal, lens):
+    inp = tiny(s_q=s_q, dtype=dtype, lens=lens, causal=causal, seed=7 + s_q)
+    o, l = run_oracle(inp)
+    ob, lb = brute_force(inp)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, lb, rtol=0, atol=1e-12)
+
+
+def test_oracle_matches_brute_force_page64():
+    inp = tiny(B=1, H=2, bs=64, lens=(70,), seed=3)
+    o, l = run_oracle(inp)
+    ob, lb = brute_force(inp)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, lb, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_single_token_returns_its_latent_row(dtype):
+    inp = tiny(B=3, H=4, dtype=dtype, lens=(1, 1, 1), seed=5)
+    o, l = run_oracle(inp)
+    bs = inp.wl.block_size
+    for b in range(3):
+        page = inp.block_table[b, 0]
+        k = orc.decode_rows(inp.kv[page, 0], dtype) * inp.kv_scale
+        np.testing.assert_array_equal(o[b, 0], np.broadcast_to(k[:512], (4, 512)))
+        q = orc.bf16_bits_to_f64(inp.q_bits[b, 0])
+        s = inp.wl.softmax_scale * (q @ k)
+        np.testing.assert_allclose(l[b, 0], s, rtol=0, atol=1e-12)
+    assert bs == 8
+
+
+def test_uniform_scores_give_mean_and_log_count():
+    inp = tiny(B=2, H=2, lens=(13, 40), q_zero=True, seed=2)
+    o, l = run_oracle(inp)
+    for b, L in enumerate(inp.seq_lens):
+        keys = np.stack([orc.decode_rows(inp.kv[inp.block_table[b, t // 8], t % 8], "bf16")
+                         for t in range(L)])
+        np.testing.assert_allclose(o[b, 0], np.broadcast_to(keys[:, :512].mean(0), (2, 512)),
+                                   rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l[b, 0], math.log(L), rtol=0, atol=1e-14)
+
+
+def test_softmax_scale_to_zero_is_uniform():
+    inp = tiny(B=1, H=2, lens=(30,), seed=9)
+    o0, l0 = run_oracle(inp, softmax_scale=0.0)
+    qz = tiny(B=1, H=2, lens=(30,), seed=9, q_zero=True)
+    o1, l1 = run_oracle(qz)
+    np.testing.assert_allclose(o0, o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l0, np.log(30.0), rtol=0, atol=1e-14)
+
+
+def test_empty_sequence_gives_zero_and_minus_inf():
+    inp = tiny(B=2, s_q=1, lens=(0, 6), seed=4)
+    o, l = run_oracle(inp)
+    assert (o[0] == 0).all() and np.isneginf(l[0]).all()
+    assert np.isfinite(l[1]).all()
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_page_permutation_leaves_result_bit_identical(dtype):
+    inp = tiny(B=3, H=4, dtype=dtype, lens=(17, 64, 3), seed=21)
+    o, l = run_oracle(inp)
+    for s in range(3):
+        p = mi.permute_pages(inp, seed=100 + s)
+        assert not np.array_equal(p.block_table, inp.block_table)
+        o2, l2 = run_oracle(p)
+        np.testing.assert_array_equal(o, o2)
+        np.testing.assert_array_equal(l, l2)
+
+
+def test_split_combine_equals_unsplit():
+    inp = tiny(B=1, H=5, lens=(150,), bs=16, seed=13)
+    keys = orc.gather_keys(inp.kv, inp.block_table[0], 150, "bf16", 1.0)
+    q = orc.bf16_bits_to_f64(inp.q_bits[0, 0])
+    sc = inp.wl.softmax_scale
+    o_ref, l_ref = orc.attend(q, keys, sc)
+    rng = np.random.default_rng(1)
+    for trial in range(5):
+        cuts = np.sort(rng.choice(np.arange(1, 150), size=trial + 1, replace=False))
+        edges = [0, *cuts.tolist(), 150]
+        parts = [orc.attend(q, keys[a:b], sc) for a, b in zip(edges[:-1], edges[1:])]
+        # an empty chunk must carry weight 0
+        parts.append(orc.attend(q, keys[:0], sc))
+        o, l = orc.combine_partials(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l, l_ref, rtol=0, atol=1e-12)
+
+
+def test_combine_of_all_empty_parts():
+    o, l = orc.combine_partials(np.zeros((3, 2, 512)), np.full((3, 2), -np.inf))
+    assert (o == 0).all() and np.isneginf(l).all()
+
+
+def test_causal_rows_match_per_token_decode():
+    s_q = 4
+    inp = tiny(B=2, s_q=s_q, H=3, lens=(9, 26), seed=31)
+    o, l = run_oracle(inp)
+    for i in range(s_q):
+        lens_i = inp.seq_lens - s_q + 1 + i
+        one = mi.Inputs(mi.Workload("t", 2, 1, 3, 8, "bf16", "fixed", (1, 1)),
+                        np.ascontiguousarray(inp.q_bits[:, i:i + 1]), inp.kv, inp.kv_scale,
+                        inp.block_table, lens_i.astype(np.int32))
+        o1, l1 = run_oracle(one, s_q=1)
+        np.testing.assert_array_equal(o[:, i], o1[:, 0])
+        np.testing.assert_array_equal(l[:, i], l1[:, 0])
+    # and the rows really differ (the mask matters)
+    assert not np.allclose(o[:, 0], o[:, -1])
+
+
+def test_duplicating_every_key_adds_log2():
+    inp = tiny(B=1, H=3, lens=(11,), bs=4, seed=17)
+    o, l = run_oracle(inp)
+    keys = orc.gather_keys(inp.kv, inp.block_table[0], 11, "bf16", 1.0)
+    dup = np.repeat(keys, 2, axis=0)
+    q = orc.bf16_bits_to_f64(inp.q_bits[0, 0])
+    o2, l2 = orc.attend(q, dup, inp.wl.softmax_scale)
+    np.testing.assert_allclose(o2, o[0, 0], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l[0, 0] + math.log(2.0), rtol=0, atol=1e-13)
+
+
+def test_lse_and_output_bounds():
+    inp = tiny(B=2, s_q=2, H=4, lens=(33, 50), seed=23)
+    o, l = run_oracle(inp)
+    sc = inp.wl.softmax_scale
+    for b in range(2):
+        L = int(inp.seq_lens[b])
+        keys = orc.gather_keys(inp.kv, inp.block_table[b], L, "bf16", 1.0)
+        for i in range(2):
+            n = L - 2 + 1 + i
+            q = orc.bf16_bits_to_f64(inp.q_bits[b, i])
+            m = (sc * (q @ keys[:n].T)).max(axis=1)
+            assert (m <= l[b, i] + 1e-12).all() and (l[b, i] <= m + math.log(n) + 1e-12).all()
+            lo, hi = keys[:n, :512].min(0), keys[:n, :512].max(0)
+            assert (o[b, i] >= lo - 1e-12).all() and (o[b, i] <= hi + 1e-12).all()
+
+
+def test_kv_scale_scales_keys_and_values():
+    inp = tiny(B=2, H=2, dtype="fp8", lens=(12, 20), seed=29)
+    c = 0.37
+    o1, l1 = run_oracle(inp, kv_scale=c)
+    o2, l2 = run_oracle(inp, kv_scale=1.0, softmax_scale=inp.wl.softmax_scale * c)
+    np.testing.assert_allclose(o1, c * o2, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-11)
+
+
+def test_poisoned_rows_are_never_read():
+    inp = tiny(B=2, H=2, lens=(5, 13), seed=41)
+    assert np.isnan(orc.bf16_bits_to_f64(inp.kv)).any()
+    o, l = run_oracle(inp)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
+# ---------------------------------------------------------------------------
+# the pages' printed numbers
+# ---------------------------------------------------------------------------
+
+def test_cos_diff_metric_and_failure_signature():
+    with open(os.path.join(GOLDEN, "kernel_test_case.json")) as f:
+        g = json.load(f)
+    x = np.random.default_rng(0).standard_normal((4, 512))
+    assert orc.cos_diff(x, x) == pytest.approx(0.0, abs=1e-15)
+    # an all-zero (unwritten) output gives exactly the value the page prints
+    assert orc.cos_diff(x, np.zeros_like(x)) == g["failure_cos_diff"]
+    assert orc.cos_diff(x, -x) == pytest.approx(2.0)
+    # a relative error e gives cos_diff ~ e^2/2, far under the page's fp8 bar at 1e-2
+    y = x + 1e-2 * np.linalg.norm(x) / math.sqrt(x.size) * np.random.default_rng(1).standard_normal(x.shape)
+    assert orc.cos_diff(x, y) < g["fp8_cos_diff_threshold"]
+
+
+def test_workload_matches_printed_kernel_test_case():
+    with open(os.path.join(GOLDEN, "kernel_test_case.json")) as f:
+        c = json.load(f)["case"]
+    wl = mi.WORKLOADS["b128_h16_L4096_fp8"]
+    assert (wl.batch, wl.s_q, wl.heads, wl.block_size, wl.causal) == \
+        (c["b"], c["s_q"], c["h_q"], c["block_size"], c["causal"])
+    assert wl.lens == "fixed" and wl.lens_arg == (c["mean_sk"],)
+    assert (orc.D_QK, orc.D_V, c["h_kv"], wl.kv_dtype) == (c["d"], c["dv"], 1, "fp8")
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each plausible oracle bug must trip at least one pin
+# ---------------------------------------------------------------------------
+
+_REAL_ATTEND = orc.attend
+
+
+def _attend_no_rope(q, k, sc):
+    o, l = _REAL_ATTEND(q[:, :512], np.ascontiguousarray(k[:, :512]), sc)
+    if k.shape[0]:
+        s = sc * (q[:, :512] @ k[:, :512].T)
+        w = np.exp(s - s.max(1, keepdims=True))
+        o = (w @ k[:, :512]) / w.sum(1, keepdims=True)
+    return o, l
+
+
+def _attend_rope_as_value(q, k, sc):
+    kk = np.concatenate([k[:, 64:], k[:, :64]], axis=1)
+    o, l = _REAL_ATTEND(q, k, sc)
+    if k.shape[0] == 0:
+        return o, l
+    s = sc * (q @ k.T)
+    w = np.exp(s - s.max(1, keepdims=True))
+    return (w @ kk[:, :512]) / w.sum(1, keepdims=True), l
+
+
+def _attend_log2_lse(q, k, sc):
+    o, l = _REAL_ATTEND(q, k, sc)
+    return o, l / math.log(2.0)
+
+
+@pytest.mark.parametrize("mutant", ["no_rope", "rope_as_value", "log2_lse", "causal_off_by_one",
+                                    "kv_scale_values_only"])
+def test_planted_mistakes_are_caught(monkeypatch, mutant):
+    inp = tiny(s_q=2, lens=(6, 11), seed=8, dtype="fp8")
+    ob, lb = brute_force(inp)
+    if mutant == "no_rope":
+        monkeypatch.setattr(orc, "attend", _attend_no_rope)
+    elif mutant == "rope_as_value":
+        monkeypatch.setattr(orc, "attend", _attend_rope_as_value)
+    elif mutant == "log2_lse":
+        monkeypatch.setattr(orc, "attend", _attend_log2_lse)
+    elif mutant == "causal_off_by_one":
+        monkeypatch.setattr(orc, "visible_keys",
+                            lambda L, s_q, i, causal: max(0, L - s_q + i) if causal else L)
+    elif mutant == "kv_scale_values_only":
+        real = orc.gather_keys
+
+        def g(kv, bt, L, dt, ks):
+            k = real(kv, bt, L, dt, 1.0)
+            k[:, :512] *= ks
+            return k
+        monkeypatch.setattr(orc, "gather_keys", g)
+    o, l = run_oracle(inp)
+    caught = not (np.allclose(o, ob, rtol=0, atol=1e-12) and np.allclose(l, lb, rtol=0, atol=1e-12))
+    assert caught, mutant
