@@ -1,0 +1,278 @@
+"""Benchmark of paged MLA decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+
+One step is one ``mla_decode`` call — split planner, decode kernel, LSE
+combine — over one synthetic batch already resident in HBM. The default
+workload is the kernel-test shape of the CUTLASS_MLA fp8 review thread in bf16
+(B=128, s_q=1, H=16, 4096-token contexts, page size 64). Rank 0 prints one
+JSON line with the whole-job algorithmic HBM throughput (value, GB/s), the
+decode kernel's roofline fraction measured with HIP events on the stream it
+runs on, and the float64 CPU oracle timed on a bounded sample of the same
+workload (``cpu_baseline``).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mla_inputs as mi  # noqa: E402
+
+DEFAULT_WORKLOAD = "b128_h16_L4096_bf16"
+METRIC = "paged MLA decode: HBM GB/s + TFLOP/s (fraction of roofline), seqs/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2516.6    # dense bf16 MFMA
+KERNEL_SRC = os.path.join(ROOT, "mla_paged_decode_04_amd", "csrc", "mla_decode.hip")
+
+
+def algorithmic_bytes(inp) -> int:
+    """q, every cached row a sequence reads (once), its block-table entries,
+    seq_lens, out and lse."""
+    wl = inp.wl
+    B, s_q, H, bs = wl.batch, wl.s_q, wl.heads, wl.block_size
+    row = 576 * (2 if wl.kv_dtype == "bf16" else 1)
+    lens = inp.seq_lens.astype(np.int64)
+    return int(lens.sum() * row + ((lens + bs - 1) // bs).sum() * 4 + B * 4
+               + B * s_q * H * (576 * 2 + 512 * 2 + 4))
+
+
+def algorithmic_flops(inp) -> int:
+    """2 * (576 + 512) per (query row, visible key): q.k and p*v."""
+    wl = inp.wl
+    lens = inp.seq_lens.astype(np.int64)
+    vis = 0
+    for i in range(wl.s_q):
+        v = lens - wl.s_q + 1 + i if wl.causal else lens
+        vis += int(np.clip(v, 0, None).sum())
+    return 2 * wl.heads * (576 + 512) * vis
+
+
+def to_device(inp, torch):
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(inp.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    if inp.wl.kv_dtype == "bf16":
+        kv = torch.from_numpy(inp.kv.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        kv = torch.from_numpy(inp.kv).to(dev).view(torch.float8_e4m3fn)
+    return q, kv, torch.from_numpy(inp.block_table).to(dev), torch.from_numpy(inp.seq_lens).to(dev)
+
+
+def source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, launch_bytes_expected: int):
+    """HBM bytes per decode-kernel launch from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"mla_decode_fwd_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_b or m_src.group(1) != source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(inp, budget_s: float = 12.0):
+    """Float64 oracle on the host cores over the same workload: whole batches
+    until about `budget_s` seconds of CPU work; throughput in GB/s of
+    algorithmic bytes so that it reads in the unit of `value`."""
+    from oracle import mla_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:   # pragma: no cover
+        cores = os.cpu_count() or 1
+    wl = inp.wl
+    # a bounded sample: the first n sequences of the batch, as many passes as fit
+    n = wl.batch
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        orc.mla_decode(inp.q_bits[:n], inp.kv, inp.block_table[:n], inp.seq_lens[:n], wl.s_q,
+                       wl.softmax_scale, inp.kv_scale, wl.kv_dtype, wl.causal)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or passes >= 20:
+            break
+    frac = n / wl.batch
+    gbs = algorithmic_bytes(inp) * frac * passes / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{passes} pass(es) over all {n} sequences of the workload, "
+                      f"float64 numpy oracle, {el:.1f} s wall",
+            "seqs_per_s": round(n * passes / el, 3)}
+
+
+def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, flush: bool):
+    import torch
+    import mla_paged_decode_04_amd as mla
+
+    wl = mi.WORKLOADS[name]
+    inp = mi.make_inputs(wl)
+    q, kv, bt, sl = to_device(inp, torch)
+    B, s_q, H = wl.batch, wl.s_q, wl.heads
+    out = torch.empty((B, s_q, H, 512), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q.device)
+    desc = mla.make_desc(B, H, wl.block_size, kv.shape[0], bt.shape[1],
+                         mla.MLA_DTYPE_BF16 if wl.kv_dtype == "bf16" else mla.MLA_DTYPE_FP8_E4M3FN,
+                         wl.causal)
+    ws_bytes = mla.workspace_size(s_q, desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    lib = mla.library()
+    stream = torch.cuda.current_stream()
+    import ctypes
+    args = (q.data_ptr(), kv.data_ptr(), bt.data_ptr(), sl.data_ptr(), s_q,
+            float(wl.softmax_scale), float(inp.kv_scale), out.data_ptr(), lse.data_ptr(),
+            ctypes.byref(desc), ws.data_ptr(), ws_bytes, stream.cuda_stream)
+    scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=q.device) if flush else None
+
+    def step():
+        st = lib.mla_decode(*args)
+        if st != 0:
+            raise RuntimeError(f"mla_decode status {st}")
+
+    def fwd():
+        st = lib.mla_decode_fwd_only(*args)
+        if st != 0:
+            raise RuntimeError(f"mla_decode_fwd_only status {st}")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole steps: K back-to-back calls bracketed by events and synchronisation
+    if flush:
+        per = []
+        for _ in range(steps):
+            scratch.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1))
+        ms_step = float(np.median(per))
+        wall_ms = float(np.sum(per))
+    else:
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        ms_step = e0.elapsed_time(e1) / steps
+
+    # the decode kernel alone, on the same stream (plan left in the workspace)
+    fwd_ms = []
+    for _ in range(steps):
+        if flush:
+            scratch.fill_(1.0)
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        fwd()
+        f1.record(stream)
+        if flush:
+            torch.cuda.synchronize()
+        fwd_ms.append((f0, f1))
+    torch.cuda.synchronize()
+    fwd_t = [a.elapsed_time(b) for a, b in fwd_ms]
+    fwd_ms_avg = float(np.mean(fwd_t))
+    # leave a correct result behind (fwd-only overwrote split partials only)
+    step()
+    torch.cuda.synchronize()
+
+    nbytes = algorithmic_bytes(inp)
+    nflops = algorithmic_flops(inp)
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    tfs = nflops / (ms_step * 1e-3) / 1e12
+    fwd_gbs = nbytes / (fwd_ms_avg * 1e-3) / 1e9
+    fwd_tfs = nflops / (fwd_ms_avg * 1e-3) / 1e12
+    hbm_bound = nbytes / (HBM_PEAK_GBS * 1e9) >= nflops / (MFMA_BF16_PEAK_TFS * 1e12)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(fwd_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(fwd_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(fwd_tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(fwd_tfs / MFMA_BF16_PEAK_TFS, 4)}
+    traffic = traffic_from_profile(name, nbytes)
+    roof["traffic"] = traffic
+    roof["kernel"] = "mla_decode_fwd"
+    roof["kernel_ms"] = round(fwd_ms_avg, 5)
+    roof["hbm_frac"] = round(fwd_gbs / HBM_PEAK_GBS, 4)
+    roof["mfma_frac"] = round(fwd_tfs / MFMA_BF16_PEAK_TFS, 4)
+
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "s_q": s_q, "heads": H,
+                   "seq_lens": wl.lens if wl.lens != "fixed" else list(set(wl.lens_arg)),
+                   "seq_len_range": list(wl.lens_arg), "block_size": wl.block_size,
+                   "kv_dtype": wl.kv_dtype, "d_qk": 576, "d_v": 512, "causal": wl.causal,
+                   "parallelism": "single_gpu"},
+        "tflops": round(tfs, 3),
+        "seqs_per_s": round(B / (ms_step * 1e-3), 1),
+        "algorithmic_bytes": nbytes,
+        "algorithmic_flops": nflops,
+        "wall_ms_timed": round(wall_ms, 3),
+        "mall_flush": flush,
+        "roofline": roof,
+    }
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(inp)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(mi.WORKLOADS))
+    ap.add_argument("--all", action="store_true", help="one line per workload")
+    ap.add_argument("--flush", action="store_true",
+                    help="evict the 256 MB Infinity Cache before every timed call")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    names = list(mi.WORKLOADS) if a.all else [a.workload]
+    for n in names:
+        res = bench_one(n, a.steps, a.warmup, with_cpu=not a.no_cpu and n == names[0],
+                        flush=a.flush)
+        print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

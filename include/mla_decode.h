@@ -1,0 +1,136 @@
+/*
+ * mla_decode.h — C ABI of an MI355X (gfx950) paged MLA decode library.
+ *
+ * The operation (plain reading of the pages):
+ *   "[WIP][Attention] FlashAttn MLA", description: MLA's decode step is
+ *   computed as multi-query attention — every query head attends to one
+ *   shared latent KV head.
+ *   "[Attention] Blackwell FP8 MLA support with CUTLASS_MLA backend", review
+ *   thread (the failing kernel test): h_kv = 1, d = 576, dv = 512, a paged
+ *   cache (page size 64 in the test; "[NVIDIA] Add Cutlass MLA backend" serves
+ *   DeepSeek-V3 with --block-size=128), causal and varlen options, the cache in
+ *   bf16 or torch.float8_e4m3fn.
+ *
+ * For sequence b with L = seq_lens[b] cached tokens (the s_q new tokens are
+ * the last s_q of them), query token i in [0, s_q) and head h in [0, H):
+ *   Leff    = causal ? L - s_q + 1 + i : L                (keys it may see)
+ *   k_t     = decode(kv_cache[block_table[b][t / bs]][t % bs][0..575]) * kv_scale
+ *   s_t     = softmax_scale * dot(q[b][i][h][0..575], k_t)          t < Leff
+ *   out[b][i][h][0..511] = sum_t softmax(s)_t * k_t[0..511]   (V = latent part)
+ *   lse[b][i][h]         = ln(sum_t exp(s_t))                  (natural log)
+ * A row that sees no key gets out = 0 and lse = -inf.
+ *
+ * Every entry point is safe to call without a GPU as long as it returns an
+ * error before launching (argument checks never touch the device).
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_D_QK 576          /* 512 latent + 64 rotary columns per cached row */
+#define MLA_D_V 512           /* the latent part of the row serves as V */
+#define MLA_MAX_HEADS 128
+#define MLA_MAX_SQ 16
+#define MLA_ABI_VERSION 1
+
+typedef enum mla_status {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misalignment, non-finite scale */
+    MLA_ERR_UNSUPPORTED = 2,        /* heads, s_q, block size or dtype outside the supported set */
+    MLA_ERR_WORKSPACE_TOO_SMALL = 3,
+    MLA_ERR_HIP = 4                 /* a HIP launch or query failed */
+} mla_status_t;
+
+typedef enum mla_dtype {
+    MLA_DTYPE_BF16 = 0,
+    MLA_DTYPE_FP8_E4M3FN = 1        /* OCP OFP8 E4M3: bias 7, max 448, no inf */
+} mla_dtype_t;
+
+/* Problem description (the kernel test's parameter set, minus the fixed
+ * h_kv = 1, d = 576, dv = 512). */
+typedef struct mla_decode_desc {
+    int32_t batch;               /* B >= 0 (B == 0 is a no-op) */
+    int32_t num_heads;           /* H, 1..128 */
+    int32_t block_size;          /* bs, 64 or 128 tokens per page */
+    int32_t num_blocks;          /* pages in kv_cache, >= 1 */
+    int32_t max_blocks_per_seq;  /* columns of block_table, >= 1 */
+    int32_t kv_dtype;            /* mla_dtype_t */
+    int32_t causal;              /* 0 or 1 */
+    int32_t split_keys;          /* 0: automatic split-KV; else every sequence is cut into
+                                    chunks of this many keys (multiple of 64) */
+} mla_decode_desc_t;
+
+/* Bytes of device workspace mla_decode needs for this problem (host-only
+ * arithmetic; returns 0 for an invalid or unsupported description). */
+size_t mla_decode_workspace_size(int32_t s_q, const mla_decode_desc_t* desc);
+
+/*
+ * Paged MLA decode.
+ *
+ * All pointers are device pointers (HIP), row-major and contiguous:
+ *   q            bf16  [B, s_q, H, 576]                16-byte aligned
+ *   kv_cache     bf16 or e4m3fn [num_blocks, bs, 576]  16-byte aligned
+ *   block_table  int32 [B, max_blocks_per_seq]; entries past ceil(L/bs) are never read
+ *   seq_lens     int32 [B], 0 <= L <= max_blocks_per_seq * bs (values outside are clamped
+ *                and flagged in the workspace header)
+ *   out          bf16  [B, s_q, H, 512]                16-byte aligned
+ *   lse          fp32  [B, s_q, H], natural log; may be NULL
+ *   workspace    >= mla_decode_workspace_size() bytes, 256-byte aligned
+ *   stream       a hipStream_t (NULL = the default stream)
+ * softmax_scale and kv_scale must be finite and > 0; pass kv_scale = 1 for a
+ * bf16 cache (it is applied either way: k = decode(code) * kv_scale).
+ *
+ * Ownership: the caller owns every buffer; nothing is allocated or retained.
+ * Every element of out (and lse) is written, so they need no initialisation.
+ * Inputs are not modified. The work is enqueued on `stream` with no host
+ * synchronisation; calls that share a workspace must be ordered on a stream.
+ * Errors: on any MLA_ERR_* other than MLA_ERR_HIP nothing is launched and
+ * nothing is written.
+ *
+ * Workspace layout after a call (for inspection by tests): int32 header
+ * [0] work items, [1] chunk keys, [2] partial slots, [3] 1 if a seq_len was
+ * clamped; at byte 256 the work items, 8 x int32 each:
+ * {b, row_group, key_begin, key_end, partial_slot (-1 = written directly), 0, 0, 0}.
+ */
+mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+                        const int32_t* seq_lens, int32_t s_q, float softmax_scale,
+                        float kv_scale, void* out, float* lse, const mla_decode_desc_t* desc,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Launches only the decode kernel (no planner, no combine), for timing that
+ * kernel on its own: `workspace` must already hold the plan of a preceding
+ * mla_decode or mla_decode_plan call with the same seq_lens and description.
+ * Rows of work items that were split get their fp32 partials in the workspace
+ * instead of out/lse. Same arguments, checks and errors as mla_decode. */
+mla_status_t mla_decode_fwd_only(const void* q, const void* kv_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t s_q, float softmax_scale,
+                                 float kv_scale, void* out, float* lse,
+                                 const mla_decode_desc_t* desc, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Runs only the split planner (the first kernel mla_decode launches) and
+ * leaves the header and work items in the workspace as described above. */
+mla_status_t mla_decode_plan(const int32_t* seq_lens, int32_t s_q, const mla_decode_desc_t* desc,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host mirror of the planner: fills items[8 * n] for host seq_lens; returns the
+ * number of items, or -1 if the description is invalid or max_items is short.
+ * Also reports rows per work item and the chunk length chosen. */
+int32_t mla_plan_host(const int32_t* seq_lens_host, int32_t s_q, const mla_decode_desc_t* desc,
+                      int32_t* items, int32_t max_items, int32_t* rows_per_item,
+                      int32_t* chunk_keys);
+
+const char* mla_status_string(mla_status_t status);
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,214 @@
+"""Paged MLA decode on MI355X (gfx950): thin Python binding over the C ABI.
+
+Every step of the computation runs in the HIP kernels of
+``libmla_decode.so``; this module only checks tensors, allocates outputs and
+workspace with torch, and passes raw device pointers plus the current torch
+stream. If the library is missing the call raises — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["mla_decode", "mla_decode_plan", "mla_plan_host", "workspace_size", "library",
+           "MlaError", "D_QK", "D_V", "LIB_PATH"]
+
+D_QK = 576
+D_V = 512
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_decode.so")
+
+MLA_DTYPE_BF16 = 0
+MLA_DTYPE_FP8_E4M3FN = 1
+ITEM_INTS = 8
+HEADER_INTS = 64
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what} failed: {_status_string(status)} ({status})")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("split_keys", ctypes.c_int32),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library() -> ctypes.CDLL:
+    """Load the in-tree HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m mla_paged_decode_04_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    pdesc = ctypes.POINTER(Desc)
+    lib.mla_decode_workspace_size.argtypes = [i32, pdesc]
+    lib.mla_decode_workspace_size.restype = sz
+    lib.mla_decode.argtypes = [vp, vp, vp, vp, i32, f32, f32, vp, vp, pdesc, vp, sz, vp]
+    lib.mla_decode.restype = ctypes.c_int
+    lib.mla_decode_fwd_only.argtypes = [vp, vp, vp, vp, i32, f32, f32, vp, vp, pdesc, vp, sz, vp]
+    lib.mla_decode_fwd_only.restype = ctypes.c_int
+    lib.mla_decode_plan.argtypes = [vp, i32, pdesc, vp, sz, vp]
+    lib.mla_decode_plan.restype = ctypes.c_int
+    lib.mla_plan_host.argtypes = [vp, i32, pdesc, vp, i32, vp, vp]
+    lib.mla_plan_host.restype = i32
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_abi_version.argtypes = []
+    lib.mla_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return library().mla_status_string(status).decode()
+    except Exception:  # pragma: no cover - only when the library itself is missing
+        return "?"
+
+
+def make_desc(batch: int, num_heads: int, block_size: int, num_blocks: int,
+              max_blocks_per_seq: int, kv_dtype: int, causal: bool, split_keys: int = 0) -> Desc:
+    return Desc(batch, num_heads, block_size, num_blocks, max_blocks_per_seq, kv_dtype,
+                int(bool(causal)), split_keys)
+
+
+def workspace_size(s_q: int, desc: Desc) -> int:
+    return int(library().mla_decode_workspace_size(s_q, ctypes.byref(desc)))
+
+
+def _kv_dtype_code(kv: torch.Tensor) -> int:
+    if kv.dtype == torch.bfloat16:
+        return MLA_DTYPE_BF16
+    if kv.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return MLA_DTYPE_FP8_E4M3FN
+    raise ValueError(f"kv_cache dtype {kv.dtype} is not bf16 or float8_e4m3fn")
+
+
+def _check(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+               seq_lens: torch.Tensor, softmax_scale: float, kv_scale: float = 1.0,
+               causal: bool = True, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               split_keys: int = 0, want_lse: bool = True
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Paged MLA decode (weight-absorbed MQA form).
+
+    q [B, s_q, H, 576] bf16; kv_cache [num_blocks, bs, 576] (or [num_blocks,
+    bs, 1, 576]) bf16 or float8_e4m3fn; block_table [B, max_blocks] int32;
+    seq_lens [B] int32. Returns out [B, s_q, H, 512] bf16 and lse [B, s_q, H]
+    fp32 (natural log), computed on the current torch stream.
+    """
+    if kv_cache.dim() == 4 and kv_cache.shape[2] == 1:
+        kv_cache = kv_cache.view(kv_cache.shape[0], kv_cache.shape[1], kv_cache.shape[3])
+    _check(q, "q", torch.bfloat16, 4)
+    _check(kv_cache, "kv_cache", None, 3)
+    _check(block_table, "block_table", torch.int32, 2)
+    _check(seq_lens, "seq_lens", torch.int32, 1)
+    B, s_q, H, d = q.shape
+    nb, bs, dk = kv_cache.shape
+    if d != D_QK or dk != D_QK:
+        raise ValueError(f"q and kv_cache rows must be {D_QK} wide")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table and seq_lens must have one row per sequence")
+    dev = q.device
+    for name, t in (("kv_cache", kv_cache), ("block_table", block_table), ("seq_lens", seq_lens)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, q on {dev}")
+    desc = make_desc(B, H, bs, nb, block_table.shape[1], _kv_dtype_code(kv_cache), causal,
+                     split_keys)
+    if out is None:
+        out = torch.empty((B, s_q, H, D_V), dtype=torch.bfloat16, device=dev)
+    else:
+        _check(out, "out", torch.bfloat16, 4)
+        if tuple(out.shape) != (B, s_q, H, D_V):
+            raise ValueError(f"out must be {(B, s_q, H, D_V)}")
+    if lse is None and want_lse:
+        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, s_q, H):
+            raise ValueError(f"lse must be {(B, s_q, H)}")
+    lib = library()
+    need = int(lib.mla_decode_workspace_size(s_q, ctypes.byref(desc)))
+    if need == 0 and B > 0:
+        raise MlaError(2, f"mla_decode (B={B}, s_q={s_q}, H={H}, bs={bs})")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.mla_decode(q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
+                        seq_lens.data_ptr(), s_q, float(softmax_scale), float(kv_scale),
+                        out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                        ctypes.byref(desc), workspace.data_ptr(), workspace.numel(), stream)
+    if st != 0:
+        raise MlaError(st, "mla_decode")
+    return out, lse
+
+
+def mla_decode_plan(seq_lens: torch.Tensor, s_q: int, num_heads: int, block_size: int,
+                    max_blocks_per_seq: int, num_blocks: int = 1, causal: bool = True,
+                    split_keys: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Run only the device split planner; returns (header int32[4], items int32[n, 8])."""
+    _check(seq_lens, "seq_lens", torch.int32, 1)
+    desc = make_desc(seq_lens.shape[0], num_heads, block_size, num_blocks, max_blocks_per_seq,
+                     MLA_DTYPE_BF16, causal, split_keys)
+    lib = library()
+    need = int(lib.mla_decode_workspace_size(s_q, ctypes.byref(desc)))
+    if need == 0:
+        raise MlaError(2, "mla_decode_plan")
+    ws = torch.empty(need, dtype=torch.uint8, device=seq_lens.device)
+    st = lib.mla_decode_plan(seq_lens.data_ptr(), s_q, ctypes.byref(desc), ws.data_ptr(), need,
+                             torch.cuda.current_stream(seq_lens.device).cuda_stream)
+    if st != 0:
+        raise MlaError(st, "mla_decode_plan")
+    ints = ws.view(torch.int32)
+    header = ints[:4].clone()
+    n = int(header[0].item())
+    items = ints[HEADER_INTS:HEADER_INTS + n * ITEM_INTS].view(n, ITEM_INTS).clone()
+    return header, items
+
+
+def mla_plan_host(seq_lens, s_q: int, num_heads: int, block_size: int, max_blocks_per_seq: int,
+                  causal: bool = True, split_keys: int = 0, max_items: int = 1 << 20):
+    """Host mirror of the planner: returns (items int32[n, 8], rows_per_item, chunk_keys)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    desc = make_desc(lens.shape[0], num_heads, block_size, 1, max_blocks_per_seq,
+                     MLA_DTYPE_BF16, causal, split_keys)
+    buf = np.zeros((max_items, ITEM_INTS), dtype=np.int32)
+    rows = ctypes.c_int32(0)
+    chunk = ctypes.c_int32(0)
+    n = library().mla_plan_host(lens.ctypes.data, s_q, ctypes.byref(desc), buf.ctypes.data,
+                                max_items, ctypes.byref(rows), ctypes.byref(chunk))
+    if n < 0:
+        raise MlaError(1, "mla_plan_host")
+    return buf[:n].copy(), rows.value, chunk.value

@@ -1,0 +1,195 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances: bf16 cache — relative Frobenius error of out <= 5e-3 and
+max |lse - ref| <= 1e-3; fp8 cache — relative Frobenius error of out <= 1e-2
+(lse is held to 1e-3 as well: both sides use the same dequantised values).
+The page's own kernel-test metric, cos_diff < 1e-4, is checked too. Outputs
+are prefilled with NaN so an unwritten element fails.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+from oracle import mla_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (5e-3, 1e-3), "fp8": (1e-2, 1e-3)}
+
+
+def have_gpu():
+    return torch.cuda.is_available()
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not have_gpu():
+        pytest.skip("no GPU")
+    import mla_paged_decode_04_amd as m
+    m.library()   # raises if the HIP library is missing: no fallback
+    return m
+
+
+def to_device(inp):
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(inp.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    if inp.wl.kv_dtype == "bf16":
+        kv = torch.from_numpy(inp.kv.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        kv = torch.from_numpy(inp.kv).to(dev).view(torch.float8_e4m3fn)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    sl = torch.from_numpy(inp.seq_lens).to(dev)
+    return q, kv, bt, sl
+
+
+def run_gpu(mla, inp, split_keys=0, dev_inputs=None):
+    q, kv, bt, sl = dev_inputs or to_device(inp)
+    wl = inp.wl
+    out = torch.full((wl.batch, wl.s_q, wl.heads, 512), float("nan"), dtype=torch.bfloat16,
+                     device=q.device)
+    lse = torch.full((wl.batch, wl.s_q, wl.heads), float("nan"), dtype=torch.float32,
+                     device=q.device)
+    mla.mla_decode(q, kv, bt, sl, wl.softmax_scale, inp.kv_scale, causal=wl.causal, out=out,
+                   lse=lse, split_keys=split_keys)
+    torch.cuda.synchronize()
+    return out.float().cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def run_oracle(inp):
+    wl = inp.wl
+    return orc.mla_decode(inp.q_bits, inp.kv, inp.block_table, inp.seq_lens, wl.s_q,
+                          wl.softmax_scale, inp.kv_scale, wl.kv_dtype, wl.causal)
+
+
+def assert_parity(o, l, ro, rl, dtype, tag=""):
+    tol_o, tol_l = TOL[dtype]
+    assert np.isfinite(o).all(), f"{tag}: non-finite or unwritten output"
+    fin = np.isfinite(rl)
+    assert (np.isneginf(l) == ~fin).all(), f"{tag}: -inf lse pattern differs"
+    # rows that see no key: exact zeros
+    assert (o[~fin] == 0).all()
+    err = orc.rel_fro(o, ro)
+    lerr = float(np.abs(l[fin] - rl[fin]).max()) if fin.any() else 0.0
+    cd = orc.cos_diff(o, ro)
+    print(f"[{tag}] rel_fro={err:.3e} max|dlse|={lerr:.3e} cos_diff={cd:.3e}", flush=True)
+    assert err <= tol_o, f"{tag}: rel Frobenius {err} > {tol_o}"
+    assert lerr <= tol_l, f"{tag}: lse error {lerr} > {tol_l}"
+    if fin.any():
+        assert cd < 1e-4, f"{tag}: cos_diff {cd}"
+
+
+# ---------------------------------------------------------------------------
+# the workloads at their full sizes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(mi.WORKLOADS))
+def test_workload_full_size(mla, name):
+    wl = mi.WORKLOADS[name]
+    print(f"workload {name}", flush=True)
+    inp = mi.make_inputs(wl)
+    o, l = run_gpu(mla, inp)
+    ro, rl = run_oracle(inp)
+    assert_parity(o, l, ro, rl, wl.kv_dtype, name)
+
+
+# ---------------------------------------------------------------------------
+# split-KV: forced chunking agrees with the oracle and with the unsplit run
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,split", [("tiny", 64), ("tiny_fp8", 128),
+                                        ("b128_h16_L4096_bf16", 448),
+                                        ("b64_h128_L1k2k_bs128_bf16", 192)])
+def test_forced_split(mla, name, split):
+    wl = mi.WORKLOADS[name]
+    if wl.batch > 16:
+        wl = mi.shrink(wl, 16)
+    inp = mi.make_inputs(wl)
+    dev = to_device(inp)
+    o1, l1 = run_gpu(mla, inp, split_keys=0, dev_inputs=dev)
+    o2, l2 = run_gpu(mla, inp, split_keys=split, dev_inputs=dev)
+    ro, rl = run_oracle(inp)
+    assert_parity(o2, l2, ro, rl, wl.kv_dtype, f"{name} split={split}")
+    # split and unsplit runs agree with each other to bf16 rounding
+    assert orc.rel_fro(o2, o1) <= 5e-3
+    assert np.abs(l2 - l1).max() <= 1e-4
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+EDGE = [
+    # (tag, B, s_q, H, bs, dtype, lens)
+    ("empty_and_one", 3, 1, 16, 64, "bf16", (0, 1, 2)),
+    ("ragged_tails", 4, 1, 16, 64, "bf16", (63, 64, 65, 127)),
+    ("sq_longer_than_seq", 2, 4, 16, 64, "bf16", (2, 5)),
+    ("one_head", 3, 1, 1, 64, "bf16", (100, 7, 300)),
+    ("heads_24", 2, 1, 24, 128, "fp8", (129, 500)),
+    ("heads_32_sq2", 2, 2, 32, 64, "bf16", (70, 1000)),
+    ("heads_64", 2, 1, 64, 128, "bf16", (333, 1200)),
+    ("heads_128_sq16", 1, 16, 128, 64, "fp8", (700,)),
+    ("non_causal_sq3", 2, 3, 16, 64, "bf16", (10, 90)),
+    ("bs128_fp8_short", 3, 1, 16, 128, "fp8", (1, 128, 129)),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(mla, case):
+    tag, B, s_q, H, bs, dtype, lens = case
+    causal = not tag.startswith("non_causal")
+    wl = mi.Workload(tag, B, s_q, H, bs, dtype, "fixed", lens, causal=causal, seed=77)
+    inp = mi.make_inputs(wl)
+    o, l = run_gpu(mla, inp)
+    ro, rl = run_oracle(inp)
+    assert_parity(o, l, ro, rl, dtype, tag)
+
+
+def test_page_permutation_is_bit_identical_on_gpu(mla):
+    wl = mi.shrink(mi.WORKLOADS["b64_h128_L1k2k_bs128_bf16"], 6)
+    inp = mi.make_inputs(wl)
+    o1, l1 = run_gpu(mla, inp)
+    o2, l2 = run_gpu(mla, mi.permute_pages(inp, seed=5))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_repeat_calls_are_deterministic(mla):
+    wl = mi.shrink(mi.WORKLOADS["b32_sq4_h128_L512_16k_fp8"], 4)
+    inp = mi.make_inputs(wl)
+    dev = to_device(inp)
+    a = run_gpu(mla, inp, dev_inputs=dev)
+    b = run_gpu(mla, inp, dev_inputs=dev)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_lse_may_be_omitted(mla):
+    inp = mi.make_inputs(mi.WORKLOADS["tiny"])
+    q, kv, bt, sl = to_device(inp)
+    wl = inp.wl
+    out, lse = mla.mla_decode(q, kv, bt, sl, wl.softmax_scale, want_lse=False)
+    assert lse is None
+    ro, _ = run_oracle(inp)
+    assert orc.rel_fro(out.float().cpu().double().numpy(), ro) <= 5e-3
+
+
+# ---------------------------------------------------------------------------
+# the split planner on the device equals its host mirror (integer work: exact)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lens,s_q,H,bs,maxb,split", [
+    ([37, 200], 1, 16, 64, 4, 0),
+    ([4096] * 128, 1, 16, 64, 64, 0),
+    ([512, 16384, 777, 5000, 9000, 600] * 5 + [1, 0], 4, 128, 64, 256, 0),
+    (list(range(0, 3000, 7)), 1, 16, 128, 24, 0),
+    ([4096, 100, 3000, 64], 1, 16, 64, 64, 192),
+])
+def test_device_plan_matches_host_mirror(mla, lens, s_q, H, bs, maxb, split):
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda:0")
+    header, items = mla.mla_decode_plan(sl, s_q, H, bs, maxb, split_keys=split)
+    host, rows, chunk = mla.mla_plan_host(lens, s_q, H, bs, maxb, split_keys=split)
+    assert int(header[0]) == len(host) and int(header[1]) == chunk and int(header[3]) == 0
+    np.testing.assert_array_equal(items.cpu().numpy(), host)
