@@ -33,7 +33,8 @@ constexpr int NTHREADS = 256;        // 4 wave64 per workgroup
 constexpr int CHUNKS = D / 8;        // 72 16-byte bf16 chunks per row
 constexpr int TILE_BYTES = NT * D * 2;            // 73728: one bf16 tile
 constexpr int OSTRIDE = DV + 4;      // fp32 row stride of the output staging
-constexpr int TARGET_ITEMS = 512;    // about two work items per CU on 256 CUs
+constexpr int TARGET_ITEMS_WIDE = 512;   // row groups of 32/64 rows: ~2 items per CU
+constexpr int TARGET_ITEMS_NARROW = 256; // <= 16 rows: one 4-wave item per CU
 constexpr int MIN_CHUNK = 256;       // shortest automatic split chunk (keys)
 constexpr int HEADER_BYTES = 256;
 constexpr int ITEM_INTS = 8;
@@ -51,9 +52,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 
 struct RowCfg {
-  int ks;     // waves that split each tile's keys (4, 2 or 1)
-  int rgs;    // query rows per work item = 16 * (4 / ks)
-  int nrg;    // row groups per sequence
+  int ks;      // waves that split each tile's keys (4, 2 or 1)
+  int rgs;     // query rows per work item = 16 * (4 / ks)
+  int nrg;     // row groups per sequence
+  int target;  // work items the automatic split aims for
 };
 
 __host__ __device__ inline RowCfg row_config(int rows) {
@@ -61,6 +63,7 @@ __host__ __device__ inline RowCfg row_config(int rows) {
   c.ks = rows <= 16 ? 4 : (rows <= 32 ? 2 : 1);
   c.rgs = 16 * (4 / c.ks);
   c.nrg = (rows + c.rgs - 1) / c.rgs;
+  c.target = rows <= 16 ? TARGET_ITEMS_NARROW : TARGET_ITEMS_WIDE;
   return c;
 }
 
@@ -76,9 +79,9 @@ __host__ __device__ inline void seq_split(int keys, int chunk, int* n, int* len)
   *n = (keys + l - 1) / l;
 }
 
-__host__ __device__ inline int chunk_from_work(long long work, int forced) {
+__host__ __device__ inline int chunk_from_work(long long work, int forced, int target) {
   if (forced > 0) return forced;
-  long long c = (work + TARGET_ITEMS - 1) / TARGET_ITEMS;
+  long long c = (work + target - 1) / target;
   c = (c + NT - 1) / NT * NT;
   if (c < MIN_CHUNK) c = MIN_CHUNK;
   if (c > (1LL << 30)) c = 1LL << 30;
@@ -93,7 +96,7 @@ inline long long max_items_bound(int batch, int rows, int max_keys, int forced) 
   if (per_seq_cap < 1) per_seq_cap = 1;
   long long cap = (long long)rc.nrg * batch * per_seq_cap;
   if (forced == 0) {
-    long long auto_cap = TARGET_ITEMS + (long long)rc.nrg * batch;
+    long long auto_cap = rc.target + (long long)rc.nrg * batch;
     long long min_cap = (long long)rc.nrg * batch * ((max_keys + MIN_CHUNK - 1) / MIN_CHUNK);
     if (min_cap < (long long)rc.nrg * batch) min_cap = (long long)rc.nrg * batch;
     if (auto_cap < cap) cap = auto_cap;
@@ -172,6 +175,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, y)) << 16);
 }
 
+// Transposed 64-bit LDS read (see the V^T operand set-up in the decode kernel).
+__device__ __forceinline__ s16x4_t read_vt(const char* p) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+  // generic -> LDS address space needs a C-style cast
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+}
+
 // ---------------------------------------------------------------------------
 // planner
 // ---------------------------------------------------------------------------
@@ -181,7 +191,7 @@ struct PlanParams {
   int32_t* header;       // [0] items [1] chunk [2] slots [3] clamp flag
   int32_t* items;        // ITEM_INTS per item
   int32_t* pairs;        // per (b, row group): first slot, number of splits
-  int batch, nrg, max_keys, forced_chunk;
+  int batch, nrg, max_keys, forced_chunk, target;
   long long max_items;
 };
 
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     if (tid < s) red[tid] += red[tid + s];
     __syncthreads();
   }
-  if (tid == 0) s_chunk = chunk_from_work(red[0], p.forced_chunk);
+  if (tid == 0) s_chunk = chunk_from_work(red[0], p.forced_chunk, p.target);
   __syncthreads();
   const int chunk = s_chunk;
 
@@ -347,6 +357,100 @@ struct TileStage<MLA_DTYPE_FP8_E4M3FN> {
   }
 };
 
+// Final step of a work item. Each of the 4 waves holds, for the 16 rows of its
+// row tile (one row per lane, lane groups splitting the dims), the running max
+// m (base 2), its share of the running sum, and unnormalised O^T. The KS
+// waves that share a row tile are merged through LDS (weights 2^(m_k - M)),
+// then the rows are written as final bf16 out + natural-log lse (slot < 0), or
+// as an fp32 split partial (normalised o and base-2 lse). Every wave must be
+// done with `smem` before the call.
+template <int KS>
+__device__ __forceinline__ void merge_and_store(const FwdParams& p, char* smem,
+                                                const f32x4_t (&o)[DV / 16], float m_run,
+                                                float l_run, int b, int rg, int slot) {
+  constexpr int RGS = 16 * (4 / KS);
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+  const float l_row = wave_sum_across_groups(l_run);
+  float* ost = reinterpret_cast<float*>(smem);                        // [4][16][OSTRIDE]
+  float* mls = reinterpret_cast<float*>(smem + 4 * 16 * OSTRIDE * 4);  // [4][16][2]
+  {
+    float* dst = ost + (w * 16 + c16) * OSTRIDE + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt)
+      *reinterpret_cast<f32x4_t*>(dst + 16 * dt) = o[dt];
+    if (g == 0) {
+      mls[(w * 16 + c16) * 2] = m_run;
+      mls[(w * 16 + c16) * 2 + 1] = l_row;
+    }
+  }
+  __syncthreads();
+
+  constexpr int TPR = NTHREADS / RGS;   // threads per row
+  constexpr int DPT = DV / TPR;         // dims per thread
+  const int rr = tid / TPR;             // row within the item
+  const int d0 = (tid % TPR) * DPT;
+  const int rtile = rr / 16, rc = rr % 16;
+  float mk[KS], wk[KS];
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    mk[k] = mls[((rtile * KS + k) * 16 + rc) * 2];
+    M = fmaxf(M, mk[k]);
+  }
+  float lsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    wk[k] = mk[k] == -INFINITY ? 0.f : exp2f(mk[k] - M);
+    lsum += wk[k] * mls[((rtile * KS + k) * 16 + rc) * 2 + 1];
+  }
+  const int grow = rg * RGS + rr;
+  if (grow >= p.rows) return;
+  const bool empty = !(lsum > 0.f);
+  const float inv = empty ? 0.f : p.out_scale / lsum;
+  const float lse2 = empty ? -INFINITY : M + log2f(lsum);
+  const size_t orow = (size_t)b * p.rows + grow;
+
+  if (slot < 0) {
+    uint16_t* dst = p.out + orow * DV + d0;
+#pragma unroll
+    for (int d = 0; d < DPT; d += 8) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+          s += wk[k] * ost[((rtile * KS + k) * 16 + rc) * OSTRIDE + d0 + d + e];
+        acc[e] = s * inv;
+      }
+      *reinterpret_cast<uint4*>(dst + d) =
+          make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    }
+    if (p.lse != nullptr && (tid % TPR) == 0) p.lse[orow] = lse2 * LN2;
+  } else {
+    float* dst = p.part_o + ((size_t)slot * RGS + rr) * DV + d0;
+#pragma unroll
+    for (int d = 0; d < DPT; d += 4) {
+      f32x4_t acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+          s += wk[k] * ost[((rtile * KS + k) * 16 + rc) * OSTRIDE + d0 + d + e];
+        acc[e] = s * inv;
+      }
+      *reinterpret_cast<f32x4_t*>(dst + d) = acc;
+    }
+    if ((tid % TPR) == 0) p.part_lse[(size_t)slot * RGS + rr] = lse2;
+  }
+}
+
 // One workgroup = 4 waves handles one work item: `rgs` query rows of one
 // sequence over keys [t0, t1). Wave w owns rows 16*(w / KS) .. +15 of the
 // item and keys [(w % KS) * 64/KS, +64/KS) of every 64-key tile. Each wave
@@ -426,15 +530,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_fwd(FwdParams p) {
   int kbase[2];
   kbase[0] = (ks * KW + c16) * 128 + ((g ^ (c16 & 7)) << 4);
   kbase[1] = (ks * KW + c16) * 128 + (((4 + g) ^ (c16 & 7)) << 4);
-  // V^T operand: dim 16*dt + c16, key (16-key tile base) + 4*g + j. Its chunk
-  // is 2*dt + (c16 >> 3), so the in-row position is
-  // ((2*(dt&3)) ^ j) ^ ((c16 >> 3) ^ 4*(g&1)): a compile-time part selects one
-  // of 8 per-lane offsets and the rest is an immediate.
-  int vbase[8];
+  // V^T operand by transposed LDS reads: within each 16-lane group, lane
+  // s = 4*j + q points at the 8 bytes V[key 4*g + j][dims 16*dt + 4*q .. +3];
+  // ds_read_b64_tr_b16 then hands lane c16 the four values V[4*g + 0..3][16*dt + c16].
+  // The row's 16-byte chunk is 2*dt + (q >> 1) at in-row position
+  // (2*(dt&3) ^ lanex) with lanex = (q >> 1) ^ 4*(g&1) ^ j, so one of four
+  // per-lane offsets plus an immediate addresses every read.
+  int vt[4];
   {
-    const int lanev = (c16 >> 3) ^ ((g & 1) << 2);
+    const int j = c16 >> 2, q = c16 & 3;
+    const int lanex = (q >> 1) ^ ((g & 1) << 2) ^ j;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) vbase[ct] = 4 * g * 128 + ((ct ^ lanev) << 4) + (c16 & 7) * 2;
+    for (int c = 0; c < 4; ++c)
+      vt[c] = (4 * g + j) * 128 + (((2 * c) ^ lanex) << 4) + (q & 1) * 8;
   }
 
   TileStage<KVT> stage;
@@ -520,11 +628,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_fwd(FwdParams p) {
       }
 #pragma unroll
       for (int dt = 0; dt < DV / 16; ++dt) {
-        s16x4_t a;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          a[j] = *reinterpret_cast<const short*>(
-              tile + vbase[((dt & 3) << 1) ^ j] + (dt >> 2) * (NT * 128) + (ks * KW + j) * 128);
+        const s16x4_t a = read_vt(tile + vt[dt & 3] + (dt >> 2) * (NT * 128) + (ks * KW) * 128);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[dt], 0, 0, 0);
       }
     } else {
@@ -539,14 +643,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_fwd(FwdParams p) {
                                  pack_bf16x2(pv[2 * u + 1][2], pv[2 * u + 1][3])));
 #pragma unroll
         for (int dt = 0; dt < DV / 16; ++dt) {
-          s16x4_t a0, a1;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const char* src = tile + vbase[((dt & 3) << 1) ^ j] + (dt >> 2) * (NT * 128) +
-                              (ks * KW + 32 * u + j) * 128;
-            a0[j] = *reinterpret_cast<const short*>(src);
-            a1[j] = *reinterpret_cast<const short*>(src + 16 * 128);
-          }
+          const char* src = tile + vt[dt & 3] + (dt >> 2) * (NT * 128) + (ks * KW + 32 * u) * 128;
+          const s16x4_t a0 = read_vt(src);
+          const s16x4_t a1 = read_vt(src + 16 * 128);
           bf16x8_t a = __builtin_bit_cast(
               bf16x8_t, make_uint4(__builtin_bit_cast(uint2, a0).x, __builtin_bit_cast(uint2, a0).y,
                                    __builtin_bit_cast(uint2, a1).x, __builtin_bit_cast(uint2, a1).y));
@@ -560,82 +659,218 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_fwd(FwdParams p) {
     buf ^= 1;
   }
 
-  // ---- merge the KS key slices of each row tile through LDS ----
-  const float l_row = wave_sum_across_groups(l_run);
-  float* ost = reinterpret_cast<float*>(smem);                        // [4][16][OSTRIDE]
-  float* mls = reinterpret_cast<float*>(smem + 4 * 16 * OSTRIDE * 4);  // [4][16][2]
+  merge_and_store<KS>(p, smem, o, m_run, l_run, b, rg, slot);
+}
+
+// ---------------------------------------------------------------------------
+// decode kernel for <= 16 query rows per sequence (HBM-bound regime)
+// ---------------------------------------------------------------------------
+//
+// Every wave streams its own 16-key tiles (keys t0 + 16*j for j = w, w+4, ...)
+// straight from HBM into a private double buffer in LDS with
+// global_load_lds_dwordx4 (no staging registers, no workgroup barrier per
+// tile): while it computes tile j, tile j+4 is in flight. Tile layout in LDS:
+// [9 column groups of 128 B][16 keys][8 x 16-byte chunks], chunk position
+// XOR-swizzled by key & 7; the DMA lanes pick their global chunk so the LDS
+// side is always 64 consecutive 16-byte slots.
+
+constexpr int H16_KT = 16;                      // keys per wave tile
+constexpr int H16_TILE = H16_KT * D * 2;        // 18432 bytes (bf16)
+constexpr int H16_DMA = H16_TILE / 1024;        // 18 wave-wide 1 KB transfers
+constexpr int H16_GSTRIDE = H16_KT * 128;       // bytes per 128-byte column group
+
+// One wave-wide 1 KB transfer HBM -> LDS: lane l's 16 bytes at gbase + voff
+// land at LDS byte address lds + 16*l (global_load_lds_dwordx4, saddr form).
+// Issued from inline asm: the compiler neither sees nor waits on it, so all
+// ordering against LDS reads is done with the explicit vmcnt waits below.
+// (M0 carries the LDS address; nothing else in these kernels uses M0.)
+__device__ __forceinline__ void lds_dma16(const char* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(gbase)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
+// Compiler fence: keeps LDS reads/writes and DMA issue in program order around
+// the explicit waits below (the compiler does not model DMA-written LDS).
+__device__ __forceinline__ void mem_fence_compiler() { asm volatile("" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int KVT>
+__global__ __launch_bounds__(NTHREADS, 1) void mla_decode_h16(FwdParams p) {
+  static_assert(KVT == MLA_DTYPE_BF16, "bf16 cache");
+  __shared__ __attribute__((aligned(1024))) char smem[4 * 2 * H16_TILE];   // 147456 bytes
+
+  const int n_items = p.header[0];
+  const int item_id = blockIdx.x;
+  if (item_id >= n_items) return;
+  const int32_t* it = p.items + (size_t)item_id * ITEM_INTS;
+  const int b = it[0], t0 = it[2], t1 = it[3], slot = it[4];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+
+  const int L = min(max(p.seq_lens[b], 0), p.max_keys);
+  const int row = c16;
+  const bool row_ok = row < p.rows;
+  int limit = 0;
+  if (row_ok) {
+    int tok = row / p.heads;
+    int vis = p.causal ? L - p.s_q + 1 + tok : L;
+    limit = min(vis, t1);
+  }
+
+  bf16x8_t qb[D / 32];
   {
-    float* dst = ost + (w * 16 + c16) * OSTRIDE + 4 * g;
+    const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt)
-      *reinterpret_cast<f32x4_t*>(dst + 16 * dt) = o[dt];
-    if (g == 0) {
-      mls[(w * 16 + c16) * 2] = m_run;
-      mls[(w * 16 + c16) * 2 + 1] = l_row;
+    for (int s = 0; s < D / 32; ++s) {
+      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
+                       : make_uint4(0, 0, 0, 0);
+      qb[s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // Consume the q loads here, so the compiler's own vmcnt wait for them sits
+  // before the first DMA and not inside the tile loop (it cannot see the DMAs).
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) asm volatile("" ::"v"(qb[s]));
+
+  f32x4_t o[DV / 16];
+#pragma unroll
+  for (int d = 0; d < DV / 16; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  // lane constants
+  const uint32_t dma_lane = (lane >> 3) * (D * 2) + (((lane & 7) ^ (lane >> 3)) << 4);
+  int kbase[2];
+  kbase[0] = c16 * 128 + ((g ^ (c16 & 7)) << 4);
+  kbase[1] = c16 * 128 + (((4 + g) ^ (c16 & 7)) << 4);
+  int vt[4];
+  {
+    const int j = c16 >> 2, q = c16 & 3;
+    const int lanex = (q >> 1) ^ ((g & 1) << 2) ^ j;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      vt[c] = (4 * g + j) * 128 + (((2 * c) ^ lanex) << 4) + (q & 1) * 8;
+  }
+
+  // The block table is read-only for the whole kernel: reading it through the
+  // constant address space keeps these uniform loads on the scalar unit, so
+  // they never enter the vmcnt queue the DMA waits below count on.
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32* bt = (const_i32*)(p.block_table + (size_t)b * p.max_blocks);
+  char* wbuf = smem + w * 2 * H16_TILE;
+  const int ntiles = (t1 - t0 + H16_KT - 1) / H16_KT;
+
+  // Issue the 18 transfers of tile j into dst (always 18 VMEM instructions, so
+  // vmcnt arithmetic below is exact). Keys past the end are fetched from a
+  // valid row and zeroed after arrival by fix_tail().
+  auto issue = [&](int j, char* dst) {
+    const int ts = t0 + H16_KT * j;
+    int page = bt[ts / p.bs];
+    if (page < 0 || page >= p.num_blocks) page = 0;
+    const char* src = reinterpret_cast<const char*>(p.kv) +
+                      ((size_t)page * p.bs + (ts % p.bs)) * (D * 2);
+    const uint32_t l0 = lds_addr(dst);
+#pragma unroll
+    for (int n = 0; n < H16_DMA; ++n)
+      lds_dma16(src + (n & 1) * 8 * (D * 2) + (n >> 1) * 128, dma_lane, l0 + n * 1024);
+  };
+  auto valid_keys = [&](int j) {
+    const int ts = t0 + H16_KT * j;
+    int page = bt[ts / p.bs];
+    if (page < 0 || page >= p.num_blocks) return 0;
+    return min(H16_KT, t1 - ts);
+  };
+  auto fix_tail = [&](int nv, char* buf) {
+    if (nv >= H16_KT) return;
+#pragma unroll
+    for (int n = 0; n < H16_DMA; ++n) {
+      const int key = (n & 1) * 8 + (lane >> 3);
+      if (key >= nv) *reinterpret_cast<uint4*>(buf + n * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  int itn = 0;
+  if (w < ntiles) issue(w, wbuf);
+  for (int j = w; j < ntiles; j += 4, ++itn) {
+    char* cur = wbuf + (itn & 1) * H16_TILE;
+    const bool has_next = j + 4 < ntiles;
+    mem_fence_compiler();
+    if (has_next) {
+      issue(j + 4, wbuf + ((itn + 1) & 1) * H16_TILE);
+      wait_vmcnt<H16_DMA>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    mem_fence_compiler();
+    fix_tail(valid_keys(j), cur);
+    const int ts = t0 + H16_KT * j;
+
+    // S^T = K Q^T (16 keys x 16 rows)
+    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(cur + kbase[s & 1] + (s >> 1) * H16_GSTRIDE);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc, 0, 0, 0);
+    }
+
+    float x[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int key = ts + 4 * g + jj;
+      float v = sacc[jj] * p.scale_log2;
+      v = key < limit ? v : -INFINITY;
+      x[jj] = v;
+      tmax = fmaxf(tmax, v);
+    }
+    tmax = wave_max_across_groups(tmax);
+    const bool need = tmax > m_run + RESCALE_SLACK;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      float alpha = 1.f;
+      if (need) {
+        alpha = exp2f(m_run - tmax);
+        m_run = tmax;
+      }
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < DV / 16; ++d) o[d] *= alpha;
+    }
+    float pv[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float e = m_run == -INFINITY ? 0.f : exp2f(x[jj] - m_run);
+      pv[jj] = e;
+      l_run += e;
+    }
+    const s16x4_t pb = __builtin_bit_cast(
+        s16x4_t, make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])));
+
+    // O^T += V^T P^T (16 keys)
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      const s16x4_t a = read_vt(cur + vt[dt & 3] + (dt >> 2) * H16_GSTRIDE);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[dt], 0, 0, 0);
     }
   }
   __syncthreads();
-
-  constexpr int TPR = NTHREADS / RGS;   // threads per row
-  constexpr int DPT = DV / TPR;         // dims per thread
-  const int rr = tid / TPR;             // row within the item
-  const int d0 = (tid % TPR) * DPT;
-  const int rtile = rr / 16, rc = rr % 16;
-  float mk[KS], wk[KS];
-  float M = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    mk[k] = mls[((rtile * KS + k) * 16 + rc) * 2];
-    M = fmaxf(M, mk[k]);
-  }
-  float lsum = 0.f;
-#pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    wk[k] = mk[k] == -INFINITY ? 0.f : exp2f(mk[k] - M);
-    lsum += wk[k] * mls[((rtile * KS + k) * 16 + rc) * 2 + 1];
-  }
-  const int grow = rg * RGS + rr;
-  if (grow >= p.rows) return;
-  const bool empty = !(lsum > 0.f);
-  const float inv = empty ? 0.f : p.out_scale / lsum;
-  const float lse2 = empty ? -INFINITY : M + log2f(lsum);
-  const size_t orow = (size_t)b * p.rows + grow;
-
-  if (slot < 0) {
-    uint16_t* dst = p.out + orow * DV + d0;
-#pragma unroll
-    for (int d = 0; d < DPT; d += 8) {
-      float acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float s = 0.f;
-#pragma unroll
-        for (int k = 0; k < KS; ++k)
-          s += wk[k] * ost[((rtile * KS + k) * 16 + rc) * OSTRIDE + d0 + d + e];
-        acc[e] = s * inv;
-      }
-      *reinterpret_cast<uint4*>(dst + d) =
-          make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-    }
-    if (p.lse != nullptr && (tid % TPR) == 0) p.lse[orow] = lse2 * LN2;
-  } else {
-    float* dst = p.part_o + ((size_t)slot * RGS + rr) * DV + d0;
-#pragma unroll
-    for (int d = 0; d < DPT; d += 4) {
-      f32x4_t acc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float s = 0.f;
-#pragma unroll
-        for (int k = 0; k < KS; ++k)
-          s += wk[k] * ost[((rtile * KS + k) * 16 + rc) * OSTRIDE + d0 + d + e];
-        acc[e] = s * inv;
-      }
-      *reinterpret_cast<f32x4_t*>(dst + d) = acc;
-    }
-    if ((tid % TPR) == 0) p.part_lse[(size_t)slot * RGS + rr] = lse2;
-  }
+  merge_and_store<4>(p, smem, o, m_run, l_run, b, 0, slot);
 }
 
 // ---------------------------------------------------------------------------
@@ -741,6 +976,7 @@ mla_status_t launch_plan(const int32_t* seq_lens, int32_t s_q, const mla_decode_
   pp.pairs = reinterpret_cast<int32_t*>(base + ws.pairs);
   pp.batch = desc->batch;
   pp.nrg = rc.nrg;
+  pp.target = rc.target;
   pp.max_keys = max_keys_of(desc);
   pp.forced_chunk = desc->split_keys;
   pp.max_items = ws.max_items;
@@ -826,7 +1062,9 @@ mla_status_t launch_fwd_and_combine(const void* q, const void* kv_cache,
   fp.scale_log2 = softmax_scale * kv_scale * LOG2E;
   fp.out_scale = kv_scale;
   dim3 grid(static_cast<unsigned>(ws.max_items));
-  if (desc->kv_dtype == MLA_DTYPE_BF16)
+  if (desc->kv_dtype == MLA_DTYPE_BF16 && rows <= 16)
+    hipLaunchKernelGGL(mla_decode_h16<MLA_DTYPE_BF16>, grid, dim3(NTHREADS), 0, hs, fp);
+  else if (desc->kv_dtype == MLA_DTYPE_BF16)
     launch_fwd<MLA_DTYPE_BF16>(rc.ks, grid, hs, fp);
   else
     launch_fwd<MLA_DTYPE_FP8_E4M3FN>(rc.ks, grid, hs, fp);
@@ -895,7 +1133,7 @@ int32_t mla_plan_host(const int32_t* seq_lens_host, int32_t s_q, const mla_decod
     int L = std::min(std::max(seq_lens_host[b], 0), max_keys);
     work += (long long)rc.nrg * round_up(L, NT);
   }
-  const int chunk = chunk_from_work(work, desc->split_keys);
+  const int chunk = chunk_from_work(work, desc->split_keys, rc.target);
   if (rows_per_item) *rows_per_item = rc.rgs;
   if (chunk_keys) *chunk_keys = chunk;
   int item = 0, slot = 0;
