@@ -46,6 +46,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // shared host/device planning arithmetic
@@ -706,9 +707,33 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// fp8 tiles: 32 keys x 576 bytes = 18432 bytes, laid out as
+// [9 column groups of 64 B][32 keys][4 x 16-byte chunks] with the chunk
+// position XOR-swizzled by f(key) = ((key >> 2) + (key >> 4)) & 3, which keeps
+// both the 8-byte K reads and the 8-bit transposed V reads spread over banks.
+constexpr int F8_KT = 32;
+constexpr int F8_GSTRIDE = F8_KT * 64;
+
+__device__ __forceinline__ int f8_swz(int key) { return ((key >> 2) + (key >> 4)) & 3; }
+
+// 8 e4m3fn codes -> 8 bf16 (exact).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8_v(uint2 w) {
+  return __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(w.x, w.y));
+}
+
+__device__ __forceinline__ uint2 read_vt8(const char* p) {
+  typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(p)));
+}
+
 template <int KVT>
 __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_h16(FwdParams p) {
-  static_assert(KVT == MLA_DTYPE_BF16, "bf16 cache");
+  constexpr bool F8 = KVT == MLA_DTYPE_FP8_E4M3FN;
+  constexpr int KT = F8 ? F8_KT : H16_KT;          // keys per wave tile
+  constexpr int ROWB = F8 ? D : D * 2;             // bytes per cached row
+  constexpr int TILE = KT * ROWB;                  // 18432 either way
+  constexpr int NDMA = TILE / 1024;                // 18
+  static_assert(TILE == H16_TILE, "same LDS budget for both caches");
   __shared__ __attribute__((aligned(1024))) char smem[4 * 2 * H16_TILE];   // 147456 bytes
 
   const int n_items = p.header[0];
@@ -743,7 +768,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_h16(FwdParams p) {
       qb[s] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
-
   // Consume the q loads here, so the compiler's own vmcnt wait for them sits
   // before the first DMA and not inside the tile loop (it cannot see the DMAs).
 #pragma unroll
@@ -755,19 +779,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_h16(FwdParams p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // lane constants
-  const uint32_t dma_lane = (lane >> 3) * (D * 2) + (((lane & 7) ^ (lane >> 3)) << 4);
-  int kbase[2];
-  kbase[0] = c16 * 128 + ((g ^ (c16 & 7)) << 4);
-  kbase[1] = c16 * 128 + (((4 + g) ^ (c16 & 7)) << 4);
-  int vt[4];
-  {
+  // ---- lane constants (LDS byte offsets inside a tile, DMA source offsets) ----
+  uint32_t dma_lane[2];
+  int kb[2][2];   // K operand: [M tile][s & 1], add (s >> 1) * column-group stride
+  int vt[4];      // V^T operand: [dt & 3], add (dt >> 2) * column-group stride
+  if constexpr (!F8) {
+    dma_lane[0] = dma_lane[1] = (lane >> 3) * ROWB + (((lane & 7) ^ (lane >> 3)) << 4);
+    kb[0][0] = c16 * 128 + ((g ^ (c16 & 7)) << 4);
+    kb[0][1] = c16 * 128 + (((4 + g) ^ (c16 & 7)) << 4);
+    kb[1][0] = kb[0][0];
+    kb[1][1] = kb[0][1];
     const int j = c16 >> 2, q = c16 & 3;
     const int lanex = (q >> 1) ^ ((g & 1) << 2) ^ j;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      vt[c] = (4 * g + j) * 128 + (((2 * c) ^ lanex) << 4) + (q & 1) * 8;
+    for (int c = 0; c < 4; ++c) vt[c] = (4 * g + j) * 128 + (((2 * c) ^ lanex) << 4) + (q & 1) * 8;
+  } else {
+    // DMA transfer n: column group n >> 1, keys 16*(n & 1) + (lane >> 2), chunk
+    // position lane & 3; f(key) = ((lane >> 4) + (n & 1)) & 3.
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      dma_lane[h] = (lane >> 2) * ROWB + (((lane & 3) ^ (((lane >> 4) + h) & 3)) << 4);
+    // K: key 16*mi + c16, bytes 32*s + 8*g -> chunk 2*s + (g >> 1), half g & 1
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        kb[mi][h] = (16 * mi + c16) * 64 +
+                    (((2 * h + (g >> 1)) ^ f8_swz(16 * mi + c16)) << 4) + (g & 1) * 8;
+    // V^T: lane s = 2*jj + q supplies V[key_jj][16*dt + 8*q ..+7] with key_jj =
+    // 4g + jj (jj < 4) or 16 + 4g + jj - 4, so ds_read_b64_tr_b8 hands lane
+    // c16 the 8 values V[key_0..7][16*dt + c16].
+    const int jj = c16 >> 1, q = c16 & 1;
+    const int key = jj < 4 ? 4 * g + jj : 16 + 4 * g + (jj - 4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vt[c] = key * 64 + ((c ^ f8_swz(key)) << 4) + q * 8;
   }
+  constexpr int GSTRIDE = F8 ? F8_GSTRIDE : H16_GSTRIDE;
 
   // The block table is read-only for the whole kernel: reading it through the
   // constant address space keeps these uniform loads on the scalar unit, so
@@ -775,33 +822,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_h16(FwdParams p) {
   typedef const __attribute__((address_space(4))) int32_t const_i32;
   const_i32* bt = (const_i32*)(p.block_table + (size_t)b * p.max_blocks);
   char* wbuf = smem + w * 2 * H16_TILE;
-  const int ntiles = (t1 - t0 + H16_KT - 1) / H16_KT;
+  const int ntiles = (t1 - t0 + KT - 1) / KT;
 
-  // Issue the 18 transfers of tile j into dst (always 18 VMEM instructions, so
-  // vmcnt arithmetic below is exact). Keys past the end are fetched from a
-  // valid row and zeroed after arrival by fix_tail().
+  // Issue the NDMA transfers of tile j into dst (always NDMA VMEM
+  // instructions, so the vmcnt arithmetic below is exact). Keys past the end
+  // are fetched from a valid row of the page and zeroed after arrival.
   auto issue = [&](int j, char* dst) {
-    const int ts = t0 + H16_KT * j;
+    const int ts = t0 + KT * j;
     int page = bt[ts / p.bs];
     if (page < 0 || page >= p.num_blocks) page = 0;
-    const char* src = reinterpret_cast<const char*>(p.kv) +
-                      ((size_t)page * p.bs + (ts % p.bs)) * (D * 2);
+    const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts % p.bs)) * ROWB;
     const uint32_t l0 = lds_addr(dst);
 #pragma unroll
-    for (int n = 0; n < H16_DMA; ++n)
-      lds_dma16(src + (n & 1) * 8 * (D * 2) + (n >> 1) * 128, dma_lane, l0 + n * 1024);
+    for (int n = 0; n < NDMA; ++n) {
+      if constexpr (!F8)
+        lds_dma16(src + (n & 1) * 8 * ROWB + (n >> 1) * 128, dma_lane[0], l0 + n * 1024);
+      else
+        lds_dma16(src + (n & 1) * 16 * ROWB + (n >> 1) * 64, dma_lane[n & 1], l0 + n * 1024);
+    }
   };
   auto valid_keys = [&](int j) {
-    const int ts = t0 + H16_KT * j;
+    const int ts = t0 + KT * j;
     int page = bt[ts / p.bs];
     if (page < 0 || page >= p.num_blocks) return 0;
-    return min(H16_KT, t1 - ts);
+    return min(KT, t1 - ts);
   };
   auto fix_tail = [&](int nv, char* buf) {
-    if (nv >= H16_KT) return;
+    if (nv >= KT) return;
 #pragma unroll
-    for (int n = 0; n < H16_DMA; ++n) {
-      const int key = (n & 1) * 8 + (lane >> 3);
+    for (int n = 0; n < NDMA; ++n) {
+      const int key = F8 ? (n & 1) * 16 + (lane >> 2) : (n & 1) * 8 + (lane >> 3);
       if (key >= nv) *reinterpret_cast<uint4*>(buf + n * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
     }
   };
@@ -814,32 +864,45 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_h16(FwdParams p) {
     mem_fence_compiler();
     if (has_next) {
       issue(j + 4, wbuf + ((itn + 1) & 1) * H16_TILE);
-      wait_vmcnt<H16_DMA>();
+      wait_vmcnt<NDMA>();
     } else {
       wait_vmcnt<0>();
     }
     mem_fence_compiler();
     fix_tail(valid_keys(j), cur);
-    const int ts = t0 + H16_KT * j;
+    const int ts = t0 + KT * j;
 
-    // S^T = K Q^T (16 keys x 16 rows)
-    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // ---- S^T = K Q^T: MT 16-key M tiles x 16 rows ----
+    constexpr int MT = KT / 16;
+    f32x4_t sacc[MT];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) sacc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(cur + kbase[s & 1] + (s >> 1) * H16_GSTRIDE);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc, 0, 0, 0);
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        bf16x8_t a;
+        if constexpr (!F8)
+          a = *reinterpret_cast<const bf16x8_t*>(cur + kb[mi][s & 1] + (s >> 1) * GSTRIDE);
+        else
+          a = fp8x8_to_bf16x8_v(*reinterpret_cast<const uint2*>(cur + kb[mi][s & 1] + (s >> 1) * GSTRIDE));
+        sacc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc[mi], 0, 0, 0);
+      }
     }
 
-    float x[4];
+    // ---- online softmax (base 2), lane = one row, 4*MT keys ----
+    float x[MT][4];
     float tmax = -INFINITY;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int key = ts + 4 * g + jj;
-      float v = sacc[jj] * p.scale_log2;
-      v = key < limit ? v : -INFINITY;
-      x[jj] = v;
-      tmax = fmaxf(tmax, v);
-    }
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int key = ts + 16 * mi + 4 * g + jj;
+        float v = sacc[mi][jj] * p.scale_log2;
+        v = key < limit ? v : -INFINITY;
+        x[mi][jj] = v;
+        tmax = fmaxf(tmax, v);
+      }
     tmax = wave_max_across_groups(tmax);
     const bool need = tmax > m_run + RESCALE_SLACK;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -852,21 +915,35 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_h16(FwdParams p) {
 #pragma unroll
       for (int d = 0; d < DV / 16; ++d) o[d] *= alpha;
     }
-    float pv[4];
+    float pv[MT][4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      float e = m_run == -INFINITY ? 0.f : exp2f(x[jj] - m_run);
-      pv[jj] = e;
-      l_run += e;
-    }
-    const s16x4_t pb = __builtin_bit_cast(
-        s16x4_t, make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])));
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float e = m_run == -INFINITY ? 0.f : exp2f(x[mi][jj] - m_run);
+        pv[mi][jj] = e;
+        l_run += e;
+      }
 
-    // O^T += V^T P^T (16 keys)
+    // ---- O^T += V^T P^T ----
+    if constexpr (!F8) {
+      const s16x4_t pb = __builtin_bit_cast(
+          s16x4_t, make_uint2(pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3])));
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) {
-      const s16x4_t a = read_vt(cur + vt[dt & 3] + (dt >> 2) * H16_GSTRIDE);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[dt], 0, 0, 0);
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        const s16x4_t a = read_vt(cur + vt[dt & 3] + (dt >> 2) * GSTRIDE);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[dt], 0, 0, 0);
+      }
+    } else {
+      // k-slots 0..3: keys 4g..4g+3 of M tile 0; 4..7: of M tile 1 (same in A)
+      const bf16x8_t pb = __builtin_bit_cast(
+          bf16x8_t, make_uint4(pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
+                               pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])));
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        const bf16x8_t a = fp8x8_to_bf16x8_v(read_vt8(cur + vt[dt & 3] + (dt >> 2) * GSTRIDE));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
+      }
     }
   }
   __syncthreads();
@@ -1064,6 +1141,8 @@ mla_status_t launch_fwd_and_combine(const void* q, const void* kv_cache,
   dim3 grid(static_cast<unsigned>(ws.max_items));
   if (desc->kv_dtype == MLA_DTYPE_BF16 && rows <= 16)
     hipLaunchKernelGGL(mla_decode_h16<MLA_DTYPE_BF16>, grid, dim3(NTHREADS), 0, hs, fp);
+  else if (rows <= 16)
+    hipLaunchKernelGGL(mla_decode_h16<MLA_DTYPE_FP8_E4M3FN>, grid, dim3(NTHREADS), 0, hs, fp);
   else if (desc->kv_dtype == MLA_DTYPE_BF16)
     launch_fwd<MLA_DTYPE_BF16>(rc.ks, grid, hs, fp);
   else
