@@ -252,6 +252,21 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, flush: bool):
     return res
 
 
+def copy_calibration(mib: int = 1024, reps: int = 3):
+    """A plain device-to-device copy of known size (torch's copy kernel), to
+    scale the FETCH_SIZE / WRITE_SIZE counters of a profile run."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n * 4,
+                                           "bytes_written_per_copy": n * 4, "copies": reps}}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,7 +277,12 @@ def main():
     ap.add_argument("--flush", action="store_true",
                     help="evict the 256 MB Infinity Cache before every timed call")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for counter calibration)")
     a = ap.parse_args()
+    if a.copy_calibration:
+        copy_calibration()
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": a.gpus}))

@@ -37,6 +37,7 @@ extern "C" {
 #define MLA_D_V 512           /* the latent part of the row serves as V */
 #define MLA_MAX_HEADS 128
 #define MLA_MAX_SQ 16
+#define MLA_MAX_BATCH 16384
 #define MLA_ABI_VERSION 1
 
 typedef enum mla_status {
@@ -55,7 +56,7 @@ typedef enum mla_dtype {
 /* Problem description (the kernel test's parameter set, minus the fixed
  * h_kv = 1, d = 576, dv = 512). */
 typedef struct mla_decode_desc {
-    int32_t batch;               /* B >= 0 (B == 0 is a no-op) */
+    int32_t batch;               /* 0 <= B <= MLA_MAX_BATCH (B == 0 is a no-op) */
     int32_t num_heads;           /* H, 1..128 */
     int32_t block_size;          /* bs, 64 or 128 tokens per page */
     int32_t num_blocks;          /* pages in kv_cache, >= 1 */

@@ -1,5 +1,5 @@
 // Paged MLA decode for MI355X (gfx950 / CDNA4): split planner, MFMA decode
-// kernel and LSE combine, behind the C ABI declared in include/mla_decode.h.
+// kernels and LSE combine, behind the C ABI declared in include/mla_decode.h.
 //
 // Operation: decode attention of MLA in its MQA form ("[WIP][Attention]
 // FlashAttn MLA", description) with d = 576, dv = 512, one KV head, a paged
@@ -9,11 +9,14 @@
 // Structure of one call (all on the caller's stream, no host sync):
 //   1. mla_plan_kernel     one workgroup turns device seq_lens into a list of
 //                          work items (sequence, row group, key range)
-//   2. mla_decode_fwd      one workgroup per item: page-table gather of 64-key
-//                          tiles into LDS (fp8 dequantised to bf16 on the way),
-//                          S^T = K Q^T and O^T += V^T P^T on MFMA, online
-//                          softmax in base 2, write of the final row or of a
-//                          split partial (fp32 o, base-2 lse)
+//   2. decode kernel       one workgroup per item, S^T = K Q^T and
+//                          O^T += V^T P^T on bf16 MFMA with a base-2 online
+//                          softmax; writes the final rows or a split partial
+//                          (fp32 normalised o, base-2 lse):
+//        mla_decode_narrow  <= 16 query rows per sequence (HBM-bound): every
+//                           wave streams its own key tiles HBM -> LDS
+//        mla_decode_wide    up to 64 / 128 rows per item (MFMA-heavy): the 4
+//                           waves share 64-key tiles, each owns 16 / 32 rows
 //   3. mla_combine_kernel  merges the partials of split (sequence, row group)
 //                          pairs with log-sum-exp weights
 #include <hip/hip_runtime.h>
@@ -28,13 +31,10 @@ namespace {
 
 constexpr int D = MLA_D_QK;          // 576
 constexpr int DV = MLA_D_V;          // 512
-constexpr int NT = 64;               // keys per LDS tile
+constexpr int NT = 64;               // key granularity of split chunks
 constexpr int NTHREADS = 256;        // 4 wave64 per workgroup
-constexpr int CHUNKS = D / 8;        // 72 16-byte bf16 chunks per row
-constexpr int TILE_BYTES = NT * D * 2;            // 73728: one bf16 tile
 constexpr int OSTRIDE = DV + 4;      // fp32 row stride of the output staging
-constexpr int TARGET_ITEMS_WIDE = 512;   // row groups of 32/64 rows: ~2 items per CU
-constexpr int TARGET_ITEMS_NARROW = 256; // <= 16 rows: one 4-wave item per CU
+constexpr int TARGET_ITEMS = 256;    // automatic split: about one work item per CU
 constexpr int MIN_CHUNK = 256;       // shortest automatic split chunk (keys)
 constexpr int HEADER_BYTES = 256;
 constexpr int ITEM_INTS = 8;
@@ -52,19 +52,23 @@ typedef int i32x2_t __attribute__((ext_vector_type(2)));
 // shared host/device planning arithmetic
 // ---------------------------------------------------------------------------
 
+// Row grouping: kind 0 = narrow kernel (<= 16 rows), kind 1 = wide kernel
+// with 16 rows per wave (64-row items). (A wide variant with 32 rows per wave,
+// 128-row items, exists as a template but does not fit the register file
+// without spilling, so it is not selected.)
 struct RowCfg {
-  int ks;      // waves that split each tile's keys (4, 2 or 1)
-  int rgs;     // query rows per work item = 16 * (4 / ks)
+  int kind;
+  int rgs;     // query rows per work item
   int nrg;     // row groups per sequence
   int target;  // work items the automatic split aims for
 };
 
 __host__ __device__ inline RowCfg row_config(int rows) {
   RowCfg c;
-  c.ks = rows <= 16 ? 4 : (rows <= 32 ? 2 : 1);
-  c.rgs = 16 * (4 / c.ks);
+  c.kind = rows <= 16 ? 0 : 1;
+  c.rgs = c.kind == 0 ? 16 : 64;
   c.nrg = (rows + c.rgs - 1) / c.rgs;
-  c.target = rows <= 16 ? TARGET_ITEMS_NARROW : TARGET_ITEMS_WIDE;
+  c.target = TARGET_ITEMS;
   return c;
 }
 
@@ -131,14 +135,6 @@ inline WsLayout ws_layout(int batch, int s_q, int heads, int max_keys, int force
 // device helpers
 // ---------------------------------------------------------------------------
 
-// Byte offset of 16-byte chunk c (0..71) of tile row `key` in the LDS tile.
-// Rows are grouped by 128-byte column group; inside a group the eight chunks
-// of a row are XOR-swizzled by the row's low three bits, so the 8 lanes that
-// read one chunk column of 8 consecutive rows hit 8 different bank groups.
-__device__ __forceinline__ int lds_off(int key, int c) {
-  return (((c >> 3) * NT + key) << 7) + ((((c & 7) ^ (key & 7))) << 4);
-}
-
 // Two OCP e4m3fn codes (bytes 0,1 of `w`, or bytes 2,3 when `hi`) to two
 // bf16 packed in one dword, by gfx950's v_cvt_scalef32_pk_bf16_fp8 with scale
 // 1. Every e4m3fn value is a bf16 value, so the conversion is exact.
@@ -197,89 +193,107 @@ struct PlanParams {
 };
 
 constexpr int PLAN_THREADS = 256;
+constexpr int PLAN_WAVES = PLAN_THREADS / 64;
 
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    T u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+// One workgroup. Thread t owns the contiguous sequences [t*per, (t+1)*per);
+// seq_lens are read once into LDS. Two block-wide steps: the total work
+// (sum of row groups x keys rounded to 64) fixes the chunk length, then an
+// exclusive scan of per-thread item / partial-slot counts places every item.
 __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
-  __shared__ long long red[PLAN_THREADS];
-  __shared__ int scan_items[PLAN_THREADS];
-  __shared__ int scan_slots[PLAN_THREADS];
-  __shared__ int s_chunk;
-  __shared__ int s_flag;
-  const int tid = threadIdx.x;
-  const int per = (p.batch + PLAN_THREADS - 1) / PLAN_THREADS;
-  const int b0 = tid * per;
-  const int b1 = min(p.batch, b0 + per);
+  extern __shared__ int32_t s_len[];          // batch entries
+  __shared__ long long s_work[PLAN_WAVES];
+  __shared__ int s_items[PLAN_WAVES], s_slots[PLAN_WAVES], s_flag[PLAN_WAVES];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
 
-  long long work = 0;
   int clamped = 0;
-  for (int b = b0; b < b1; ++b) {
+  for (int b = tid; b < p.batch; b += PLAN_THREADS) {
     int L = p.seq_lens[b];
-    if (L < 0 || L > p.max_keys) clamped = 1;
-    L = min(max(L, 0), p.max_keys);
-    work += (long long)p.nrg * round_up(L, NT);
+    clamped |= (L < 0 || L > p.max_keys);
+    s_len[b] = min(max(L, 0), p.max_keys);
   }
-  red[tid] = work;
-  if (tid == 0) s_flag = 0;
   __syncthreads();
-  if (clamped) atomicOr(&s_flag, 1);
-  __syncthreads();
-  for (int s = PLAN_THREADS / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
+
+  const int per = (p.batch + PLAN_THREADS - 1) / PLAN_THREADS;
+  const int b0 = min(p.batch, tid * per);
+  const int b1 = min(p.batch, b0 + per);
+  long long work = 0;
+  for (int b = b0; b < b1; ++b) work += (long long)p.nrg * round_up(s_len[b], NT);
+  work = wave_inclusive_scan(work);
+  const int any_clamped = __any(clamped);
+  if (lane == 63) {
+    s_work[wv] = work;
+    s_flag[wv] = any_clamped;
   }
-  if (tid == 0) s_chunk = chunk_from_work(red[0], p.forced_chunk, p.target);
   __syncthreads();
-  const int chunk = s_chunk;
+  long long total = 0;
+  int flag = 0;
+#pragma unroll
+  for (int i = 0; i < PLAN_WAVES; ++i) {
+    total += s_work[i];
+    flag |= s_flag[i];
+  }
+  const int chunk = chunk_from_work(total, p.forced_chunk, p.target);
 
   int my_items = 0, my_slots = 0;
   for (int b = b0; b < b1; ++b) {
-    int L = min(max(p.seq_lens[b], 0), p.max_keys);
     int n, len;
-    seq_split(L, chunk, &n, &len);
+    seq_split(s_len[b], chunk, &n, &len);
     my_items += p.nrg * n;
     if (n > 1) my_slots += p.nrg * n;
   }
-  scan_items[tid] = my_items;
-  scan_slots[tid] = my_slots;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over the 256 per-thread counts
-  for (int off = 1; off < PLAN_THREADS; off <<= 1) {
-    int a = tid >= off ? scan_items[tid - off] : 0;
-    int c = tid >= off ? scan_slots[tid - off] : 0;
-    __syncthreads();
-    scan_items[tid] += a;
-    scan_slots[tid] += c;
-    __syncthreads();
+  const int inc_items = wave_inclusive_scan(my_items);
+  const int inc_slots = wave_inclusive_scan(my_slots);
+  if (lane == 63) {
+    s_items[wv] = inc_items;
+    s_slots[wv] = inc_slots;
   }
-  int item = scan_items[tid] - my_items;
-  int slot = scan_slots[tid] - my_slots;
+  __syncthreads();
+  int item = inc_items - my_items, slot = inc_slots - my_slots;
+  int tot_items = 0, tot_slots = 0;
+#pragma unroll
+  for (int i = 0; i < PLAN_WAVES; ++i) {
+    if (i < wv) {
+      item += s_items[i];
+      slot += s_slots[i];
+    }
+    tot_items += s_items[i];
+    tot_slots += s_slots[i];
+  }
+
   for (int b = b0; b < b1; ++b) {
-    int L = min(max(p.seq_lens[b], 0), p.max_keys);
+    const int L = s_len[b];
     int n, len;
     seq_split(L, chunk, &n, &len);
     for (int rg = 0; rg < p.nrg; ++rg) {
-      int first = n > 1 ? slot : -1;
-      p.pairs[2 * (b * p.nrg + rg)] = first;
+      p.pairs[2 * (b * p.nrg + rg)] = n > 1 ? slot : -1;
       p.pairs[2 * (b * p.nrg + rg) + 1] = n;
       for (int s = 0; s < n; ++s) {
         if (item < p.max_items) {
-          int32_t* it = p.items + (size_t)item * ITEM_INTS;
-          it[0] = b;
-          it[1] = rg;
-          it[2] = s * len;
-          it[3] = min(L, (s + 1) * len);
-          it[4] = n > 1 ? slot + s : -1;
-          it[5] = 0; it[6] = 0; it[7] = 0;
+          int4* it = reinterpret_cast<int4*>(p.items + (size_t)item * ITEM_INTS);
+          it[0] = make_int4(b, rg, s * len, min(L, (s + 1) * len));
+          it[1] = make_int4(n > 1 ? slot + s : -1, 0, 0, 0);
         }
         ++item;
       }
       if (n > 1) slot += n;
     }
   }
-  if (tid == PLAN_THREADS - 1) {
-    p.header[0] = (int)min((long long)scan_items[PLAN_THREADS - 1], p.max_items);
+  if (tid == 0) {
+    p.header[0] = (int)min((long long)tot_items, p.max_items);
     p.header[1] = chunk;
-    p.header[2] = scan_slots[PLAN_THREADS - 1];
-    p.header[3] = s_flag;
+    p.header[2] = tot_slots;
+    p.header[3] = flag;
   }
 }
 
@@ -301,61 +315,6 @@ struct FwdParams {
   int heads, s_q, rows, bs, max_blocks, max_keys, causal, num_blocks;
   float scale_log2;   // softmax_scale * kv_scale * log2(e)
   float out_scale;    // kv_scale
-};
-
-template <int KVT>
-struct TileStage;
-
-// bf16 cache: 18 x 16 bytes per thread per 64-key tile (73728 bytes).
-template <>
-struct TileStage<MLA_DTYPE_BF16> {
-  static constexpr int N = TILE_BYTES / 16 / NTHREADS;   // 18
-  uint4 v[N];
-  __device__ __forceinline__ void load(const uint8_t* src, int n_valid, int tid) {
-    const uint4* s = reinterpret_cast<const uint4*>(src);
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      int qi = j * NTHREADS + tid;
-      int key = qi / CHUNKS;
-      v[j] = key < n_valid ? s[qi] : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      int qi = j * NTHREADS + tid;
-      int key = qi / CHUNKS;
-      int c = qi - key * CHUNKS;
-      *reinterpret_cast<uint4*>(lds + lds_off(key, c)) = v[j];
-    }
-  }
-};
-
-// fp8 cache: 9 x 16 bytes (16 codes) per thread per tile (36864 bytes),
-// widened to bf16 when written to LDS.
-template <>
-struct TileStage<MLA_DTYPE_FP8_E4M3FN> {
-  static constexpr int N = NT * D / 16 / NTHREADS;   // 9
-  uint4 v[N];
-  __device__ __forceinline__ void load(const uint8_t* src, int n_valid, int tid) {
-    const uint4* s = reinterpret_cast<const uint4*>(src);
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      int qi = j * NTHREADS + tid;
-      int key = qi / (CHUNKS / 2);
-      v[j] = key < n_valid ? s[qi] : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      int qi = j * NTHREADS + tid;
-      int key = qi / (CHUNKS / 2);
-      int c = 2 * (qi - key * (CHUNKS / 2));
-      *reinterpret_cast<uint4*>(lds + lds_off(key, c)) = fp8x8_to_bf16x8(v[j].x, v[j].y);
-      *reinterpret_cast<uint4*>(lds + lds_off(key, c + 1)) = fp8x8_to_bf16x8(v[j].z, v[j].w);
-    }
-  }
 };
 
 // Final step of a work item. Each of the 4 waves holds, for the 16 rows of its
@@ -409,13 +368,13 @@ __device__ __forceinline__ void merge_and_store(const FwdParams& p, char* smem,
     lsum += wk[k] * mls[((rtile * KS + k) * 16 + rc) * 2 + 1];
   }
   const int grow = rg * RGS + rr;
-  if (grow >= p.rows) return;
+  const bool row_ok = grow < p.rows;
   const bool empty = !(lsum > 0.f);
   const float inv = empty ? 0.f : p.out_scale / lsum;
   const float lse2 = empty ? -INFINITY : M + log2f(lsum);
   const size_t orow = (size_t)b * p.rows + grow;
 
-  if (slot < 0) {
+  if (slot < 0 && row_ok) {
     uint16_t* dst = p.out + orow * DV + d0;
 #pragma unroll
     for (int d = 0; d < DPT; d += 8) {
@@ -433,7 +392,7 @@ __device__ __forceinline__ void merge_and_store(const FwdParams& p, char* smem,
                      pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
     }
     if (p.lse != nullptr && (tid % TPR) == 0) p.lse[orow] = lse2 * LN2;
-  } else {
+  } else if (slot >= 0 && row_ok) {
     float* dst = p.part_o + ((size_t)slot * RGS + rr) * DV + d0;
 #pragma unroll
     for (int d = 0; d < DPT; d += 4) {
@@ -450,217 +409,6 @@ __device__ __forceinline__ void merge_and_store(const FwdParams& p, char* smem,
     }
     if ((tid % TPR) == 0) p.part_lse[(size_t)slot * RGS + rr] = lse2;
   }
-}
-
-// One workgroup = 4 waves handles one work item: `rgs` query rows of one
-// sequence over keys [t0, t1). Wave w owns rows 16*(w / KS) .. +15 of the
-// item and keys [(w % KS) * 64/KS, +64/KS) of every 64-key tile. Each wave
-// keeps its own running max / sum / O^T; the KS partial states of a row tile
-// are merged through LDS at the end.
-//
-// MFMA formulation (16x16 output tiles, lane l: column l%16, rows 4*(l/16)+j):
-//   S^T[key, row] = K[key, :] . Q^T[:, row]   A = K from LDS, B = Q^T in VGPRs
-//   O^T[dim, row] += V^T[dim, key] P^T[key, row]
-// so each lane owns one query row (l%16) and the softmax statistics never
-// leave the lane except for a max over the 4 lane groups; the S^T accumulator
-// already has the layout of the P^T operand of the next product.
-template <int KVT, int KS>
-__global__ __launch_bounds__(NTHREADS, 1) void mla_decode_fwd(FwdParams p) {
-  constexpr int KW = NT / KS;          // keys per wave per tile
-  constexpr int MT = KW / 16;          // 16-key M tiles per wave per tile
-  constexpr int RGS = 16 * (4 / KS);   // rows per work item
-  static_assert(2 * TILE_BYTES >= 4 * 16 * OSTRIDE * 4 + 4 * 16 * 8, "staging fits");
-
-  __shared__ __attribute__((aligned(16))) char smem[2 * TILE_BYTES];
-
-  const int n_items = p.header[0];
-  const int item_id = blockIdx.x;
-  if (item_id >= n_items) return;
-  const int32_t* it = p.items + (size_t)item_id * ITEM_INTS;
-  const int b = it[0], rg = it[1], t0 = it[2], t1 = it[3], slot = it[4];
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
-  const int g = lane >> 4;
-  const int c16 = lane & 15;
-  const int ks = w % KS;
-  const int rt = w / KS;
-
-  const int L = min(max(p.seq_lens[b], 0), p.max_keys);
-  const int row_local = rt * 16 + c16;
-  const int row = rg * RGS + row_local;
-  const bool row_ok = row < p.rows;
-  int limit = 0;   // keys [t0, limit) are visible to this lane's row
-  if (row_ok) {
-    int tok = row / p.heads;
-    int vis = p.causal ? L - p.s_q + 1 + tok : L;
-    limit = min(vis, t1);
-  }
-
-  // Q^T operand: lane holds row c16, features 32*s + 8*g .. +7 for s = 0..17.
-  bf16x8_t qb[D / 32];
-  {
-    const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
-                       : make_uint4(0, 0, 0, 0);
-      qb[s] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
-
-  f32x4_t o[DV / 16];
-#pragma unroll
-  for (int d = 0; d < DV / 16; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // running max of base-2 scores (row-uniform)
-  float l_run = 0.f;         // this lane's share of the running sum
-
-  const size_t row_bytes = KVT == MLA_DTYPE_BF16 ? D * 2 : D;
-  const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
-  // A page id outside [0, num_blocks) is a caller error: its keys are read
-  // as zeros instead of faulting.
-  auto tile_src = [&](int ts, int& n_valid) {
-    int page = bt[ts / p.bs];
-    if (page < 0 || page >= p.num_blocks) { n_valid = 0; page = 0; }
-    return p.kv + ((size_t)page * p.bs + (ts % p.bs)) * row_bytes;
-  };
-
-  // Per-lane LDS byte offsets (see lds_off). K operand: key ks*KW + c16,
-  // chunk 4*s + g, whose in-row position is (4*(s&1) + g) ^ (c16 & 7).
-  int kbase[2];
-  kbase[0] = (ks * KW + c16) * 128 + ((g ^ (c16 & 7)) << 4);
-  kbase[1] = (ks * KW + c16) * 128 + (((4 + g) ^ (c16 & 7)) << 4);
-  // V^T operand by transposed LDS reads: within each 16-lane group, lane
-  // s = 4*j + q points at the 8 bytes V[key 4*g + j][dims 16*dt + 4*q .. +3];
-  // ds_read_b64_tr_b16 then hands lane c16 the four values V[4*g + 0..3][16*dt + c16].
-  // The row's 16-byte chunk is 2*dt + (q >> 1) at in-row position
-  // (2*(dt&3) ^ lanex) with lanex = (q >> 1) ^ 4*(g&1) ^ j, so one of four
-  // per-lane offsets plus an immediate addresses every read.
-  int vt[4];
-  {
-    const int j = c16 >> 2, q = c16 & 3;
-    const int lanex = (q >> 1) ^ ((g & 1) << 2) ^ j;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      vt[c] = (4 * g + j) * 128 + (((2 * c) ^ lanex) << 4) + (q & 1) * 8;
-  }
-
-  TileStage<KVT> stage;
-  int buf = 0;
-  if (t0 < t1) {
-    int nv = min(NT, t1 - t0);
-    const uint8_t* src = tile_src(t0, nv);
-    stage.load(src, nv, tid);
-    stage.store(smem, tid);
-  }
-  __syncthreads();
-
-  for (int ts = t0; ts < t1; ts += NT) {
-    const bool has_next = ts + NT < t1;
-    if (has_next) {
-      int nv = min(NT, t1 - ts - NT);
-      const uint8_t* src = tile_src(ts + NT, nv);
-      stage.load(src, nv, tid);
-    }
-
-    const char* tile = smem + buf * TILE_BYTES;
-
-    // ---- S^T = K Q^T for this wave's MT x 16 keys ----
-    // lane reads key kk = ks*KW + 16*mi + c16, chunk 4*s + g: with the swizzle
-    // that is kbase[s & 1] + (s >> 1) * 64 rows * 128 B + mi * 16 rows * 128 B.
-    f32x4_t sacc[MT];
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-      sacc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        const char* src = tile + kbase[s & 1] + (s >> 1) * (NT * 128) + mi * (16 * 128);
-        bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(src);
-        sacc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc[mi], 0, 0, 0);
-      }
-    }
-
-    // ---- online softmax (base 2), lane = one row, 4*MT keys ----
-    float x[MT][4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int key = ts + ks * KW + mi * 16 + 4 * g + j;
-        float v = sacc[mi][j] * p.scale_log2;
-        v = key < limit ? v : -INFINITY;
-        x[mi][j] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    }
-    tmax = wave_max_across_groups(tmax);
-    const bool need = tmax > m_run + RESCALE_SLACK;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      float alpha = 1.f;
-      if (need) {
-        alpha = exp2f(m_run - tmax);   // m_run = -inf gives 0
-        m_run = tmax;
-      }
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < DV / 16; ++d) o[d] *= alpha;
-    }
-    float pv[MT][4];
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float e = m_run == -INFINITY ? 0.f : exp2f(x[mi][j] - m_run);
-        pv[mi][j] = e;
-        l_run += e;
-      }
-    }
-
-    // ---- O^T += V^T P^T ----
-    if constexpr (MT == 1) {
-      // 16 keys: 16x16x16 MFMA, B = P^T (keys 4g..4g+3 of the M tile)
-      s16x4_t pb;
-      {
-        uint32_t p01 = pack_bf16x2(pv[0][0], pv[0][1]);
-        uint32_t p23 = pack_bf16x2(pv[0][2], pv[0][3]);
-        pb = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
-      }
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) {
-        const s16x4_t a = read_vt(tile + vt[dt & 3] + (dt >> 2) * (NT * 128) + (ks * KW) * 128);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[dt], 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < MT / 2; ++u) {
-        // 32 keys = M tiles 2u and 2u+1; k-slots 0..3 -> keys 4g..4g+3 of the
-        // first, k-slots 4..7 -> keys 4g..4g+3 of the second (same in A and B)
-        bf16x8_t pb = __builtin_bit_cast(
-            bf16x8_t, make_uint4(pack_bf16x2(pv[2 * u][0], pv[2 * u][1]),
-                                 pack_bf16x2(pv[2 * u][2], pv[2 * u][3]),
-                                 pack_bf16x2(pv[2 * u + 1][0], pv[2 * u + 1][1]),
-                                 pack_bf16x2(pv[2 * u + 1][2], pv[2 * u + 1][3])));
-#pragma unroll
-        for (int dt = 0; dt < DV / 16; ++dt) {
-          const char* src = tile + vt[dt & 3] + (dt >> 2) * (NT * 128) + (ks * KW + 32 * u) * 128;
-          const s16x4_t a0 = read_vt(src);
-          const s16x4_t a1 = read_vt(src + 16 * 128);
-          bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, make_uint4(__builtin_bit_cast(uint2, a0).x, __builtin_bit_cast(uint2, a0).y,
-                                   __builtin_bit_cast(uint2, a1).x, __builtin_bit_cast(uint2, a1).y));
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
-        }
-      }
-    }
-
-    if (has_next) stage.store(smem + (buf ^ 1) * TILE_BYTES, tid);
-    __syncthreads();
-    buf ^= 1;
-  }
-
-  merge_and_store<KS>(p, smem, o, m_run, l_run, b, rg, slot);
 }
 
 // ---------------------------------------------------------------------------
@@ -685,10 +433,18 @@ constexpr int H16_GSTRIDE = H16_KT * 128;       // bytes per 128-byte column gro
 // Issued from inline asm: the compiler neither sees nor waits on it, so all
 // ordering against LDS reads is done with the explicit vmcnt waits below.
 // (M0 carries the LDS address; nothing else in these kernels uses M0.)
+// Pin a wave-uniform value into SGPRs (the "s" asm constraints below need it).
+__device__ __forceinline__ const char* uniform_ptr(const char* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 __device__ __forceinline__ void lds_dma16(const char* gbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds), "v"(voff), "s"(gbase)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(gbase))
                : "memory");
 }
 
@@ -727,7 +483,7 @@ __device__ __forceinline__ uint2 read_vt8(const char* p) {
 }
 
 template <int KVT>
-__global__ __launch_bounds__(NTHREADS, 1) void mla_decode_h16(FwdParams p) {
+__global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
   constexpr bool F8 = KVT == MLA_DTYPE_FP8_E4M3FN;
   constexpr int KT = F8 ? F8_KT : H16_KT;          // keys per wave tile
   constexpr int ROWB = F8 ? D : D * 2;             // bytes per cached row
@@ -740,7 +496,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_h16(FwdParams p) {
   const int item_id = blockIdx.x;
   if (item_id >= n_items) return;
   const int32_t* it = p.items + (size_t)item_id * ITEM_INTS;
-  const int b = it[0], t0 = it[2], t1 = it[3], slot = it[4];
+  // work-item fields are uniform: keep them (and all tile addressing derived
+  // from them) in SGPRs, so no vector load ever enters the DMA vmcnt queue
+  const int b = __builtin_amdgcn_readfirstlane(it[0]);
+  const int t0 = __builtin_amdgcn_readfirstlane(it[2]);
+  const int t1 = __builtin_amdgcn_readfirstlane(it[3]);
+  const int slot = __builtin_amdgcn_readfirstlane(it[4]);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -748,7 +509,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_h16(FwdParams p) {
   const int g = lane >> 4;
   const int c16 = lane & 15;
 
-  const int L = min(max(p.seq_lens[b], 0), p.max_keys);
+  const int L = __builtin_amdgcn_readfirstlane(min(max(p.seq_lens[b], 0), p.max_keys));
   const int row = c16;
   const bool row_ok = row < p.rows;
   int limit = 0;
@@ -951,6 +712,299 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_h16(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// decode kernel for up to 64 / 128 query rows per item (MFMA-heavy regime)
+// ---------------------------------------------------------------------------
+//
+// The 4 waves share 64-key tiles that they stream HBM -> LDS together (each
+// wave issues a quarter of the DMA transfers) into a double buffer; wave w
+// owns RPW row tiles of 16 rows, so every K or V^T operand read from LDS
+// feeds RPW MFMAs. A tile is processed as two 32-key halves, each with its
+// own running-max update. LDS tile layouts are the narrow kernel's, with 64
+// keys per column group: bf16 [9 x 128 B][64 keys], chunk position
+// (c & 7) ^ (key & 7); fp8 [9 x 64 B][64 keys], chunk position (c & 3) ^ f(key).
+
+constexpr int W_NTK = 64;                     // keys per shared tile
+constexpr int W_TILE_MAX = W_NTK * D * 2;     // 73728 bytes (bf16 tile)
+
+template <int KVT, int RPW>
+__global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
+  constexpr bool F8 = KVT == MLA_DTYPE_FP8_E4M3FN;
+  constexpr int RGS = 4 * RPW * 16;                 // rows per work item
+  constexpr int ROWB = F8 ? D : D * 2;
+  constexpr int TILE = W_NTK * ROWB;                // 73728 / 36864 bytes
+  constexpr int NDMA = TILE / 1024 / 4;             // transfers per wave per tile
+  constexpr int GSTRIDE = W_NTK * (F8 ? 64 : 128);  // bytes per column group
+  __shared__ __attribute__((aligned(1024))) char smem[2 * W_TILE_MAX];   // 147456 bytes
+
+  const int n_items = p.header[0];
+  const int item_id = blockIdx.x;
+  if (item_id >= n_items) return;
+  const int32_t* it = p.items + (size_t)item_id * ITEM_INTS;
+  // uniform work-item fields, pinned to SGPRs (see the narrow kernel)
+  const int b = __builtin_amdgcn_readfirstlane(it[0]);
+  const int rg = __builtin_amdgcn_readfirstlane(it[1]);
+  const int t0 = __builtin_amdgcn_readfirstlane(it[2]);
+  const int t1 = __builtin_amdgcn_readfirstlane(it[3]);
+  const int slot = __builtin_amdgcn_readfirstlane(it[4]);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+  const int L = __builtin_amdgcn_readfirstlane(min(max(p.seq_lens[b], 0), p.max_keys));
+
+  int limit[RPW];
+  bf16x8_t qb[RPW][D / 32];
+#pragma unroll
+  for (int rt = 0; rt < RPW; ++rt) {
+    const int row = rg * RGS + (w * RPW + rt) * 16 + c16;
+    const bool row_ok = row < p.rows;
+    limit[rt] = 0;
+    if (row_ok) {
+      const int tok = row / p.heads;
+      const int vis = p.causal ? L - p.s_q + 1 + tok : L;
+      limit[rt] = min(vis, t1);
+    }
+    const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
+                       : make_uint4(0, 0, 0, 0);
+      qb[rt][s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  // q loads complete here, before the first (compiler-invisible) DMA
+#pragma unroll
+  for (int rt = 0; rt < RPW; ++rt)
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) asm volatile("" ::"v"(qb[rt][s]));
+
+  f32x4_t o[RPW][DV / 16];
+  float m_run[RPW], l_run[RPW];
+#pragma unroll
+  for (int rt = 0; rt < RPW; ++rt) {
+#pragma unroll
+    for (int d = 0; d < DV / 16; ++d) o[rt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
+  }
+
+  // ---- lane constants: DMA source offsets and LDS operand offsets ----
+  uint32_t dma_lane[4];
+  int kb[4][2];   // K operand [M tile][s & 1]; add (s >> 1) * GSTRIDE
+  int vt[2][4];   // V^T operand [32-key half][dt & 3]; add (dt >> 2) * GSTRIDE
+  if constexpr (!F8) {
+    const uint32_t dl = (lane >> 3) * ROWB + (((lane & 7) ^ (lane >> 3)) << 4);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) dma_lane[h] = dl;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      kb[mi][0] = (16 * mi + c16) * 128 + ((g ^ (c16 & 7)) << 4);
+      kb[mi][1] = (16 * mi + c16) * 128 + (((4 + g) ^ (c16 & 7)) << 4);
+    }
+    const int j = c16 >> 2, q = c16 & 3;
+    const int lanex = (q >> 1) ^ ((g & 1) << 2) ^ j;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        vt[u][c] = (32 * u + 4 * g + j) * 128 + (((2 * c) ^ lanex) << 4) + (q & 1) * 8;
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      dma_lane[h] = (lane >> 2) * ROWB + (((lane & 3) ^ (((lane >> 4) + h) & 3)) << 4);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        kb[mi][h] = (16 * mi + c16) * 64 +
+                    (((2 * h + (g >> 1)) ^ f8_swz(16 * mi + c16)) << 4) + (g & 1) * 8;
+    const int jj = c16 >> 1, q = c16 & 1;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int key = 32 * u + (jj < 4 ? 4 * g + jj : 16 + 4 * g + (jj - 4));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) vt[u][c] = key * 64 + ((c ^ f8_swz(key)) << 4) + q * 8;
+    }
+  }
+
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32* bt = (const_i32*)(p.block_table + (size_t)b * p.max_blocks);
+
+  // This wave's NDMA transfers of the tile at key ts (always NDMA VMEM
+  // instructions); transfer n covers 1 KB of the tile's LDS image.
+  auto issue = [&](int ts, char* dst) {
+    int page = bt[ts / p.bs];
+    if (page < 0 || page >= p.num_blocks) page = 0;
+    const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts % p.bs)) * ROWB;
+    const uint32_t l0 = lds_addr(dst);
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int n = w * NDMA + i;
+      if constexpr (!F8)
+        lds_dma16(src + (n & 7) * 8 * ROWB + (n >> 3) * 128, dma_lane[0], l0 + n * 1024);
+      else
+        lds_dma16(src + (n & 3) * 16 * ROWB + (n >> 2) * 64, dma_lane[n & 3], l0 + n * 1024);
+    }
+  };
+  auto valid_keys = [&](int ts) {
+    int page = bt[ts / p.bs];
+    if (page < 0 || page >= p.num_blocks) return 0;
+    return min(W_NTK, t1 - ts);
+  };
+  // zero this wave's slots that hold keys >= nv (after its transfers landed)
+  auto fix_tail = [&](int nv, char* buf) {
+    if (nv >= W_NTK) return;
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int n = w * NDMA + i;
+      const int key = F8 ? (n & 3) * 16 + (lane >> 2) : (n & 7) * 8 + (lane >> 3);
+      if (key >= nv) *reinterpret_cast<uint4*>(buf + n * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  if (t0 < t1) {
+    issue(t0, smem);
+    wait_vmcnt<0>();
+    mem_fence_compiler();
+    fix_tail(valid_keys(t0), smem);
+  }
+  __syncthreads();
+
+  int itn = 0;
+  for (int ts = t0; ts < t1; ts += W_NTK, ++itn) {
+    const char* cur = smem + (itn & 1) * W_TILE_MAX;
+    char* nxt = smem + ((itn + 1) & 1) * W_TILE_MAX;
+    const bool has_next = ts + W_NTK < t1;
+    mem_fence_compiler();
+    if (has_next) issue(ts + W_NTK, nxt);
+    mem_fence_compiler();
+
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // ---- S^T for keys ts + 32u .. +31 (M tiles 2u, 2u+1) x RPW row tiles ----
+      f32x4_t sacc[RPW][2];
+#pragma unroll
+      for (int rt = 0; rt < RPW; ++rt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) sacc[rt][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const char* src = cur + kb[2 * u + h][s & 1] + (s >> 1) * GSTRIDE;
+          bf16x8_t a;
+          if constexpr (!F8)
+            a = *reinterpret_cast<const bf16x8_t*>(src);
+          else
+            a = fp8x8_to_bf16x8_v(*reinterpret_cast<const uint2*>(src));
+#pragma unroll
+          for (int rt = 0; rt < RPW; ++rt)
+            sacc[rt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[rt][s], sacc[rt][h], 0, 0, 0);
+        }
+      }
+
+      // ---- online softmax per row tile (lane = one row, 8 keys) ----
+      bf16x8_t pb[RPW];
+#pragma unroll
+      for (int rt = 0; rt < RPW; ++rt) {
+        float x[2][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int key = ts + 32 * u + 16 * h + 4 * g + jj;
+            float v = sacc[rt][h][jj] * p.scale_log2;
+            v = key < limit[rt] ? v : -INFINITY;
+            x[h][jj] = v;
+            tmax = fmaxf(tmax, v);
+          }
+        tmax = wave_max_across_groups(tmax);
+        const bool need = tmax > m_run[rt] + RESCALE_SLACK;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          float alpha = 1.f;
+          if (need) {
+            alpha = exp2f(m_run[rt] - tmax);
+            m_run[rt] = tmax;
+          }
+          l_run[rt] *= alpha;
+#pragma unroll
+          for (int d = 0; d < DV / 16; ++d) o[rt][d] *= alpha;
+        }
+        float e[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            e[h][jj] = m_run[rt] == -INFINITY ? 0.f : exp2f(x[h][jj] - m_run[rt]);
+            l_run[rt] += e[h][jj];
+          }
+        pb[rt] = __builtin_bit_cast(
+            bf16x8_t, make_uint4(pack_bf16x2(e[0][0], e[0][1]), pack_bf16x2(e[0][2], e[0][3]),
+                                 pack_bf16x2(e[1][0], e[1][1]), pack_bf16x2(e[1][2], e[1][3])));
+      }
+
+      // ---- O^T += V^T P^T over these 32 keys ----
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        const char* src = cur + vt[u][dt & 3] + (dt >> 2) * GSTRIDE;
+        bf16x8_t a;
+        if constexpr (!F8) {
+          const s16x4_t a0 = read_vt(src);
+          const s16x4_t a1 = read_vt(src + 16 * 128);
+          a = __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint2, a0).x,
+                                                      __builtin_bit_cast(uint2, a0).y,
+                                                      __builtin_bit_cast(uint2, a1).x,
+                                                      __builtin_bit_cast(uint2, a1).y));
+        } else {
+          a = fp8x8_to_bf16x8_v(read_vt8(src));
+        }
+#pragma unroll
+        for (int rt = 0; rt < RPW; ++rt)
+          o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], o[rt][dt], 0, 0, 0);
+      }
+    }
+
+    mem_fence_compiler();
+    wait_vmcnt<0>();   // this wave's share of the next tile has landed
+    mem_fence_compiler();
+    if (has_next) fix_tail(valid_keys(ts + W_NTK), nxt);
+    __syncthreads();   // next tile complete, current tile consumed by all waves
+  }
+
+  // ---- write this wave's rows: final (slot < 0) or split partial ----
+#pragma unroll
+  for (int rt = 0; rt < RPW; ++rt) {
+    const float l_row = wave_sum_across_groups(l_run[rt]);
+    const int row_local = (w * RPW + rt) * 16 + c16;
+    const int row = rg * RGS + row_local;
+    if (row >= p.rows) continue;
+    const bool empty = !(l_row > 0.f);
+    const float inv = empty ? 0.f : p.out_scale / l_row;
+    const float lse2 = empty ? -INFINITY : m_run[rt] + log2f(l_row);
+    const size_t orow = (size_t)b * p.rows + row;
+    if (slot < 0) {
+      uint16_t* dst = p.out + orow * DV + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        const f32x4_t v = o[rt][dt] * inv;
+        *reinterpret_cast<uint2*>(dst + 16 * dt) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+      if (p.lse != nullptr && g == 0) p.lse[orow] = lse2 * LN2;
+    } else {
+      float* dst = p.part_o + ((size_t)slot * RGS + row_local) * DV + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt)
+        *reinterpret_cast<f32x4_t*>(dst + 16 * dt) = o[rt][dt] * inv;
+      if (g == 0) p.part_lse[(size_t)slot * RGS + row_local] = lse2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine kernel
 // ---------------------------------------------------------------------------
 
@@ -1022,7 +1076,8 @@ mla_status_t check_desc(int32_t s_q, const mla_decode_desc_t* d) {
   if (d->batch < 0 || d->num_heads < 1 || s_q < 1 || d->num_blocks < 1 ||
       d->max_blocks_per_seq < 1 || d->split_keys < 0 || (d->causal != 0 && d->causal != 1))
     return MLA_ERR_INVALID_ARGUMENT;
-  if (d->num_heads > MLA_MAX_HEADS || s_q > MLA_MAX_SQ) return MLA_ERR_UNSUPPORTED;
+  if (d->num_heads > MLA_MAX_HEADS || s_q > MLA_MAX_SQ || d->batch > MLA_MAX_BATCH)
+    return MLA_ERR_UNSUPPORTED;
   if (d->block_size != 64 && d->block_size != 128) return MLA_ERR_UNSUPPORTED;
   if (d->kv_dtype != MLA_DTYPE_BF16 && d->kv_dtype != MLA_DTYPE_FP8_E4M3FN) return MLA_ERR_UNSUPPORTED;
   if (d->split_keys % NT != 0) return MLA_ERR_INVALID_ARGUMENT;
@@ -1034,11 +1089,10 @@ mla_status_t check_desc(int32_t s_q, const mla_decode_desc_t* d) {
 int max_keys_of(const mla_decode_desc_t* d) { return d->max_blocks_per_seq * d->block_size; }
 
 template <int KVT>
-void launch_fwd(int ks, dim3 grid, hipStream_t st, const FwdParams& fp) {
-  switch (ks) {
-    case 4: hipLaunchKernelGGL((mla_decode_fwd<KVT, 4>), grid, dim3(NTHREADS), 0, st, fp); break;
-    case 2: hipLaunchKernelGGL((mla_decode_fwd<KVT, 2>), grid, dim3(NTHREADS), 0, st, fp); break;
-    default: hipLaunchKernelGGL((mla_decode_fwd<KVT, 1>), grid, dim3(NTHREADS), 0, st, fp); break;
+void launch_decode(int kind, dim3 grid, hipStream_t st, const FwdParams& fp) {
+  switch (kind) {
+    case 0: hipLaunchKernelGGL((mla_decode_narrow<KVT>), grid, dim3(NTHREADS), 0, st, fp); break;
+    default: hipLaunchKernelGGL((mla_decode_wide<KVT, 1>), grid, dim3(NTHREADS), 0, st, fp); break;
   }
 }
 
@@ -1057,7 +1111,8 @@ mla_status_t launch_plan(const int32_t* seq_lens, int32_t s_q, const mla_decode_
   pp.max_keys = max_keys_of(desc);
   pp.forced_chunk = desc->split_keys;
   pp.max_items = ws.max_items;
-  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, pp);
+  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(PLAN_THREADS),
+                     static_cast<unsigned>(desc->batch) * sizeof(int32_t), st, pp);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }
@@ -1109,7 +1164,7 @@ mla_status_t check_call(const void* q, const void* kv_cache, const int32_t* bloc
   return MLA_OK;
 }
 
-mla_status_t launch_fwd_and_combine(const void* q, const void* kv_cache,
+mla_status_t launch_decode_kernel(const void* q, const void* kv_cache,
                                     const int32_t* block_table, const int32_t* seq_lens,
                                     int32_t s_q, float softmax_scale, float kv_scale, void* out,
                                     float* lse, const mla_decode_desc_t* desc, void* workspace,
@@ -1139,14 +1194,10 @@ mla_status_t launch_fwd_and_combine(const void* q, const void* kv_cache,
   fp.scale_log2 = softmax_scale * kv_scale * LOG2E;
   fp.out_scale = kv_scale;
   dim3 grid(static_cast<unsigned>(ws.max_items));
-  if (desc->kv_dtype == MLA_DTYPE_BF16 && rows <= 16)
-    hipLaunchKernelGGL(mla_decode_h16<MLA_DTYPE_BF16>, grid, dim3(NTHREADS), 0, hs, fp);
-  else if (rows <= 16)
-    hipLaunchKernelGGL(mla_decode_h16<MLA_DTYPE_FP8_E4M3FN>, grid, dim3(NTHREADS), 0, hs, fp);
-  else if (desc->kv_dtype == MLA_DTYPE_BF16)
-    launch_fwd<MLA_DTYPE_BF16>(rc.ks, grid, hs, fp);
+  if (desc->kv_dtype == MLA_DTYPE_BF16)
+    launch_decode<MLA_DTYPE_BF16>(rc.kind, grid, hs, fp);
   else
-    launch_fwd<MLA_DTYPE_FP8_E4M3FN>(rc.ks, grid, hs, fp);
+    launch_decode<MLA_DTYPE_FP8_E4M3FN>(rc.kind, grid, hs, fp);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   if (!combine) return MLA_OK;
 
@@ -1181,7 +1232,7 @@ mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* bloc
   hipStream_t hs = static_cast<hipStream_t>(stream);
   st = launch_plan(seq_lens, s_q, desc, workspace, ws, hs);
   if (st != MLA_OK) return st;
-  return launch_fwd_and_combine(q, kv_cache, block_table, seq_lens, s_q, softmax_scale, kv_scale,
+  return launch_decode_kernel(q, kv_cache, block_table, seq_lens, s_q, softmax_scale, kv_scale,
                                 out, lse, desc, workspace, ws, hs, true);
 }
 
@@ -1195,7 +1246,7 @@ mla_status_t mla_decode_fwd_only(const void* q, const void* kv_cache, const int3
                                out, lse, desc, workspace, workspace_bytes, &ws);
   if (st != MLA_OK) return st;
   if (desc->batch == 0) return MLA_OK;
-  return launch_fwd_and_combine(q, kv_cache, block_table, seq_lens, s_q, softmax_scale, kv_scale,
+  return launch_decode_kernel(q, kv_cache, block_table, seq_lens, s_q, softmax_scale, kv_scale,
                                 out, lse, desc, workspace, ws, static_cast<hipStream_t>(stream),
                                 false);
 }
