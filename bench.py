@@ -73,10 +73,15 @@ def source_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str, launch_bytes_expected: int):
+def decode_kernel_name(rows: int) -> str:
+    """The decode kernel the library launches for this many query rows."""
+    return "mla_decode_narrow" if rows <= 16 else "mla_decode_wide"
+
+
+def traffic_from_profile(kernel: str, workload: str):
     """HBM bytes per decode-kernel launch from the committed rocprofv3 counter
     summary, or None when there is none or the kernel source changed since."""
-    path = os.path.join(ROOT, "profiles", f"mla_decode_fwd_{workload}_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -214,9 +219,9 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, flush: bool):
     else:
         roof = {"bound": "mfma", "achieved": round(fwd_tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(fwd_tfs / MFMA_BF16_PEAK_TFS, 4)}
-    traffic = traffic_from_profile(name, nbytes)
-    roof["traffic"] = traffic
-    roof["kernel"] = "mla_decode_fwd"
+    kernel = decode_kernel_name(s_q * H)
+    roof["traffic"] = traffic_from_profile(kernel, name)
+    roof["kernel"] = kernel
     roof["kernel_ms"] = round(fwd_ms_avg, 5)
     roof["hbm_frac"] = round(fwd_gbs / HBM_PEAK_GBS, 4)
     roof["mfma_frac"] = round(fwd_tfs / MFMA_BF16_PEAK_TFS, 4)
