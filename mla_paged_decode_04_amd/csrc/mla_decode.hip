@@ -1027,52 +1027,65 @@ struct CombineParams {
   int rows, rgs, nrg, n_pairs;
 };
 
-// One workgroup per (sequence, row group); only pairs that were split do work.
-// Merge: lse = log2(sum_s 2^lse_s), out = sum_s 2^(lse_s - lse) o_s.
+// Grid (pair, chunk): thread (row, 8-dim slice) of one (sequence, row group)
+// pair; only pairs that were split do work. Merge of the pair's n partials:
+// lse = log2(sum_s 2^lse_s), out = sum_s 2^(lse_s - lse) o_s.
+constexpr int COMBINE_SLICES = DV / 8;   // 64 threads per row
+
 __global__ __launch_bounds__(NTHREADS) void mla_combine_kernel(CombineParams p) {
   const int pair = blockIdx.x;
-  if (pair >= p.n_pairs) return;
   const int first = p.pairs[2 * pair];
   const int n = p.pairs[2 * pair + 1];
   if (first < 0 || n <= 1) return;
+  const int idx = blockIdx.y * NTHREADS + threadIdx.x;
+  const int rr = idx / COMBINE_SLICES;
+  const int d0 = (idx % COMBINE_SLICES) * 8;
   const int b = pair / p.nrg, rg = pair % p.nrg;
-  const int tpr = NTHREADS / p.rgs;
-  const int dpt = DV / tpr;
-  const int rr = threadIdx.x / tpr;
-  const int d0 = (threadIdx.x % tpr) * dpt;
   const int grow = rg * p.rgs + rr;
-  if (grow >= p.rows) return;
+  if (rr >= p.rgs || grow >= p.rows) return;
 
+  const float* lse_s = p.part_lse + (size_t)first * p.rgs + rr;
   float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, p.part_lse[(size_t)(first + s) * p.rgs + rr]);
+  for (int s = 0; s < n; ++s) M = fmaxf(M, lse_s[(size_t)s * p.rgs]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int s = 0; s < n; ++s) {
-    float ls = p.part_lse[(size_t)(first + s) * p.rgs + rr];
-    den += ls == -INFINITY ? 0.f : exp2f(ls - M);
+  const float* src = p.part_o + ((size_t)first * p.rgs + rr) * DV + d0;
+  const size_t sstride = (size_t)p.rgs * DV;
+  int s = 0;
+  for (; s + 2 <= n; s += 2) {   // two splits per step: four 16-byte loads in flight
+    const float l0 = lse_s[(size_t)s * p.rgs], l1 = lse_s[(size_t)(s + 1) * p.rgs];
+    const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(src + s * sstride);
+    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(src + s * sstride + 4);
+    const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(src + (s + 1) * sstride);
+    const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(src + (s + 1) * sstride + 4);
+    const float w0 = l0 == -INFINITY ? 0.f : exp2f(l0 - M);
+    const float w1 = l1 == -INFINITY ? 0.f : exp2f(l1 - M);
+    den += w0 + w1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += w0 * a0[e] + w1 * c0[e];
+      acc[4 + e] += w0 * a1[e] + w1 * c1[e];
+    }
+  }
+  if (s < n) {
+    const float l0 = lse_s[(size_t)s * p.rgs];
+    const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(src + s * sstride);
+    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(src + s * sstride + 4);
+    const float w0 = l0 == -INFINITY ? 0.f : exp2f(l0 - M);
+    den += w0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += w0 * a0[e];
+      acc[4 + e] += w0 * a1[e];
+    }
   }
   const bool empty = !(den > 0.f);
   const float inv = empty ? 0.f : 1.f / den;
   const size_t orow = (size_t)b * p.rows + grow;
-  for (int d = 0; d < dpt; d += 8) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n; ++s) {
-      float ls = p.part_lse[(size_t)(first + s) * p.rgs + rr];
-      float wgt = ls == -INFINITY ? 0.f : exp2f(ls - M) * inv;
-      const float* src = p.part_o + ((size_t)(first + s) * p.rgs + rr) * DV + d0 + d;
-      f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(src);
-      f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(src + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += wgt * v0[e];
-        acc[4 + e] += wgt * v1[e];
-      }
-    }
-    *reinterpret_cast<uint4*>(p.out + orow * DV + d0 + d) =
-        make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-  }
-  if (p.lse != nullptr && (threadIdx.x % tpr) == 0)
-    p.lse[orow] = empty ? -INFINITY : (M + log2f(den)) * LN2;
+  *reinterpret_cast<uint4*>(p.out + orow * DV + d0) =
+      make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                 pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
+  if (p.lse != nullptr && d0 == 0) p.lse[orow] = empty ? -INFINITY : (M + log2f(den)) * LN2;
 }
 
 // ---------------------------------------------------------------------------
@@ -1221,7 +1234,8 @@ mla_status_t launch_decode_kernel(const void* q, const void* kv_cache,
   cp.rgs = rc.rgs;
   cp.nrg = rc.nrg;
   cp.n_pairs = desc->batch * rc.nrg;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(cp.n_pairs), dim3(NTHREADS), 0, hs, cp);
+  const unsigned chunks = (unsigned)((rc.rgs * COMBINE_SLICES + NTHREADS - 1) / NTHREADS);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(cp.n_pairs, chunks), dim3(NTHREADS), 0, hs, cp);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }
