@@ -24,6 +24,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "mla_decode.h"
 
@@ -40,7 +41,13 @@ constexpr int HEADER_BYTES = 256;
 constexpr int ITEM_INTS = 8;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-constexpr float RESCALE_SLACK = 8.0f;   // base-2 headroom before the running max moves
+// Online softmax with a lazily moved reference max (base 2): probabilities
+// are exp2(score - m_ref) with m_ref the row max of the first tile that row
+// saw. Later scores up to m_ref + BIG_SLACK are accumulated as they are
+// (p <= 2^64 is exact enough in bf16 and fp32: relative precision does not
+// depend on magnitude), so the accumulators are never rescaled in the fast
+// loop. A larger jump switches the work item to a slow loop that rescales.
+constexpr float BIG_SLACK = 64.0f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -627,9 +634,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
     }
   };
 
-  int itn = 0;
-  if (w < ntiles) issue(w, wbuf);
-  for (int j = w; j < ntiles; j += 4, ++itn) {
+  // Make tile j (this wave's itn-th) resident: issue the DMA of tile j + 4,
+  // wait for tile j, zero its keys past the end. Returns its LDS buffer.
+  auto prepare = [&](int j, int itn) -> const char* {
     char* cur = wbuf + (itn & 1) * H16_TILE;
     const bool has_next = j + 4 < ntiles;
     mem_fence_compiler();
@@ -641,9 +648,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
     }
     mem_fence_compiler();
     fix_tail(valid_keys(j), cur);
-    const int ts = t0 + KT * j;
+    return cur;
+  };
 
-    // ---- S^T = K Q^T: MT 16-key M tiles x 16 rows ----
+  // One tile: S^T, softmax, O^T += V^T P^T. The fast variant never touches
+  // the accumulators with VALU code and returns false (before consuming the
+  // tile) if a row's max jumped more than BIG_SLACK above its reference.
+  auto compute = [&](const char* cur, int ts, auto slow_tag) -> bool {
+    constexpr bool SLOW = decltype(slow_tag)::value;
     constexpr int MT = KT / 16;
     f32x4_t sacc[MT];
 #pragma unroll
@@ -661,7 +673,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
       }
     }
 
-    // ---- online softmax (base 2), lane = one row, 4*MT keys ----
     float x[MT][4];
     float tmax = -INFINITY;
 #pragma unroll
@@ -675,28 +686,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
         tmax = fmaxf(tmax, v);
       }
     tmax = wave_max_across_groups(tmax);
-    const bool need = tmax > m_run + RESCALE_SLACK;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      float alpha = 1.f;
-      if (need) {
-        alpha = exp2f(m_run - tmax);
-        m_run = tmax;
-      }
-      l_run *= alpha;
+    if constexpr (!SLOW) {
+      if (m_run == -INFINITY) m_run = tmax;   // o and l of this row are still zero
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + BIG_SLACK)) return false;
+    } else {
+      const bool need = tmax > m_run;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        float alpha = 1.f;
+        if (need) {
+          alpha = exp2f(m_run - tmax);   // m_run = -inf gives 0
+          m_run = tmax;
+        }
+        l_run *= alpha;
 #pragma unroll
-      for (int d = 0; d < DV / 16; ++d) o[d] *= alpha;
+        for (int d = 0; d < DV / 16; ++d) o[d] *= alpha;
+      }
     }
     float pv[MT][4];
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        float e = m_run == -INFINITY ? 0.f : exp2f(x[mi][jj] - m_run);
+        const float e = m_run == -INFINITY ? 0.f : exp2f(x[mi][jj] - m_run);
         pv[mi][jj] = e;
         l_run += e;
       }
 
-    // ---- O^T += V^T P^T ----
     if constexpr (!F8) {
       const s16x4_t pb = __builtin_bit_cast(
           s16x4_t, make_uint2(pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3])));
@@ -716,35 +731,58 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
       }
     }
+    return true;
+  };
+
+  int j = w, itn = 0;
+  const char* cur = nullptr;
+  if (w < ntiles) issue(w, wbuf);
+  for (; j < ntiles; j += 4, ++itn) {
+    cur = prepare(j, itn);
+    if (!compute(cur, t0 + KT * j, std::false_type{})) break;
+  }
+  if (j < ntiles) {   // rare: finish with rescaling, starting at the resident tile j
+    compute(cur, t0 + KT * j, std::true_type{});
+    for (j += 4, ++itn; j < ntiles; j += 4, ++itn)
+      compute(prepare(j, itn), t0 + KT * j, std::true_type{});
   }
   __syncthreads();
   merge_and_store<4>(p, smem, o, m_run, l_run, b, 0, slot);
 }
 
 // ---------------------------------------------------------------------------
-// decode kernel for up to 64 / 128 query rows per item (MFMA-heavy regime)
+// decode kernel for up to 64 query rows per item (MFMA-heavy regime)
 // ---------------------------------------------------------------------------
 //
-// The 4 waves share 64-key tiles that they stream HBM -> LDS together (each
-// wave issues a quarter of the DMA transfers) into a double buffer; wave w
-// owns RPW row tiles of 16 rows, so every K or V^T operand read from LDS
-// feeds RPW MFMAs. A tile is processed as two 32-key halves, each with its
-// own running-max update. LDS tile layouts are the narrow kernel's, with 64
-// keys per column group: bf16 [9 x 128 B][64 keys], chunk position
-// (c & 7) ^ (key & 7); fp8 [9 x 64 B][64 keys], chunk position (c & 3) ^ f(key).
+// The 4 waves share 32-key tiles streamed HBM -> LDS through a 4-deep ring,
+// so three tiles are in flight while one is computed; one workgroup barrier
+// per tile. Wave w owns 16 query rows. bf16 tiles are DMA'd straight into the
+// bf16 layout [9 column groups of 128 B][32 keys][8 x 16 B], chunk position
+// (c & 7) ^ (key & 7). fp8 tiles are DMA'd raw (row-major, 576 B per key) into
+// a 4-deep ring and widened once per tile, by all 256 threads, into a
+// double-buffered bf16 tile of the same layout, so every wave reads bf16.
 
-constexpr int W_NTK = 64;                     // keys per shared tile
-constexpr int W_TILE_MAX = W_NTK * D * 2;     // 73728 bytes (bf16 tile)
+constexpr int W_NTK = 32;                         // keys per tile
+constexpr int W_TILE = W_NTK * D * 2;             // 36864 bytes (bf16 tile)
+constexpr int W_RAW8 = W_NTK * D;                 // 18432 bytes (raw fp8 tile)
+constexpr int W_GSTRIDE = W_NTK * 128;            // bytes per 128-byte column group
+
+__device__ __forceinline__ int w_off(int key, int c) {
+  return (((c >> 3) * W_NTK + key) << 7) + (((c & 7) ^ (key & 7)) << 4);
+}
 
 template <int KVT, int RPW>
 __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
+  static_assert(RPW == 1, "16 rows per wave");
   constexpr bool F8 = KVT == MLA_DTYPE_FP8_E4M3FN;
   constexpr int RGS = 4 * RPW * 16;                 // rows per work item
-  constexpr int ROWB = F8 ? D : D * 2;
-  constexpr int TILE = W_NTK * ROWB;                // 73728 / 36864 bytes
-  constexpr int NDMA = TILE / 1024 / 4;             // transfers per wave per tile
-  constexpr int GSTRIDE = W_NTK * (F8 ? 64 : 128);  // bytes per column group
-  __shared__ __attribute__((aligned(1024))) char smem[2 * W_TILE_MAX];   // 147456 bytes
+  constexpr int ROWB = F8 ? D : D * 2;              // bytes per cached row
+  // bf16: ring of 4 tiles, 9 transfers per wave per tile.
+  // fp8: ring of 4 raw tiles (waves 0-1 issue 9 transfers each) + 2 bf16 tiles.
+  constexpr int NDMA = 9;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * W_TILE];   // 147456 bytes
+  char* const raw8 = smem;                          // fp8: 4 x 18432
+  char* const bfbuf = smem + (F8 ? 4 * W_RAW8 : 0); // fp8: 2 x 36864
 
   const int n_items = p.header[0];
   const int item_id = blockIdx.x;
@@ -764,242 +802,248 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
   const int c16 = lane & 15;
   const int L = __builtin_amdgcn_readfirstlane(min(max(p.seq_lens[b], 0), p.max_keys));
 
-  int limit[RPW];
-  bf16x8_t qb[RPW][D / 32];
-#pragma unroll
-  for (int rt = 0; rt < RPW; ++rt) {
-    const int row = rg * RGS + (w * RPW + rt) * 16 + c16;
-    const bool row_ok = row < p.rows;
-    limit[rt] = 0;
-    if (row_ok) {
-      const int tok = row / p.heads;
-      const int vis = p.causal ? L - p.s_q + 1 + tok : L;
-      limit[rt] = min(vis, t1);
-    }
+  const int row_local = w * 16 + c16;
+  const int row = rg * RGS + row_local;
+  const bool row_ok = row < p.rows;
+  int limit = 0;
+  if (row_ok) {
+    const int tok = row / p.heads;
+    const int vis = p.causal ? L - p.s_q + 1 + tok : L;
+    limit = min(vis, t1);
+  }
+  bf16x8_t qb[D / 32];
+  {
     const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
                        : make_uint4(0, 0, 0, 0);
-      qb[rt][s] = __builtin_bit_cast(bf16x8_t, v);
+      qb[s] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
   // q loads complete here, before the first (compiler-invisible) DMA
 #pragma unroll
-  for (int rt = 0; rt < RPW; ++rt)
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) asm volatile("" ::"v"(qb[rt][s]));
+  for (int s = 0; s < D / 32; ++s) asm volatile("" ::"v"(qb[s]));
 
-  f32x4_t o[RPW][DV / 16];
-  float m_run[RPW], l_run[RPW];
+  f32x4_t o[DV / 16];
 #pragma unroll
-  for (int rt = 0; rt < RPW; ++rt) {
+  for (int d = 0; d < DV / 16; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // ---- lane constants ----
+  // bf16 DMA: transfer n (0..35) = column group n >> 2, keys 8*(n & 3) + (lane >> 3)
+  const uint32_t dma_lane = F8 ? lane * 16 : (lane >> 3) * ROWB + (((lane & 7) ^ (lane >> 3)) << 4);
+  int kb[2][2];   // K operand [M tile][s & 1]; add (s >> 1) * W_GSTRIDE
 #pragma unroll
-    for (int d = 0; d < DV / 16; ++d) o[rt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
+  for (int h = 0; h < 2; ++h) {
+    kb[h][0] = (16 * h + c16) * 128 + ((g ^ (c16 & 7)) << 4);
+    kb[h][1] = (16 * h + c16) * 128 + (((4 + g) ^ (c16 & 7)) << 4);
   }
-
-  // ---- lane constants: DMA source offsets and LDS operand offsets ----
-  uint32_t dma_lane[4];
-  int kb[4][2];   // K operand [M tile][s & 1]; add (s >> 1) * GSTRIDE
-  int vt[2][4];   // V^T operand [32-key half][dt & 3]; add (dt >> 2) * GSTRIDE
-  if constexpr (!F8) {
-    const uint32_t dl = (lane >> 3) * ROWB + (((lane & 7) ^ (lane >> 3)) << 4);
-#pragma unroll
-    for (int h = 0; h < 4; ++h) dma_lane[h] = dl;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      kb[mi][0] = (16 * mi + c16) * 128 + ((g ^ (c16 & 7)) << 4);
-      kb[mi][1] = (16 * mi + c16) * 128 + (((4 + g) ^ (c16 & 7)) << 4);
-    }
+  int vt[4];      // V^T operand [dt & 3]; add (dt >> 2) * W_GSTRIDE, second half + 16 rows
+  {
     const int j = c16 >> 2, q = c16 & 3;
     const int lanex = (q >> 1) ^ ((g & 1) << 2) ^ j;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        vt[u][c] = (32 * u + 4 * g + j) * 128 + (((2 * c) ^ lanex) << 4) + (q & 1) * 8;
-  } else {
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-      dma_lane[h] = (lane >> 2) * ROWB + (((lane & 3) ^ (((lane >> 4) + h) & 3)) << 4);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        kb[mi][h] = (16 * mi + c16) * 64 +
-                    (((2 * h + (g >> 1)) ^ f8_swz(16 * mi + c16)) << 4) + (g & 1) * 8;
-    const int jj = c16 >> 1, q = c16 & 1;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int key = 32 * u + (jj < 4 ? 4 * g + jj : 16 + 4 * g + (jj - 4));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) vt[u][c] = key * 64 + ((c ^ f8_swz(key)) << 4) + q * 8;
-    }
+    for (int c = 0; c < 4; ++c) vt[c] = (4 * g + j) * 128 + (((2 * c) ^ lanex) << 4) + (q & 1) * 8;
   }
 
   typedef const __attribute__((address_space(4))) int32_t const_i32;
   const_i32* bt = (const_i32*)(p.block_table + (size_t)b * p.max_blocks);
+  const int ntiles = (t1 - t0 + W_NTK - 1) / W_NTK;
+  // fp8 tiles are fetched by waves 0 and 1 only (18 transfers per tile)
+  const bool dma_wave = !F8 || w < 2;
 
-  // This wave's NDMA transfers of the tile at key ts (always NDMA VMEM
-  // instructions); transfer n covers 1 KB of the tile's LDS image.
-  auto issue = [&](int ts, char* dst) {
+  // Issue this wave's NDMA transfers of tile j (exactly NDMA VMEM
+  // instructions per participating wave; vmcnt arithmetic relies on it).
+  auto issue = [&](int j) {
+    const int ts = t0 + W_NTK * j;
     int page = bt[ts / p.bs];
     if (page < 0 || page >= p.num_blocks) page = 0;
     const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts % p.bs)) * ROWB;
-    const uint32_t l0 = lds_addr(dst);
+    if constexpr (!F8) {
+      const uint32_t l0 = lds_addr(smem + (j & 3) * W_TILE);
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int n = w * NDMA + i;
-      if constexpr (!F8)
-        lds_dma16(src + (n & 7) * 8 * ROWB + (n >> 3) * 128, dma_lane[0], l0 + n * 1024);
-      else
-        lds_dma16(src + (n & 3) * 16 * ROWB + (n >> 2) * 64, dma_lane[n & 3], l0 + n * 1024);
+      for (int i = 0; i < NDMA; ++i) {
+        const int n = w * NDMA + i;
+        lds_dma16_nt(src + (n & 3) * 8 * ROWB + (n >> 2) * 128, dma_lane, l0 + n * 1024);
+      }
+    } else {
+      const uint32_t l0 = lds_addr(raw8 + (j & 3) * W_RAW8);
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int n = w * NDMA + i;
+        lds_dma16_nt(src + n * 1024, dma_lane, l0 + n * 1024);
+      }
     }
   };
-  auto valid_keys = [&](int ts) {
+  auto valid_keys = [&](int j) {
+    const int ts = t0 + W_NTK * j;
     int page = bt[ts / p.bs];
     if (page < 0 || page >= p.num_blocks) return 0;
     return min(W_NTK, t1 - ts);
   };
-  // zero this wave's slots that hold keys >= nv (after its transfers landed)
-  auto fix_tail = [&](int nv, char* buf) {
-    if (nv >= W_NTK) return;
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int n = w * NDMA + i;
-      const int key = F8 ? (n & 3) * 16 + (lane >> 2) : (n & 7) * 8 + (lane >> 3);
-      if (key >= nv) *reinterpret_cast<uint4*>(buf + n * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
-    }
+  // wait until this wave's transfers of tile j landed, given that tiles up to
+  // j + ahead were issued after it
+  auto wait_tile = [&](int ahead) {
+    if (!dma_wave) return;
+    if (ahead >= 2)
+      wait_vmcnt<2 * NDMA>();
+    else if (ahead == 1)
+      wait_vmcnt<NDMA>();
+    else
+      wait_vmcnt<0>();
   };
 
-  if (t0 < t1) {
-    issue(t0, smem);
-    wait_vmcnt<0>();
-    mem_fence_compiler();
-    fix_tail(valid_keys(t0), smem);
+  if (dma_wave) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      if (k < ntiles) issue(k);
   }
-  __syncthreads();
 
-  int itn = 0;
-  for (int ts = t0; ts < t1; ts += W_NTK, ++itn) {
-    const char* cur = smem + (itn & 1) * W_TILE_MAX;
-    char* nxt = smem + ((itn + 1) & 1) * W_TILE_MAX;
-    const bool has_next = ts + W_NTK < t1;
+  // Make tile j resident for every wave (wait for this wave's transfers,
+  // barrier, issue tile j + 3; fp8: widen to bf16). Returns the bf16 tile.
+  auto prepare = [&](int j) -> const char* {
     mem_fence_compiler();
-    if (has_next) issue(ts + W_NTK, nxt);
+    wait_tile(min(2, ntiles - 1 - j));
     mem_fence_compiler();
-
+    const int nv = valid_keys(j);
+    const char* cur;
+    if constexpr (!F8) {
+      cur = smem + (j & 3) * W_TILE;
+      if (nv < W_NTK) {   // zero this wave's slots of keys >= nv
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      // ---- S^T for keys ts + 32u .. +31 (M tiles 2u, 2u+1) x RPW row tiles ----
-      f32x4_t sacc[RPW][2];
-#pragma unroll
-      for (int rt = 0; rt < RPW; ++rt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) sacc[rt][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const char* src = cur + kb[2 * u + h][s & 1] + (s >> 1) * GSTRIDE;
-          bf16x8_t a;
-          if constexpr (!F8)
-            a = *reinterpret_cast<const bf16x8_t*>(src);
-          else
-            a = fp8x8_to_bf16x8_v(*reinterpret_cast<const uint2*>(src));
-#pragma unroll
-          for (int rt = 0; rt < RPW; ++rt)
-            sacc[rt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[rt][s], sacc[rt][h], 0, 0, 0);
+        for (int i = 0; i < NDMA; ++i) {
+          const int n = w * NDMA + i;
+          const int key = (n & 3) * 8 + (lane >> 3);
+          if (key >= nv)
+            *reinterpret_cast<uint4*>(smem + (j & 3) * W_TILE + n * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
         }
       }
-
-      // ---- online softmax per row tile (lane = one row, 8 keys) ----
-      bf16x8_t pb[RPW];
+      __syncthreads();   // tile j complete; tile j-1 consumed by every wave
+      if (dma_wave && j + 3 < ntiles) issue(j + 3);
+    } else {
+      __syncthreads();   // raw tile j landed; raw j-1 and bf16 tile (j-2) consumed
+      if (dma_wave && j + 3 < ntiles) issue(j + 3);
+      // widen raw tile j into bf16 tile j & 1: 1152 chunks of 16 codes
+      char* dst = bfbuf + (j & 1) * W_TILE;
+      const char* rsrc = raw8 + (j & 3) * W_RAW8;
 #pragma unroll
-      for (int rt = 0; rt < RPW; ++rt) {
-        float x[2][4];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int key = ts + 32 * u + 16 * h + 4 * g + jj;
-            float v = sacc[rt][h][jj] * p.scale_log2;
-            v = key < limit[rt] ? v : -INFINITY;
-            x[h][jj] = v;
-            tmax = fmaxf(tmax, v);
-          }
-        tmax = wave_max_across_groups(tmax);
-        const bool need = tmax > m_run[rt] + RESCALE_SLACK;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-          float alpha = 1.f;
-          if (need) {
-            alpha = exp2f(m_run[rt] - tmax);
-            m_run[rt] = tmax;
-          }
-          l_run[rt] *= alpha;
-#pragma unroll
-          for (int d = 0; d < DV / 16; ++d) o[rt][d] *= alpha;
+      for (int i = 0; i < (W_RAW8 / 16 + NTHREADS - 1) / NTHREADS; ++i) {
+        const int qc = i * NTHREADS + tid;
+        if (qc < W_RAW8 / 16) {
+          const int key = qc / (D / 16);
+          const int c = 2 * (qc - key * (D / 16));
+          uint4 v = *reinterpret_cast<const uint4*>(rsrc + qc * 16);
+          uint4 lo = fp8x8_to_bf16x8(v.x, v.y), hi = fp8x8_to_bf16x8(v.z, v.w);
+          if (key >= nv) lo = hi = make_uint4(0, 0, 0, 0);
+          *reinterpret_cast<uint4*>(dst + w_off(key, c)) = lo;
+          *reinterpret_cast<uint4*>(dst + w_off(key, c + 1)) = hi;
         }
-        float e[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            e[h][jj] = m_run[rt] == -INFINITY ? 0.f : exp2f(x[h][jj] - m_run[rt]);
-            l_run[rt] += e[h][jj];
-          }
-        pb[rt] = __builtin_bit_cast(
-            bf16x8_t, make_uint4(pack_bf16x2(e[0][0], e[0][1]), pack_bf16x2(e[0][2], e[0][3]),
-                                 pack_bf16x2(e[1][0], e[1][1]), pack_bf16x2(e[1][2], e[1][3])));
       }
+      __syncthreads();   // bf16 tile complete
+      cur = dst;
+    }
+    return cur;
+  };
 
-      // ---- O^T += V^T P^T over these 32 keys ----
+  // One 32-key tile. The fast variant never touches the accumulators with
+  // VALU code and returns false (before consuming the tile) if a row's max
+  // jumped more than BIG_SLACK above its reference.
+  auto compute = [&](const char* cur, int ts, auto slow_tag) -> bool {
+    constexpr bool SLOW = decltype(slow_tag)::value;
+
+    // ---- S^T for 32 keys (two M tiles) x this wave's 16 rows ----
+    f32x4_t sacc[2][2];   // [M tile][even/odd k-step]: four independent chains
 #pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) {
-        const char* src = cur + vt[u][dt & 3] + (dt >> 2) * GSTRIDE;
-        bf16x8_t a;
-        if constexpr (!F8) {
-          const s16x4_t a0 = read_vt(src);
-          const s16x4_t a1 = read_vt(src + 16 * 128);
-          a = __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint2, a0).x,
-                                                      __builtin_bit_cast(uint2, a0).y,
-                                                      __builtin_bit_cast(uint2, a1).x,
-                                                      __builtin_bit_cast(uint2, a1).y));
-        } else {
-          a = fp8x8_to_bf16x8_v(read_vt8(src));
-        }
+    for (int h = 0; h < 2; ++h) sacc[h][0] = sacc[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rt = 0; rt < RPW; ++rt)
-          o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], o[rt][dt], 0, 0, 0);
+    for (int s = 0; s < D / 32; ++s) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(cur + kb[h][s & 1] + (s >> 1) * W_GSTRIDE);
+        sacc[h][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc[h][s & 1], 0, 0, 0);
       }
     }
 
-    mem_fence_compiler();
-    wait_vmcnt<0>();   // this wave's share of the next tile has landed
-    mem_fence_compiler();
-    if (has_next) fix_tail(valid_keys(ts + W_NTK), nxt);
-    __syncthreads();   // next tile complete, current tile consumed by all waves
+    // ---- online softmax (lane = one row, 8 keys) ----
+    float x[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int key = ts + 16 * h + 4 * g + jj;
+        float v = (sacc[h][0][jj] + sacc[h][1][jj]) * p.scale_log2;
+        v = key < limit ? v : -INFINITY;
+        x[h][jj] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = wave_max_across_groups(tmax);
+    if constexpr (!SLOW) {
+      if (m_run == -INFINITY) m_run = tmax;   // o and l of this row are still zero
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + BIG_SLACK)) return false;
+    } else {
+      const bool need = tmax > m_run;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        float alpha = 1.f;
+        if (need) {
+          alpha = exp2f(m_run - tmax);   // m_run = -inf gives 0
+          m_run = tmax;
+        }
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DV / 16; ++d) o[d] *= alpha;
+      }
+    }
+    float e[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        e[h][jj] = m_run == -INFINITY ? 0.f : exp2f(x[h][jj] - m_run);
+        l_run += e[h][jj];
+      }
+    const bf16x8_t pb = __builtin_bit_cast(
+        bf16x8_t, make_uint4(pack_bf16x2(e[0][0], e[0][1]), pack_bf16x2(e[0][2], e[0][3]),
+                             pack_bf16x2(e[1][0], e[1][1]), pack_bf16x2(e[1][2], e[1][3])));
+
+    // ---- O^T += V^T P^T over these 32 keys ----
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      const char* src = cur + vt[dt & 3] + (dt >> 2) * W_GSTRIDE;
+      const s16x4_t a0 = read_vt(src);
+      const s16x4_t a1 = read_vt(src + 16 * 128);
+      const bf16x8_t a = __builtin_bit_cast(
+          bf16x8_t, make_uint4(__builtin_bit_cast(uint2, a0).x, __builtin_bit_cast(uint2, a0).y,
+                               __builtin_bit_cast(uint2, a1).x, __builtin_bit_cast(uint2, a1).y));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
+    }
+      return true;
+  };
+
+  int j = 0;
+  const char* cur = nullptr;
+  for (; j < ntiles; ++j) {
+    cur = prepare(j);
+    if (!compute(cur, t0 + W_NTK * j, std::false_type{})) break;
+  }
+  if (j < ntiles) {   // rare: finish with rescaling, starting at the resident tile j
+    compute(cur, t0 + W_NTK * j, std::true_type{});
+    for (++j; j < ntiles; ++j) compute(prepare(j), t0 + W_NTK * j, std::true_type{});
   }
 
   // ---- write this wave's rows: final (slot < 0) or split partial ----
-#pragma unroll
-  for (int rt = 0; rt < RPW; ++rt) {
-    const float l_row = wave_sum_across_groups(l_run[rt]);
-    const int row_local = (w * RPW + rt) * 16 + c16;
-    const int row = rg * RGS + row_local;
-    if (row >= p.rows) continue;
+  const float l_row = wave_sum_across_groups(l_run);
+  if (row_ok) {
     const bool empty = !(l_row > 0.f);
     const float inv = empty ? 0.f : p.out_scale / l_row;
-    const float lse2 = empty ? -INFINITY : m_run[rt] + log2f(l_row);
+    const float lse2 = empty ? -INFINITY : m_run + log2f(l_row);
     const size_t orow = (size_t)b * p.rows + row;
     if (slot < 0) {
       uint16_t* dst = p.out + orow * DV + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < DV / 16; ++dt) {
-        const f32x4_t v = o[rt][dt] * inv;
+        const f32x4_t v = o[dt] * inv;
         *reinterpret_cast<uint2*>(dst + 16 * dt) =
             make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
@@ -1008,7 +1052,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
       float* dst = p.part_o + ((size_t)slot * RGS + row_local) * DV + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < DV / 16; ++dt)
-        *reinterpret_cast<f32x4_t*>(dst + 16 * dt) = o[rt][dt] * inv;
+        *reinterpret_cast<f32x4_t*>(dst + 16 * dt) = o[dt] * inv;
       if (g == 0) p.part_lse[(size_t)slot * RGS + row_local] = lse2;
     }
   }

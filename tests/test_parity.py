@@ -147,6 +147,51 @@ def test_edge_cases(mla, case):
     assert_parity(o, l, ro, rl, dtype, tag)
 
 
+# Score jumps: a key aligned with one query row lifts that row's running max by
+# far more than any ordinary tile does, after some tiles have been accumulated
+# (and again later), so the kernels must rescale what they already summed.
+JUMPS = [
+    # (tag, B, s_q, H, bs, dtype, lens, spikes as (position, strength))
+    ("jump_h16_bf16", 2, 1, 16, 64, "bf16", (1500, 700), ((200, 3.0), (650, 6.0))),
+    ("jump_h16_fp8", 2, 1, 16, 64, "fp8", (1500, 700), ((200, 3.0), (650, 6.0))),
+    ("jump_h128_bf16", 2, 1, 128, 128, "bf16", (1500, 700), ((200, 3.0), (650, 6.0))),
+    ("jump_h128_sq4_fp8", 2, 4, 128, 64, "fp8", (3000, 700), ((100, 3.0), (600, 6.0))),
+    ("jump_first_key_huge", 2, 1, 16, 64, "bf16", (900, 300), ((0, 6.0), (250, 3.0))),
+]
+
+
+def plant_spikes(inp, spikes):
+    """Overwrite cache rows with strength * sign(q) of head 0 of the last query
+    token: that row's score jumps by strength * softmax_scale * sum|q|."""
+    wl = inp.wl
+    q = inp.q_bits.astype(np.uint32) << 16
+    q = q.view(np.float32)
+    for b in range(wl.batch):
+        sign = np.where(q[b, wl.s_q - 1, 0] < 0, -1.0, 1.0).astype(np.float32)
+        for t, strength in spikes:
+            if t >= inp.seq_lens[b] - wl.s_q + 1:
+                continue
+            page, slot = inp.block_table[b, t // wl.block_size], t % wl.block_size
+            if wl.kv_dtype == "bf16":
+                inp.kv[page, slot] = mi.f32_to_bf16_bits(strength * sign)
+            else:
+                inp.kv[page, slot] = mi.f32_to_e4m3fn_codes(strength * sign / np.float32(inp.kv_scale))
+    return inp
+
+
+@pytest.mark.parametrize("case", JUMPS, ids=[e[0] for e in JUMPS])
+@pytest.mark.parametrize("split", [0, 192])
+def test_score_jumps_rescale(mla, case, split):
+    tag, B, s_q, H, bs, dtype, lens, spikes = case
+    wl = mi.Workload(tag, B, s_q, H, bs, dtype, "fixed", lens, seed=91)
+    inp = plant_spikes(mi.make_inputs(wl), spikes)
+    o, l = run_gpu(mla, inp, split_keys=split)
+    ro, rl = run_oracle(inp)
+    # the planted rows dominate: head 0 of the last token is (nearly) the spike row
+    assert np.abs(rl[:, s_q - 1, 0]).max() > 100.0
+    assert_parity(o, l, ro, rl, dtype, f"{tag} split={split}")
+
+
 def test_page_permutation_is_bit_identical_on_gpu(mla):
     wl = mi.shrink(mi.WORKLOADS["b64_h128_L1k2k_bs128_bf16"], 6)
     inp = mi.make_inputs(wl)
