@@ -33,7 +33,13 @@ DEFAULT_WORKLOAD = "b128_h16_L4096_bf16"
 METRIC = "paged MLA decode: HBM GB/s + TFLOP/s (fraction of roofline), seqs/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2516.6    # dense bf16 MFMA
-KERNEL_SRC = os.path.join(ROOT, "mla_paged_decode_04_amd", "csrc", "mla_decode.hip")
+CSRC = os.path.join(ROOT, "mla_paged_decode_04_amd", "csrc")
+# the sources each decode kernel is compiled from (a counter summary is only
+# used while these are unchanged)
+KERNEL_SOURCES = {
+    "mla_decode_narrow": ("mla_internal.h", "mla_narrow.hip"),
+    "mla_decode_wide": ("mla_internal.h", "mla_wide.hip"),
+}
 
 
 def algorithmic_bytes(inp) -> int:
@@ -68,9 +74,12 @@ def to_device(inp, torch):
     return q, kv, torch.from_numpy(inp.block_table).to(dev), torch.from_numpy(inp.seq_lens).to(dev)
 
 
-def source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def decode_kernel_name(rows: int) -> str:
@@ -87,7 +96,7 @@ def traffic_from_profile(kernel: str, workload: str):
     text = open(path).read()
     m_src = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_src or not m_b or m_src.group(1) != source_digest():
+    if not m_src or not m_b or m_src.group(1) != source_digest(kernel):
         return None
     return float(m_b.group(1))
 

@@ -14,7 +14,9 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "mla_decode.hip")
+CSRC = os.path.join(PKG, "csrc")
+# host C ABI + planner + combine, and one file per decode kernel
+SRCS = [os.path.join(CSRC, f) for f in ("mla_decode.hip", "mla_narrow.hip", "mla_wide.hip")]
 LIB = os.path.join(PKG, "libmla_decode.so")
 ARCH = "gfx950"
 
@@ -40,7 +42,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile the library (always; a stale build is never reused)."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

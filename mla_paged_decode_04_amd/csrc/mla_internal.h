@@ -1,0 +1,237 @@
+// Internal declarations shared by the translation units of the paged MLA
+// decode library: problem constants, the split-plan arithmetic used by both
+// the host and the device planner, device helpers (fp8 -> bf16, LDS DMA,
+// transposed LDS reads) and the parameter block of the decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "mla_decode.h"
+
+namespace mla_detail {
+constexpr int D = MLA_D_QK;          // 576
+constexpr int DV = MLA_D_V;          // 512
+constexpr int NT = 64;               // key granularity of split chunks
+constexpr int NTHREADS = 256;        // 4 wave64 per workgroup
+constexpr int OSTRIDE = DV + 4;      // fp32 row stride of the output staging
+constexpr int TARGET_ITEMS = 256;    // automatic split: about one work item per CU
+constexpr int MIN_CHUNK = 256;       // shortest automatic split chunk (keys)
+constexpr int HEADER_BYTES = 256;
+constexpr int ITEM_INTS = 8;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+// Online softmax with a lazily moved reference max (base 2): probabilities
+// are exp2(score - m_ref) with m_ref the row max of the first tile that row
+// saw. Later scores up to m_ref + BIG_SLACK are accumulated as they are
+// (p <= 2^64 is exact enough in bf16 and fp32: relative precision does not
+// depend on magnitude), so the accumulators are never rescaled in the fast
+// loop. A larger jump switches the work item to a slow loop that rescales.
+constexpr float BIG_SLACK = 64.0f;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// shared host/device planning arithmetic
+// ---------------------------------------------------------------------------
+
+// Row grouping: kind 0 = narrow kernel (<= 16 rows), kind 1 = wide kernel
+// with 16 rows per wave (64-row items). (A wide variant with 32 rows per wave,
+// 128-row items, exists as a template but does not fit the register file
+// without spilling, so it is not selected.)
+struct RowCfg {
+  int kind;
+  int rgs;     // query rows per work item
+  int nrg;     // row groups per sequence
+  int target;  // work items the automatic split aims for
+};
+
+__host__ __device__ inline RowCfg row_config(int rows) {
+  RowCfg c;
+  c.kind = rows <= 16 ? 0 : 1;
+  c.rgs = c.kind == 0 ? 16 : 64;
+  c.nrg = (rows + c.rgs - 1) / c.rgs;
+  c.target = TARGET_ITEMS;
+  return c;
+}
+
+__host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Split of one sequence's key range [0, keys) into n chunks of `len` keys
+// (len a multiple of the tile); keys == 0 still yields one (empty) chunk.
+__host__ __device__ inline void seq_split(int keys, int chunk, int* n, int* len) {
+  if (keys <= 0) { *n = 1; *len = 0; return; }
+  int n0 = (keys + chunk - 1) / chunk;
+  int l = round_up((keys + n0 - 1) / n0, NT);
+  *len = l;
+  *n = (keys + l - 1) / l;
+}
+
+__host__ __device__ inline int chunk_from_work(long long work, int forced, int target) {
+  if (forced > 0) return forced;
+  long long c = (work + target - 1) / target;
+  c = (c + NT - 1) / NT * NT;
+  if (c < MIN_CHUNK) c = MIN_CHUNK;
+  if (c > (1LL << 30)) c = 1LL << 30;
+  return static_cast<int>(c);
+}
+
+// Upper bound on work items (and partial slots) for a description.
+inline long long max_items_bound(int batch, int rows, int max_keys, int forced) {
+  RowCfg rc = row_config(rows);
+  long long per_seq_cap = (max_keys + NT - 1) / NT;             // chunks are >= 64 keys
+  if (forced > 0) per_seq_cap = (max_keys + forced - 1) / forced;
+  if (per_seq_cap < 1) per_seq_cap = 1;
+  long long cap = (long long)rc.nrg * batch * per_seq_cap;
+  if (forced == 0) {
+    long long auto_cap = rc.target + (long long)rc.nrg * batch;
+    long long min_cap = (long long)rc.nrg * batch * ((max_keys + MIN_CHUNK - 1) / MIN_CHUNK);
+    if (min_cap < (long long)rc.nrg * batch) min_cap = (long long)rc.nrg * batch;
+    if (auto_cap < cap) cap = auto_cap;
+    if (min_cap < cap) cap = min_cap;
+  }
+  return cap;
+}
+
+struct WsLayout {
+  size_t items, pairs, part_lse, part_o, total;
+  long long max_items;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline WsLayout ws_layout(int batch, int s_q, int heads, int max_keys, int forced) {
+  int rows = s_q * heads;
+  RowCfg rc = row_config(rows);
+  WsLayout w;
+  w.max_items = max_items_bound(batch, rows, max_keys, forced);
+  size_t off = HEADER_BYTES;
+  w.items = off;   off = align256(off + (size_t)w.max_items * ITEM_INTS * 4);
+  w.pairs = off;   off = align256(off + (size_t)batch * rc.nrg * 2 * 4);
+  w.part_lse = off; off = align256(off + (size_t)w.max_items * rc.rgs * 4);
+  w.part_o = off;  off = align256(off + (size_t)w.max_items * rc.rgs * DV * 4);
+  w.total = off;
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+
+// Two OCP e4m3fn codes (bytes 0,1 of `w`, or bytes 2,3 when `hi`) to two
+// bf16 packed in one dword, by gfx950's v_cvt_scalef32_pk_bf16_fp8 with scale
+// 1. Every e4m3fn value is a bf16 value, so the conversion is exact.
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  bf16x2_t r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, true)
+                  : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  uint4 r;
+  r.x = fp8x2_to_bf16x2(w0, false);
+  r.y = fp8x2_to_bf16x2(w0, true);
+  r.z = fp8x2_to_bf16x2(w1, false);
+  r.w = fp8x2_to_bf16x2(w1, true);
+  return r;
+}
+
+__device__ __forceinline__ float wave_max_across_groups(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_across_groups(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = static_cast<__bf16>(a);
+  __bf16 y = static_cast<__bf16>(b);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, y)) << 16);
+}
+
+// Transposed 64-bit LDS read (see the V^T operand set-up in the decode kernel).
+__device__ __forceinline__ s16x4_t read_vt(const char* p) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+  // generic -> LDS address space needs a C-style cast
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+}
+
+// One wave-wide 1 KB transfer HBM -> LDS: lane l's 16 bytes at gbase + voff
+// land at LDS byte address lds + 16*l (global_load_lds_dwordx4, saddr form).
+// Issued from inline asm: the compiler neither sees nor waits on it, so all
+// ordering against LDS reads is done with the explicit vmcnt waits below.
+// (M0 carries the LDS address; nothing else in these kernels uses M0.)
+// Pin a wave-uniform value into SGPRs (the "s" asm constraints below need it).
+__device__ __forceinline__ const char* uniform_ptr(const char* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ void lds_dma16(const char* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(gbase))
+               : "memory");
+}
+
+// Same with the non-temporal hint: data that is read exactly once streams
+// through the caches (measured on MI355X: 6.9 TB/s vs 5.8 TB/s for a plain
+// HBM -> LDS copy of 1.2 GB).
+__device__ __forceinline__ void lds_dma16_nt(const char* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(gbase))
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
+// Compiler fence: keeps LDS reads/writes and DMA issue in program order around
+// the explicit waits below (the compiler does not model DMA-written LDS).
+__device__ __forceinline__ void mem_fence_compiler() { asm volatile("" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint8_t* kv;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  uint16_t* out;
+  float* lse;
+  const int32_t* header;
+  const int32_t* items;
+  float* part_o;
+  float* part_lse;
+  int heads, s_q, rows, bs, max_blocks, max_keys, causal, num_blocks;
+  float scale_log2;   // softmax_scale * kv_scale * log2(e)
+  float out_scale;    // kv_scale
+};
+
+// Decode-kernel launchers (one per translation unit); the grid is one
+// workgroup per potential work item.
+void launch_narrow(int kv_dtype, dim3 grid, hipStream_t st, const FwdParams& fp);
+void launch_wide(int kv_dtype, int kind, dim3 grid, hipStream_t st, const FwdParams& fp);
+
+}  // namespace mla_detail

@@ -1,0 +1,406 @@
+// Paged MLA decode, <= 16 query rows per sequence (the HBM-bound regime of
+// the 16-head cases): decode attention of MLA in its MQA form ("[WIP][Attention]
+// FlashAttn MLA", description) over a paged bf16 or fp8 e4m3fn cache
+// ("[Attention] Blackwell FP8 MLA support with CUTLASS_MLA backend", review
+// thread: the kernel test's parameters).
+#include <type_traits>
+
+#include "mla_internal.h"
+
+using namespace mla_detail;
+
+namespace {
+
+// Final step of a work item. Each of the 4 waves holds, for the 16 rows of its
+// row tile (one row per lane, lane groups splitting the dims), the running max
+// m (base 2), its share of the running sum, and unnormalised O^T. The KS
+// waves that share a row tile are merged through LDS (weights 2^(m_k - M)),
+// then the rows are written as final bf16 out + natural-log lse (slot < 0), or
+// as an fp32 split partial (normalised o and base-2 lse). Every wave must be
+// done with `smem` before the call.
+template <int KS>
+__device__ __forceinline__ void merge_and_store(const FwdParams& p, char* smem,
+                                                const f32x4_t (&o)[DV / 16], float m_run,
+                                                float l_run, int b, int rg, int slot) {
+  constexpr int RGS = 16 * (4 / KS);
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+  const float l_row = wave_sum_across_groups(l_run);
+  float* ost = reinterpret_cast<float*>(smem);                        // [4][16][OSTRIDE]
+  float* mls = reinterpret_cast<float*>(smem + 4 * 16 * OSTRIDE * 4);  // [4][16][2]
+  {
+    float* dst = ost + (w * 16 + c16) * OSTRIDE + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt)
+      *reinterpret_cast<f32x4_t*>(dst + 16 * dt) = o[dt];
+    if (g == 0) {
+      mls[(w * 16 + c16) * 2] = m_run;
+      mls[(w * 16 + c16) * 2 + 1] = l_row;
+    }
+  }
+  __syncthreads();
+
+  constexpr int TPR = NTHREADS / RGS;   // threads per row
+  constexpr int DPT = DV / TPR;         // dims per thread
+  const int rr = tid / TPR;             // row within the item
+  const int d0 = (tid % TPR) * DPT;
+  const int rtile = rr / 16, rc = rr % 16;
+  float mk[KS], wk[KS];
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    mk[k] = mls[((rtile * KS + k) * 16 + rc) * 2];
+    M = fmaxf(M, mk[k]);
+  }
+  float lsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    wk[k] = mk[k] == -INFINITY ? 0.f : exp2f(mk[k] - M);
+    lsum += wk[k] * mls[((rtile * KS + k) * 16 + rc) * 2 + 1];
+  }
+  const int grow = rg * RGS + rr;
+  const bool row_ok = grow < p.rows;
+  const bool empty = !(lsum > 0.f);
+  const float inv = empty ? 0.f : p.out_scale / lsum;
+  const float lse2 = empty ? -INFINITY : M + log2f(lsum);
+  const size_t orow = (size_t)b * p.rows + grow;
+
+  if (slot < 0 && row_ok) {
+    uint16_t* dst = p.out + orow * DV + d0;
+#pragma unroll
+    for (int d = 0; d < DPT; d += 8) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+          s += wk[k] * ost[((rtile * KS + k) * 16 + rc) * OSTRIDE + d0 + d + e];
+        acc[e] = s * inv;
+      }
+      *reinterpret_cast<uint4*>(dst + d) =
+          make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    }
+    if (p.lse != nullptr && (tid % TPR) == 0) p.lse[orow] = lse2 * LN2;
+  } else if (slot >= 0 && row_ok) {
+    float* dst = p.part_o + ((size_t)slot * RGS + rr) * DV + d0;
+#pragma unroll
+    for (int d = 0; d < DPT; d += 4) {
+      f32x4_t acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+          s += wk[k] * ost[((rtile * KS + k) * 16 + rc) * OSTRIDE + d0 + d + e];
+        acc[e] = s * inv;
+      }
+      *reinterpret_cast<f32x4_t*>(dst + d) = acc;
+    }
+    if ((tid % TPR) == 0) p.part_lse[(size_t)slot * RGS + rr] = lse2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode kernel for <= 16 query rows per sequence (HBM-bound regime)
+// ---------------------------------------------------------------------------
+//
+// Every wave streams its own 16-key tiles (keys t0 + 16*j for j = w, w+4, ...)
+// straight from HBM into a private double buffer in LDS with
+// global_load_lds_dwordx4 (no staging registers, no workgroup barrier per
+// tile): while it computes tile j, tile j+4 is in flight. Tile layout in LDS:
+// [9 column groups of 128 B][16 keys][8 x 16-byte chunks], chunk position
+// XOR-swizzled by key & 7; the DMA lanes pick their global chunk so the LDS
+// side is always 64 consecutive 16-byte slots.
+
+constexpr int H16_KT = 16;                      // keys per wave tile
+constexpr int H16_TILE = H16_KT * D * 2;        // 18432 bytes (bf16)
+constexpr int H16_DMA = H16_TILE / 1024;        // 18 wave-wide 1 KB transfers
+constexpr int H16_GSTRIDE = H16_KT * 128;       // bytes per 128-byte column group
+
+// fp8 tiles: 32 keys x 576 bytes = 18432 bytes, laid out as
+// [9 column groups of 64 B][32 keys][4 x 16-byte chunks] with the chunk
+// position XOR-swizzled by f(key) = ((key >> 2) + (key >> 4)) & 3, which keeps
+// both the 8-byte K reads and the 8-bit transposed V reads spread over banks.
+constexpr int F8_KT = 32;
+constexpr int F8_GSTRIDE = F8_KT * 64;
+
+__device__ __forceinline__ int f8_swz(int key) { return ((key >> 2) + (key >> 4)) & 3; }
+
+// 8 e4m3fn codes -> 8 bf16 (exact).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8_v(uint2 w) {
+  return __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(w.x, w.y));
+}
+
+__device__ __forceinline__ uint2 read_vt8(const char* p) {
+  typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(p)));
+}
+
+template <int KVT>
+__global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
+  constexpr bool F8 = KVT == MLA_DTYPE_FP8_E4M3FN;
+  constexpr int KT = F8 ? F8_KT : H16_KT;          // keys per wave tile
+  constexpr int ROWB = F8 ? D : D * 2;             // bytes per cached row
+  constexpr int TILE = KT * ROWB;                  // 18432 either way
+  constexpr int NDMA = TILE / 1024;                // 18
+  static_assert(TILE == H16_TILE, "same LDS budget for both caches");
+  __shared__ __attribute__((aligned(1024))) char smem[4 * 2 * H16_TILE];   // 147456 bytes
+
+  const int n_items = p.header[0];
+  const int item_id = blockIdx.x;
+  if (item_id >= n_items) return;
+  const int32_t* it = p.items + (size_t)item_id * ITEM_INTS;
+  // work-item fields are uniform: keep them (and all tile addressing derived
+  // from them) in SGPRs, so no vector load ever enters the DMA vmcnt queue
+  const int b = __builtin_amdgcn_readfirstlane(it[0]);
+  const int t0 = __builtin_amdgcn_readfirstlane(it[2]);
+  const int t1 = __builtin_amdgcn_readfirstlane(it[3]);
+  const int slot = __builtin_amdgcn_readfirstlane(it[4]);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+
+  const int L = __builtin_amdgcn_readfirstlane(min(max(p.seq_lens[b], 0), p.max_keys));
+  const int row = c16;
+  const bool row_ok = row < p.rows;
+  int limit = 0;
+  if (row_ok) {
+    int tok = row / p.heads;
+    int vis = p.causal ? L - p.s_q + 1 + tok : L;
+    limit = min(vis, t1);
+  }
+
+  bf16x8_t qb[D / 32];
+  {
+    const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
+                       : make_uint4(0, 0, 0, 0);
+      qb[s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  // Consume the q loads here, so the compiler's own vmcnt wait for them sits
+  // before the first DMA and not inside the tile loop (it cannot see the DMAs).
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) asm volatile("" ::"v"(qb[s]));
+
+  f32x4_t o[DV / 16];
+#pragma unroll
+  for (int d = 0; d < DV / 16; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  // ---- lane constants (LDS byte offsets inside a tile, DMA source offsets) ----
+  uint32_t dma_lane[2];
+  int kb[2][2];   // K operand: [M tile][s & 1], add (s >> 1) * column-group stride
+  int vt[4];      // V^T operand: [dt & 3], add (dt >> 2) * column-group stride
+  if constexpr (!F8) {
+    dma_lane[0] = dma_lane[1] = (lane >> 3) * ROWB + (((lane & 7) ^ (lane >> 3)) << 4);
+    kb[0][0] = c16 * 128 + ((g ^ (c16 & 7)) << 4);
+    kb[0][1] = c16 * 128 + (((4 + g) ^ (c16 & 7)) << 4);
+    kb[1][0] = kb[0][0];
+    kb[1][1] = kb[0][1];
+    const int j = c16 >> 2, q = c16 & 3;
+    const int lanex = (q >> 1) ^ ((g & 1) << 2) ^ j;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vt[c] = (4 * g + j) * 128 + (((2 * c) ^ lanex) << 4) + (q & 1) * 8;
+  } else {
+    // DMA transfer n: column group n >> 1, keys 16*(n & 1) + (lane >> 2), chunk
+    // position lane & 3; f(key) = ((lane >> 4) + (n & 1)) & 3.
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      dma_lane[h] = (lane >> 2) * ROWB + (((lane & 3) ^ (((lane >> 4) + h) & 3)) << 4);
+    // K: key 16*mi + c16, bytes 32*s + 8*g -> chunk 2*s + (g >> 1), half g & 1
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        kb[mi][h] = (16 * mi + c16) * 64 +
+                    (((2 * h + (g >> 1)) ^ f8_swz(16 * mi + c16)) << 4) + (g & 1) * 8;
+    // V^T: lane s = 2*jj + q supplies V[key_jj][16*dt + 8*q ..+7] with key_jj =
+    // 4g + jj (jj < 4) or 16 + 4g + jj - 4, so ds_read_b64_tr_b8 hands lane
+    // c16 the 8 values V[key_0..7][16*dt + c16].
+    const int jj = c16 >> 1, q = c16 & 1;
+    const int key = jj < 4 ? 4 * g + jj : 16 + 4 * g + (jj - 4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vt[c] = key * 64 + ((c ^ f8_swz(key)) << 4) + q * 8;
+  }
+  constexpr int GSTRIDE = F8 ? F8_GSTRIDE : H16_GSTRIDE;
+
+  // The block table is read-only for the whole kernel: reading it through the
+  // constant address space keeps these uniform loads on the scalar unit, so
+  // they never enter the vmcnt queue the DMA waits below count on.
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32* bt = (const_i32*)(p.block_table + (size_t)b * p.max_blocks);
+  char* wbuf = smem + w * 2 * H16_TILE;
+  const int ntiles = (t1 - t0 + KT - 1) / KT;
+
+  // Issue the NDMA transfers of tile j into dst (always NDMA VMEM
+  // instructions, so the vmcnt arithmetic below is exact). Keys past the end
+  // are fetched from a valid row of the page and zeroed after arrival.
+  auto issue = [&](int j, char* dst) {
+    const int ts = t0 + KT * j;
+    int page = bt[ts / p.bs];
+    if (page < 0 || page >= p.num_blocks) page = 0;
+    const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts % p.bs)) * ROWB;
+    const uint32_t l0 = lds_addr(dst);
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) {
+      if constexpr (!F8)
+        lds_dma16_nt(src + (n & 1) * 8 * ROWB + (n >> 1) * 128, dma_lane[0], l0 + n * 1024);
+      else
+        lds_dma16(src + (n & 1) * 16 * ROWB + (n >> 1) * 64, dma_lane[n & 1], l0 + n * 1024);
+    }
+  };
+  auto valid_keys = [&](int j) {
+    const int ts = t0 + KT * j;
+    int page = bt[ts / p.bs];
+    if (page < 0 || page >= p.num_blocks) return 0;
+    return min(KT, t1 - ts);
+  };
+  auto fix_tail = [&](int nv, char* buf) {
+    if (nv >= KT) return;
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) {
+      const int key = F8 ? (n & 1) * 16 + (lane >> 2) : (n & 1) * 8 + (lane >> 3);
+      if (key >= nv) *reinterpret_cast<uint4*>(buf + n * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  // Make tile j (this wave's itn-th) resident: issue the DMA of tile j + 4,
+  // wait for tile j, zero its keys past the end. Returns its LDS buffer.
+  auto prepare = [&](int j, int itn) -> const char* {
+    char* cur = wbuf + (itn & 1) * H16_TILE;
+    const bool has_next = j + 4 < ntiles;
+    mem_fence_compiler();
+    if (has_next) {
+      issue(j + 4, wbuf + ((itn + 1) & 1) * H16_TILE);
+      wait_vmcnt<NDMA>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    mem_fence_compiler();
+    fix_tail(valid_keys(j), cur);
+    return cur;
+  };
+
+  // One tile: S^T, softmax, O^T += V^T P^T. The fast variant never touches
+  // the accumulators with VALU code and returns false (before consuming the
+  // tile) if a row's max jumped more than BIG_SLACK above its reference.
+  auto compute = [&](const char* cur, int ts, auto slow_tag) -> bool {
+    constexpr bool SLOW = decltype(slow_tag)::value;
+    constexpr int MT = KT / 16;
+    f32x4_t sacc[MT];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) sacc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        bf16x8_t a;
+        if constexpr (!F8)
+          a = *reinterpret_cast<const bf16x8_t*>(cur + kb[mi][s & 1] + (s >> 1) * GSTRIDE);
+        else
+          a = fp8x8_to_bf16x8_v(*reinterpret_cast<const uint2*>(cur + kb[mi][s & 1] + (s >> 1) * GSTRIDE));
+        sacc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc[mi], 0, 0, 0);
+      }
+    }
+
+    float x[MT][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int key = ts + 16 * mi + 4 * g + jj;
+        float v = sacc[mi][jj] * p.scale_log2;
+        v = key < limit ? v : -INFINITY;
+        x[mi][jj] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = wave_max_across_groups(tmax);
+    if constexpr (!SLOW) {
+      if (m_run == -INFINITY) m_run = tmax;   // o and l of this row are still zero
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + BIG_SLACK)) return false;
+    } else {
+      const bool need = tmax > m_run;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        float alpha = 1.f;
+        if (need) {
+          alpha = exp2f(m_run - tmax);   // m_run = -inf gives 0
+          m_run = tmax;
+        }
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DV / 16; ++d) o[d] *= alpha;
+      }
+    }
+    float pv[MT][4];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float e = m_run == -INFINITY ? 0.f : exp2f(x[mi][jj] - m_run);
+        pv[mi][jj] = e;
+        l_run += e;
+      }
+
+    if constexpr (!F8) {
+      const s16x4_t pb = __builtin_bit_cast(
+          s16x4_t, make_uint2(pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3])));
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        const s16x4_t a = read_vt(cur + vt[dt & 3] + (dt >> 2) * GSTRIDE);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[dt], 0, 0, 0);
+      }
+    } else {
+      // k-slots 0..3: keys 4g..4g+3 of M tile 0; 4..7: of M tile 1 (same in A)
+      const bf16x8_t pb = __builtin_bit_cast(
+          bf16x8_t, make_uint4(pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
+                               pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])));
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        const bf16x8_t a = fp8x8_to_bf16x8_v(read_vt8(cur + vt[dt & 3] + (dt >> 2) * GSTRIDE));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
+      }
+    }
+    return true;
+  };
+
+  int j = w, itn = 0;
+  const char* cur = nullptr;
+  if (w < ntiles) issue(w, wbuf);
+  for (; j < ntiles; j += 4, ++itn) {
+    cur = prepare(j, itn);
+    if (!compute(cur, t0 + KT * j, std::false_type{})) break;
+  }
+  if (j < ntiles) {   // rare: finish with rescaling, starting at the resident tile j
+    compute(cur, t0 + KT * j, std::true_type{});
+    for (j += 4, ++itn; j < ntiles; j += 4, ++itn)
+      compute(prepare(j, itn), t0 + KT * j, std::true_type{});
+  }
+  __syncthreads();
+  merge_and_store<4>(p, smem, o, m_run, l_run, b, 0, slot);
+}
+
+}  // namespace
+
+namespace mla_detail {
+
+void launch_narrow(int kv_dtype, dim3 grid, hipStream_t st, const FwdParams& fp) {
+  if (kv_dtype == MLA_DTYPE_BF16)
+    hipLaunchKernelGGL((mla_decode_narrow<MLA_DTYPE_BF16>), grid, dim3(NTHREADS), 0, st, fp);
+  else
+    hipLaunchKernelGGL((mla_decode_narrow<MLA_DTYPE_FP8_E4M3FN>), grid, dim3(NTHREADS), 0, st, fp);
+}
+
+}  // namespace mla_detail
