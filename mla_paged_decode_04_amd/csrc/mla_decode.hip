@@ -15,8 +15,9 @@
 //                          (fp32 normalised o, base-2 lse):
 //        mla_decode_narrow  <= 16 query rows per sequence (HBM-bound): every
 //                           wave streams its own key tiles HBM -> LDS
-//        mla_decode_wide    up to 64 / 128 rows per item (MFMA-heavy): the 4
-//                           waves share 64-key tiles, each owns 16 / 32 rows
+//        mla_decode_wide    32 / 64 / 128 rows per item (MFMA-heavy): two
+//                           wave pairs share the key tiles; the waves of a
+//                           pair split the head dimensions
 //   3. mla_combine_kernel  merges the partials of split (sequence, row group)
 //                          pairs with log-sum-exp weights
 #include <algorithm>
@@ -347,7 +348,8 @@ mla_status_t launch_decode_kernel(const void* q, const void* kv_cache,
   fp.num_blocks = desc->num_blocks;
   fp.scale_log2 = softmax_scale * kv_scale * LOG2E;
   fp.out_scale = kv_scale;
-  dim3 grid(static_cast<unsigned>(ws.max_items));
+  // a multiple of 8 workgroups: the wide kernel deals items out per XCD
+  dim3 grid(static_cast<unsigned>((ws.max_items + 7) / 8 * 8));
   launch_decode(desc->kv_dtype, rc.kind, grid, hs, fp);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   if (!combine) return MLA_OK;

@@ -24,6 +24,24 @@ constexpr int W_NTK = 32;                         // keys per tile
 constexpr int W_TILE = W_NTK * D * 2;             // 36864 bytes (bf16 tile)
 constexpr int W_RAW8 = W_NTK * D;                 // 18432 bytes (raw fp8 tile)
 constexpr int W_GSTRIDE = W_NTK * 128;            // bytes per 128-byte column group
+#ifndef QK_AHEAD
+#define QK_AHEAD 8                                // K-operand LDS reads kept in flight
+#endif
+
+// Max over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) with
+// gfx950's row-swap permutes: v_permlane32_swap exchanges the two 32-lane
+// halves of its operands, v_permlane16_swap the odd and even 16-lane rows
+// (VALU only, no LDS round trip as with ds_bpermute). Issued from inline asm:
+// the compiler folds max(swap(x, x)) to x, as if a swap of a value with itself
+// moved nothing. The s_nop pairs cover the VALU-write -> permlane hazards.
+__device__ __forceinline__ float max_across_groups(float v) {
+  float y = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(v), "+v"(y));
+  v = fmaxf(v, y);
+  y = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(v), "+v"(y));
+  return fmaxf(v, y);
+}
 
 __device__ __forceinline__ int w_off(int key, int c) {
   return (((c >> 3) * W_NTK + key) << 7) + (((c & 7) ^ (key & 7)) << 4);
@@ -42,8 +60,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
   char* const raw8 = smem;                          // fp8: 4 x 18432
   char* const bfbuf = smem + (F8 ? 4 * W_RAW8 : 0); // fp8: 2 x 36864
 
+  // XCD-aware item order: consecutive workgroups go to different XCDs, so
+  // hand each XCD a contiguous run of items (the row groups and chunks of one
+  // sequence then share that XCD's L2). The grid is a multiple of 8.
   const int n_items = p.header[0];
-  const int item_id = blockIdx.x;
+  const int per_xcd = (n_items + 7) >> 3;
+  const int xw = blockIdx.x;
+  if ((xw >> 3) >= per_xcd) return;
+  const int item_id = (xw & 7) * per_xcd + (xw >> 3);
   if (item_id >= n_items) return;
   const int32_t* it = p.items + (size_t)item_id * ITEM_INTS;
   // uniform work-item fields, pinned to SGPRs (see the narrow kernel)
@@ -222,6 +246,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
         sacc[h][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc[h][s & 1], 0, 0, 0);
       }
     }
+    // Keep QK_AHEAD K-operand reads in flight ahead of the MFMAs: with one
+    // wave per SIMD nothing else hides the LDS latency.
+#pragma unroll
+    for (int i = 0; i < QK_AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < D / 16 - QK_AHEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < QK_AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 
     // ---- online softmax (lane = one row, 8 keys) ----
     float x[2][4];
@@ -236,7 +271,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
         x[h][jj] = v;
         tmax = fmaxf(tmax, v);
       }
-    tmax = wave_max_across_groups(tmax);
+    tmax = max_across_groups(tmax);
     if constexpr (!SLOW) {
       if (m_run == -INFINITY) m_run = tmax;   // o and l of this row are still zero
       if (__builtin_amdgcn_ballot_w64(tmax > m_run + BIG_SLACK)) return false;
@@ -258,7 +293,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        e[h][jj] = m_run == -INFINITY ? 0.f : exp2f(x[h][jj] - m_run);
+        e[h][jj] = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[h][jj] - m_run);
         l_run += e[h][jj];
       }
     const bf16x8_t pb = __builtin_bit_cast(
