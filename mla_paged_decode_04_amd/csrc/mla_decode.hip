@@ -29,6 +29,151 @@ using namespace mla_detail;
 
 namespace {
 
+constexpr int TARGET_ITEMS = 256;    // automatic split: about one work item per CU
+constexpr int MIN_CHUNK = 256;       // shortest automatic split chunk (keys)
+constexpr int HEADER_BYTES = 256;
+
+// ---------------------------------------------------------------------------
+// shared host/device planning arithmetic
+// ---------------------------------------------------------------------------
+
+// Row grouping: kind 0 = narrow kernel (<= 16 rows), kind 1 = wide kernel
+// with 16 rows per wave (64-row items). (A wide variant with 32 rows per wave,
+// 128-row items, exists as a template but does not fit the register file
+// without spilling, so it is not selected.)
+struct RowCfg {
+  int kind;
+  int rgs;     // query rows per work item
+  int nrg;     // row groups per sequence
+  int target;  // work items the automatic split aims for
+};
+
+__host__ __device__ inline RowCfg row_config(int rows) {
+  RowCfg c;
+  c.kind = rows <= 16 ? 0 : 1;
+  c.rgs = c.kind == 0 ? 16 : 64;
+  c.nrg = (rows + c.rgs - 1) / c.rgs;
+  c.target = TARGET_ITEMS;
+  return c;
+}
+
+__host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Split of one sequence's key range [0, keys) into n chunks of `len` keys
+// (len a multiple of the tile); keys == 0 still yields one (empty) chunk.
+__host__ __device__ inline void seq_split(int keys, int chunk, int* n, int* len) {
+  if (keys <= 0) { *n = 1; *len = 0; return; }
+  int n0 = (keys + chunk - 1) / chunk;
+  int l = round_up((keys + n0 - 1) / n0, NT);
+  *len = l;
+  *n = (keys + l - 1) / l;
+}
+
+__host__ __device__ inline int chunk_from_work(long long work, int forced, int target) {
+  if (forced > 0) return forced;
+  long long c = (work + target - 1) / target;
+  c = (c + NT - 1) / NT * NT;
+  if (c < MIN_CHUNK) c = MIN_CHUNK;
+  if (c > (1LL << 30)) c = 1LL << 30;
+  return static_cast<int>(c);
+}
+
+// Automatic chunk length: the decode kernels run one workgroup per CU, so a
+// plan is a list schedule of work items on SLOTS workers. For few (sequence,
+// row group) pairs the chunk is chosen among CHUNK_CANDIDATES lengths between
+// work / (4 * SLOTS) and twice work / SLOTS by an estimate of the makespan in
+// key units: every item costs its keys plus ITEM_OVERHEAD (prologue, first
+// tile latency, partial write); with n items of at most mx keys and wk keys
+// in all,
+//   n <= SLOTS : mx + ITEM_OVERHEAD
+//   otherwise  : max(mx + o, ceil((wk + n * o) / SLOTS) + (mx + o) / 2).
+// Ties go to the longer chunk (fewer partials). With many pairs the split
+// from the average (work / SLOTS) is kept. All integer, so the host mirror
+// reproduces the device plan exactly. (A batch of equal lengths keeps the
+// average split: every item then has the same length.)
+constexpr int SLOTS = 256;
+constexpr int CHUNK_CANDIDATES = 32;
+constexpr int ITEM_OVERHEAD = 96;
+constexpr int SEARCH_MAX_PAIRS = 1024;
+
+struct ChunkRange {
+  int lo, hi;
+  bool search;
+};
+
+__host__ __device__ inline ChunkRange chunk_range(long long work, int pairs, bool uniform, int forced,
+                                                  int target) {
+  ChunkRange r;
+  const int c0 = chunk_from_work(work, forced, target);
+  r.search = forced == 0 && pairs < SEARCH_MAX_PAIRS && !uniform;
+  r.lo = r.hi = c0;
+  if (r.search) {
+    r.lo = chunk_from_work(work, 0, 4 * SLOTS);
+    r.hi = c0 >= (1 << 29) ? c0 : 2 * c0;
+  }
+  return r;
+}
+
+// Candidate k: lo + k * step with step = ceil((hi - lo) / (candidates - 1))
+// rounded up to 64 keys, capped at hi.
+__host__ __device__ inline int chunk_step(const ChunkRange& r) {
+  return round_up((r.hi - r.lo + CHUNK_CANDIDATES - 2) / (CHUNK_CANDIDATES - 1), NT);
+}
+
+__host__ __device__ inline int chunk_candidate(const ChunkRange& r, int step, int k) {
+  const long long c = r.lo + (long long)step * k;
+  return c < r.hi ? (int)c : r.hi;
+}
+
+__host__ __device__ inline unsigned long long plan_cost(unsigned long long n, unsigned long long mx,
+                                                        unsigned long long wk) {
+  const unsigned long long o = ITEM_OVERHEAD;
+  if (n <= SLOTS) return mx + o;
+  const unsigned long long avg = ((wk + n * o + SLOTS - 1) >> 8) + ((mx + o) >> 1);
+  static_assert(SLOTS == 256, "the shift above divides by SLOTS");
+  return avg > mx + o ? avg : mx + o;
+}
+
+// Upper bound on work items (and partial slots) for a description.
+inline long long max_items_bound(int batch, int rows, int max_keys, int forced) {
+  RowCfg rc = row_config(rows);
+  long long per_seq_cap = (max_keys + NT - 1) / NT;             // chunks are >= 64 keys
+  if (forced > 0) per_seq_cap = (max_keys + forced - 1) / forced;
+  if (per_seq_cap < 1) per_seq_cap = 1;
+  long long cap = (long long)rc.nrg * batch * per_seq_cap;
+  if (forced == 0) {
+    // the chunk is at least work / (4 * SLOTS): at most 4 * SLOTS items beyond
+    // one per (sequence, row group)
+    long long auto_cap = 4LL * SLOTS + (long long)rc.nrg * batch;
+    long long min_cap = (long long)rc.nrg * batch * ((max_keys + MIN_CHUNK - 1) / MIN_CHUNK);
+    if (min_cap < (long long)rc.nrg * batch) min_cap = (long long)rc.nrg * batch;
+    if (auto_cap < cap) cap = auto_cap;
+    if (min_cap < cap) cap = min_cap;
+  }
+  return cap;
+}
+
+struct WsLayout {
+  size_t items, pairs, part_lse, part_o, total;
+  long long max_items;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline WsLayout ws_layout(int batch, int s_q, int heads, int max_keys, int forced) {
+  int rows = s_q * heads;
+  RowCfg rc = row_config(rows);
+  WsLayout w;
+  w.max_items = max_items_bound(batch, rows, max_keys, forced);
+  size_t off = HEADER_BYTES;
+  w.items = off;   off = align256(off + (size_t)w.max_items * ITEM_INTS * 4);
+  w.pairs = off;   off = align256(off + (size_t)batch * rc.nrg * 2 * 4);
+  w.part_lse = off; off = align256(off + (size_t)w.max_items * rc.rgs * 4);
+  w.part_o = off;  off = align256(off + (size_t)w.max_items * rc.rgs * DV * 4);
+  w.total = off;
+  return w;
+}
+
 // ---------------------------------------------------------------------------
 // planner
 // ---------------------------------------------------------------------------
@@ -57,12 +202,15 @@ __device__ __forceinline__ T wave_inclusive_scan(T v) {
 }
 
 // One workgroup. Thread t owns the contiguous sequences [t*per, (t+1)*per);
-// seq_lens are read once into LDS. Two block-wide steps: the total work
-// (sum of row groups x keys rounded to 64) fixes the chunk length, then an
-// exclusive scan of per-thread item / partial-slot counts places every item.
+// seq_lens are read once into LDS. Block-wide steps: the total work (sum of
+// row groups x keys rounded to 64) bounds the chunk length, the candidate
+// chunks are costed (few pairs only), then an exclusive scan of per-thread
+// item / partial-slot counts places every item.
 __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
   extern __shared__ int32_t s_len[];          // batch entries
-  __shared__ long long s_work[PLAN_WAVES];
+  __shared__ long long s_work[PLAN_WAVES], s_keys[PLAN_WAVES];
+  __shared__ int s_min[PLAN_WAVES], s_max[PLAN_WAVES];
+  __shared__ int s_cnt[CHUNK_CANDIDATES], s_mx[CHUNK_CANDIDATES];
   __shared__ int s_items[PLAN_WAVES], s_slots[PLAN_WAVES], s_flag[PLAN_WAVES];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
 
@@ -77,23 +225,87 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
   const int per = (p.batch + PLAN_THREADS - 1) / PLAN_THREADS;
   const int b0 = min(p.batch, tid * per);
   const int b1 = min(p.batch, b0 + per);
-  long long work = 0;
-  for (int b = b0; b < b1; ++b) work += (long long)p.nrg * round_up(s_len[b], NT);
-  work = wave_inclusive_scan(work);
+  long long work = 0, keys = 0;
+  int lmin = INT32_MAX, lmax = 0;
+  for (int b = b0; b < b1; ++b) {
+    work += (long long)p.nrg * round_up(s_len[b], NT);
+    keys += (long long)p.nrg * s_len[b];
+    lmin = min(lmin, s_len[b]);
+    lmax = max(lmax, s_len[b]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {   // four independent reductions per step
+    work += __shfl_xor(work, off);
+    keys += __shfl_xor(keys, off);
+    lmin = min(lmin, __shfl_xor(lmin, off));
+    lmax = max(lmax, __shfl_xor(lmax, off));
+  }
   const int any_clamped = __any(clamped);
-  if (lane == 63) {
+  if (lane == 0) {
     s_work[wv] = work;
+    s_keys[wv] = keys;
+    s_min[wv] = lmin;
+    s_max[wv] = lmax;
     s_flag[wv] = any_clamped;
   }
   __syncthreads();
-  long long total = 0;
+  long long total = 0, total_keys = 0;
   int flag = 0;
+  lmin = INT32_MAX;
+  lmax = 0;
 #pragma unroll
   for (int i = 0; i < PLAN_WAVES; ++i) {
     total += s_work[i];
+    total_keys += s_keys[i];
+    lmin = min(lmin, s_min[i]);
+    lmax = max(lmax, s_max[i]);
     flag |= s_flag[i];
   }
-  const int chunk = chunk_from_work(total, p.forced_chunk, p.target);
+  const ChunkRange cr = chunk_range(total, p.batch * p.nrg, lmin == lmax, p.forced_chunk, p.target);
+  int chunk = cr.lo;
+  if (cr.search) {
+    // items and longest item for every candidate chunk (8 threads per
+    // candidate, all candidates at once), then the cheapest
+    constexpr int TPC = PLAN_THREADS / CHUNK_CANDIDATES;
+    static_assert(TPC == 8, "three xor steps below");
+    const int step = chunk_step(cr);
+    {
+      const int k = tid / TPC, sub = tid % TPC;
+      const int c = chunk_candidate(cr, step, k);
+      int cnt = 0, mx = 0;
+      for (int b = sub; b < p.batch; b += TPC) {
+        int n, len;
+        seq_split(s_len[b], c, &n, &len);
+        cnt += n;
+        mx = max(mx, min(len, s_len[b]));
+      }
+#pragma unroll
+      for (int off = 1; off < TPC; off <<= 1) {
+        cnt += __shfl_xor(cnt, off);
+        mx = max(mx, __shfl_xor(mx, off));
+      }
+      if (sub == 0) {
+        s_cnt[k] = cnt;
+        s_mx[k] = mx;
+      }
+    }
+    __syncthreads();
+    // argmin over the candidates in one wave (ties: the larger k)
+    unsigned long long cost = ~0ull;
+    int kb = lane;
+    if (lane < CHUNK_CANDIDATES)
+      cost = plan_cost((unsigned long long)s_cnt[lane] * p.nrg, s_mx[lane], total_keys);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const unsigned long long oc = __shfl_xor(cost, off);
+      const int ok = __shfl_xor(kb, off);
+      if (oc < cost || (oc == cost && ok > kb)) {
+        cost = oc;
+        kb = ok;
+      }
+    }
+    chunk = chunk_candidate(cr, step, kb);
+  }
 
   int my_items = 0, my_slots = 0;
   for (int b = b0; b < b1; ++b) {
@@ -412,12 +624,38 @@ int32_t mla_plan_host(const int32_t* seq_lens_host, int32_t s_q, const mla_decod
     return -1;
   RowCfg rc = row_config(s_q * desc->num_heads);
   const int max_keys = max_keys_of(desc);
-  long long work = 0;
+  long long work = 0, keys = 0;
+  int lmin = INT32_MAX, lmax = 0;
   for (int b = 0; b < desc->batch; ++b) {
     int L = std::min(std::max(seq_lens_host[b], 0), max_keys);
     work += (long long)rc.nrg * round_up(L, NT);
+    keys += (long long)rc.nrg * L;
+    lmin = std::min(lmin, L);
+    lmax = std::max(lmax, L);
   }
-  const int chunk = chunk_from_work(work, desc->split_keys, rc.target);
+  const ChunkRange cr = chunk_range(work, desc->batch * rc.nrg, lmin == lmax, desc->split_keys, rc.target);
+  int chunk = cr.lo;
+  if (cr.search) {
+    const int step = chunk_step(cr);
+    unsigned long long best = ~0ull;
+    for (int k = 0; k < CHUNK_CANDIDATES; ++k) {
+      const int c = chunk_candidate(cr, step, k);
+      long long n = 0;
+      int mx = 0;
+      for (int b = 0; b < desc->batch; ++b) {
+        int L = std::min(std::max(seq_lens_host[b], 0), max_keys);
+        int nb, len;
+        seq_split(L, c, &nb, &len);
+        n += nb;
+        mx = std::max(mx, std::min(len, L));
+      }
+      const unsigned long long cost = plan_cost((unsigned long long)n * rc.nrg, mx, keys);
+      if (cost <= best) {
+        best = cost;
+        chunk = c;
+      }
+    }
+  }
   if (rows_per_item) *rows_per_item = rc.rgs;
   if (chunk_keys) *chunk_keys = chunk;
   int item = 0, slot = 0;

@@ -17,9 +17,6 @@ constexpr int DV = MLA_D_V;          // 512
 constexpr int NT = 64;               // key granularity of split chunks
 constexpr int NTHREADS = 256;        // 4 wave64 per workgroup
 constexpr int OSTRIDE = DV + 4;      // fp32 row stride of the output staging
-constexpr int TARGET_ITEMS = 256;    // automatic split: about one work item per CU
-constexpr int MIN_CHUNK = 256;       // shortest automatic split chunk (keys)
-constexpr int HEADER_BYTES = 256;
 constexpr int ITEM_INTS = 8;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -36,89 +33,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
-
-// ---------------------------------------------------------------------------
-// shared host/device planning arithmetic
-// ---------------------------------------------------------------------------
-
-// Row grouping: kind 0 = narrow kernel (<= 16 rows), kind 1 = wide kernel
-// with 16 rows per wave (64-row items). (A wide variant with 32 rows per wave,
-// 128-row items, exists as a template but does not fit the register file
-// without spilling, so it is not selected.)
-struct RowCfg {
-  int kind;
-  int rgs;     // query rows per work item
-  int nrg;     // row groups per sequence
-  int target;  // work items the automatic split aims for
-};
-
-__host__ __device__ inline RowCfg row_config(int rows) {
-  RowCfg c;
-  c.kind = rows <= 16 ? 0 : 1;
-  c.rgs = c.kind == 0 ? 16 : 64;
-  c.nrg = (rows + c.rgs - 1) / c.rgs;
-  c.target = TARGET_ITEMS;
-  return c;
-}
-
-__host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
-
-// Split of one sequence's key range [0, keys) into n chunks of `len` keys
-// (len a multiple of the tile); keys == 0 still yields one (empty) chunk.
-__host__ __device__ inline void seq_split(int keys, int chunk, int* n, int* len) {
-  if (keys <= 0) { *n = 1; *len = 0; return; }
-  int n0 = (keys + chunk - 1) / chunk;
-  int l = round_up((keys + n0 - 1) / n0, NT);
-  *len = l;
-  *n = (keys + l - 1) / l;
-}
-
-__host__ __device__ inline int chunk_from_work(long long work, int forced, int target) {
-  if (forced > 0) return forced;
-  long long c = (work + target - 1) / target;
-  c = (c + NT - 1) / NT * NT;
-  if (c < MIN_CHUNK) c = MIN_CHUNK;
-  if (c > (1LL << 30)) c = 1LL << 30;
-  return static_cast<int>(c);
-}
-
-// Upper bound on work items (and partial slots) for a description.
-inline long long max_items_bound(int batch, int rows, int max_keys, int forced) {
-  RowCfg rc = row_config(rows);
-  long long per_seq_cap = (max_keys + NT - 1) / NT;             // chunks are >= 64 keys
-  if (forced > 0) per_seq_cap = (max_keys + forced - 1) / forced;
-  if (per_seq_cap < 1) per_seq_cap = 1;
-  long long cap = (long long)rc.nrg * batch * per_seq_cap;
-  if (forced == 0) {
-    long long auto_cap = rc.target + (long long)rc.nrg * batch;
-    long long min_cap = (long long)rc.nrg * batch * ((max_keys + MIN_CHUNK - 1) / MIN_CHUNK);
-    if (min_cap < (long long)rc.nrg * batch) min_cap = (long long)rc.nrg * batch;
-    if (auto_cap < cap) cap = auto_cap;
-    if (min_cap < cap) cap = min_cap;
-  }
-  return cap;
-}
-
-struct WsLayout {
-  size_t items, pairs, part_lse, part_o, total;
-  long long max_items;
-};
-
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-inline WsLayout ws_layout(int batch, int s_q, int heads, int max_keys, int forced) {
-  int rows = s_q * heads;
-  RowCfg rc = row_config(rows);
-  WsLayout w;
-  w.max_items = max_items_bound(batch, rows, max_keys, forced);
-  size_t off = HEADER_BYTES;
-  w.items = off;   off = align256(off + (size_t)w.max_items * ITEM_INTS * 4);
-  w.pairs = off;   off = align256(off + (size_t)batch * rc.nrg * 2 * 4);
-  w.part_lse = off; off = align256(off + (size_t)w.max_items * rc.rgs * 4);
-  w.part_o = off;  off = align256(off + (size_t)w.max_items * rc.rgs * DV * 4);
-  w.total = off;
-  return w;
-}
 
 // ---------------------------------------------------------------------------
 // device helpers
