@@ -69,10 +69,9 @@ __device__ __forceinline__ float wave_sum_across_groups(float v) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = static_cast<__bf16>(a);
-  __bf16 y = static_cast<__bf16>(b);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, y)) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  // one v_cvt_pk_bf16_f32 (round to nearest even)
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
 // Transposed 64-bit LDS read (see the V^T operand set-up in the decode kernel).

@@ -31,15 +31,16 @@ constexpr int W_GSTRIDE = W_NTK * 128;            // bytes per 128-byte column g
 // Max over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) with
 // gfx950's row-swap permutes: v_permlane32_swap exchanges the two 32-lane
 // halves of its operands, v_permlane16_swap the odd and even 16-lane rows
-// (VALU only, no LDS round trip as with ds_bpermute). Issued from inline asm:
-// the compiler folds max(swap(x, x)) to x, as if a swap of a value with itself
-// moved nothing. The s_nop pairs cover the VALU-write -> permlane hazards.
+// (VALU only, no LDS round trip as with ds_bpermute). Issued from inline asm
+// (not volatile, so it stays free to schedule): through the builtins the
+// compiler folds max(swap result 0, swap result 1) to result 0. The s_nop
+// pairs cover the VALU-write -> permlane hazards.
 __device__ __forceinline__ float max_across_groups(float v) {
   float y = v;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(v), "+v"(y));
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(v), "+v"(y));
   v = fmaxf(v, y);
   y = v;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(v), "+v"(y));
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(v), "+v"(y));
   return fmaxf(v, y);
 }
 
@@ -235,15 +236,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
     constexpr bool SLOW = decltype(slow_tag)::value;
 
     // ---- S^T for 32 keys (two M tiles) x this wave's 16 rows ----
-    f32x4_t sacc[2][2];   // [M tile][even/odd k-step]: four independent chains
+    f32x4_t sacc[2];   // [M tile]: two independent accumulation chains
 #pragma unroll
-    for (int h = 0; h < 2; ++h) sacc[h][0] = sacc[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) sacc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(cur + kb[h][s & 1] + (s >> 1) * W_GSTRIDE);
-        sacc[h][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc[h][s & 1], 0, 0, 0);
+        sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc[h], 0, 0, 0);
       }
     }
     // Keep QK_AHEAD K-operand reads in flight ahead of the MFMAs: with one
@@ -258,20 +259,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < QK_AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 
-    // ---- online softmax (lane = one row, 8 keys) ----
+    // ---- online softmax (lane = one row, 8 keys), on the raw scores: the
+    // scale is folded into the max and into the exponent's FMA ----
     float x[2][4];
-    float tmax = -INFINITY;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int key = ts + 16 * h + 4 * g + jj;
-        float v = (sacc[h][0][jj] + sacc[h][1][jj]) * p.scale_log2;
-        v = key < limit ? v : -INFINITY;
-        x[h][jj] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = max_across_groups(tmax);
+      for (int jj = 0; jj < 4; ++jj) x[h][jj] = sacc[h][jj];
+    if (__builtin_amdgcn_ballot_w64(ts + W_NTK > limit)) {   // a tile that reaches a row's limit
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int key = ts + 16 * h + 4 * g + jj;
+          x[h][jj] = key < limit ? x[h][jj] : -INFINITY;
+        }
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+    tmax = max_across_groups(tmax) * p.scale_log2;
     if constexpr (!SLOW) {
       if (m_run == -INFINITY) m_run = tmax;   // o and l of this row are still zero
       if (__builtin_amdgcn_ballot_w64(tmax > m_run + BIG_SLACK)) return false;
@@ -288,12 +294,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
         for (int d = 0; d < DV / 16; ++d) o[d] *= alpha;
       }
     }
+    // a row without any key so far keeps m = -inf: a finite stand-in makes its
+    // masked scores (-inf) give exp2(-inf) = 0, never NaN
+    const float neg_m = -fmaxf(m_run, -1e30f);
     float e[2][4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        e[h][jj] = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[h][jj] - m_run);
+        e[h][jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[h][jj], p.scale_log2, neg_m));
         l_run += e[h][jj];
       }
     const bf16x8_t pb = __builtin_bit_cast(
