@@ -43,23 +43,23 @@ __device__ __forceinline__ void merge_and_store(const FwdParams& p, char* smem,
   }
   __syncthreads();
 
-  constexpr int TPR = NTHREADS / RGS;   // threads per row
-  constexpr int DPT = DV / TPR;         // dims per thread
-  const int rr = tid / TPR;             // row within the item
-  const int d0 = (tid % TPR) * DPT;
-  const int rtile = rr / 16, rc = rr % 16;
+  // 16 threads per row; thread c of row rr handles dims 4c + 64i (i = 0..7):
+  // every LDS read and global write of 16 threads is one contiguous run
+  static_assert(KS == 4 && RGS == 16, "one 16-row tile merged over four waves");
+  const int rr = tid >> 4;
+  const int c4 = (tid & 15) * 4;
   float mk[KS], wk[KS];
   float M = -INFINITY;
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
-    mk[k] = mls[((rtile * KS + k) * 16 + rc) * 2];
+    mk[k] = mls[(k * 16 + rr) * 2];
     M = fmaxf(M, mk[k]);
   }
   float lsum = 0.f;
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
     wk[k] = mk[k] == -INFINITY ? 0.f : exp2f(mk[k] - M);
-    lsum += wk[k] * mls[((rtile * KS + k) * 16 + rc) * 2 + 1];
+    lsum += wk[k] * mls[(k * 16 + rr) * 2 + 1];
   }
   const int grow = rg * RGS + rr;
   const bool row_ok = grow < p.rows;
@@ -67,41 +67,28 @@ __device__ __forceinline__ void merge_and_store(const FwdParams& p, char* smem,
   const float inv = empty ? 0.f : p.out_scale / lsum;
   const float lse2 = empty ? -INFINITY : M + log2f(lsum);
   const size_t orow = (size_t)b * p.rows + grow;
-
-  if (slot < 0 && row_ok) {
-    uint16_t* dst = p.out + orow * DV + d0;
+  if (!row_ok) return;
+  f32x4_t acc[DV / 64];
 #pragma unroll
-    for (int d = 0; d < DPT; d += 8) {
-      float acc[8];
+  for (int i = 0; i < DV / 64; ++i) {
+    f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float s = 0.f;
+    for (int k = 0; k < KS; ++k)
+      a += wk[k] * *reinterpret_cast<const f32x4_t*>(ost + (k * 16 + rr) * OSTRIDE + c4 + 64 * i);
+    acc[i] = a * inv;
+  }
+  if (slot < 0) {
+    uint16_t* dst = p.out + orow * DV + c4;
 #pragma unroll
-        for (int k = 0; k < KS; ++k)
-          s += wk[k] * ost[((rtile * KS + k) * 16 + rc) * OSTRIDE + d0 + d + e];
-        acc[e] = s * inv;
-      }
-      *reinterpret_cast<uint4*>(dst + d) =
-          make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-    }
-    if (p.lse != nullptr && (tid % TPR) == 0) p.lse[orow] = lse2 * LN2;
-  } else if (slot >= 0 && row_ok) {
-    float* dst = p.part_o + ((size_t)slot * RGS + rr) * DV + d0;
+    for (int i = 0; i < DV / 64; ++i)
+      *reinterpret_cast<uint2*>(dst + 64 * i) =
+          make_uint2(pack_bf16x2(acc[i][0], acc[i][1]), pack_bf16x2(acc[i][2], acc[i][3]));
+    if (p.lse != nullptr && c4 == 0) p.lse[orow] = lse2 * LN2;
+  } else {
+    float* dst = p.part_o + ((size_t)slot * RGS + rr) * DV + c4;
 #pragma unroll
-    for (int d = 0; d < DPT; d += 4) {
-      f32x4_t acc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float s = 0.f;
-#pragma unroll
-        for (int k = 0; k < KS; ++k)
-          s += wk[k] * ost[((rtile * KS + k) * 16 + rc) * OSTRIDE + d0 + d + e];
-        acc[e] = s * inv;
-      }
-      *reinterpret_cast<f32x4_t*>(dst + d) = acc;
-    }
-    if ((tid % TPR) == 0) p.part_lse[(size_t)slot * RGS + rr] = lse2;
+    for (int i = 0; i < DV / 64; ++i) *reinterpret_cast<f32x4_t*>(dst + 64 * i) = acc[i];
+    if (c4 == 0) p.part_lse[(size_t)slot * RGS + rr] = lse2;
   }
 }
 
