@@ -36,7 +36,7 @@ extern "C" {
 #define MLA_D_QK 576          /* 512 latent + 64 rotary columns per cached row */
 #define MLA_D_V 512           /* the latent part of the row serves as V */
 #define MLA_MAX_HEADS 128
-#define MLA_MAX_SQ 16
+#define MLA_MAX_SQ 512        /* query tokens per sequence, up to the decode threshold */
 #define MLA_MAX_BATCH 16384
 #define MLA_ABI_VERSION 1
 
@@ -95,8 +95,10 @@ size_t mla_decode_workspace_size(int32_t s_q, const mla_decode_desc_t* desc);
  * nothing is written.
  *
  * Workspace layout after a call (for inspection by tests): int32 header
- * [0] work items, [1] chunk keys, [2] partial slots, [3] 1 if a seq_len was
- * clamped; at byte 256 the work items, 8 x int32 each:
+ * [0] work items, [1] chunk keys, [2] partial slots, [3] flags (bit 0: a
+ * seq_len was clamped; bit 1: the plan did not fit the workspace bounds, which
+ * the bounds exclude, and nothing was computed); at byte 256 the work items,
+ * 8 x int32 each:
  * {b, row_group, key_begin, key_end, partial_slot (-1 = written directly), 0, 0, 0}.
  */
 mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,

@@ -155,7 +155,7 @@ inline long long max_items_bound(int batch, int rows, int max_keys, int forced) 
 
 struct WsLayout {
   size_t items, pairs, part_lse, part_o, total;
-  long long max_items;
+  long long max_items, max_slots;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -165,11 +165,15 @@ inline WsLayout ws_layout(int batch, int s_q, int heads, int max_keys, int force
   RowCfg rc = row_config(rows);
   WsLayout w;
   w.max_items = max_items_bound(batch, rows, max_keys, forced);
+  // Partial slots: a pair split n >= 2 ways uses n <= 2(n - 1) slots, and the
+  // automatic chunk is at least work / (4 * SLOTS), so sum(n - 1) <= 4 * SLOTS.
+  w.max_slots = w.max_items;
+  if (forced == 0 && w.max_slots > 8LL * SLOTS) w.max_slots = 8LL * SLOTS;
   size_t off = HEADER_BYTES;
   w.items = off;   off = align256(off + (size_t)w.max_items * ITEM_INTS * 4);
   w.pairs = off;   off = align256(off + (size_t)batch * rc.nrg * 2 * 4);
-  w.part_lse = off; off = align256(off + (size_t)w.max_items * rc.rgs * 4);
-  w.part_o = off;  off = align256(off + (size_t)w.max_items * rc.rgs * DV * 4);
+  w.part_lse = off; off = align256(off + (size_t)w.max_slots * rc.rgs * 4);
+  w.part_o = off;  off = align256(off + (size_t)w.max_slots * rc.rgs * DV * 4);
   w.total = off;
   return w;
 }
@@ -184,7 +188,7 @@ struct PlanParams {
   int32_t* items;        // ITEM_INTS per item
   int32_t* pairs;        // per (b, row group): first slot, number of splits
   int batch, nrg, max_keys, forced_chunk, target;
-  long long max_items;
+  long long max_items, max_slots;
 };
 
 constexpr int PLAN_THREADS = 256;
@@ -333,10 +337,14 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     tot_slots += s_slots[i];
   }
 
+  // Cannot happen within the workspace bounds; if it did, no item runs and
+  // the header says so (bit 1 of the flag word).
+  const bool overflow = tot_items > p.max_items || tot_slots > p.max_slots;
   for (int b = b0; b < b1; ++b) {
     const int L = s_len[b];
     int n, len;
     seq_split(L, chunk, &n, &len);
+    if (overflow) n = 1;
     for (int rg = 0; rg < p.nrg; ++rg) {
       p.pairs[2 * (b * p.nrg + rg)] = n > 1 ? slot : -1;
       p.pairs[2 * (b * p.nrg + rg) + 1] = n;
@@ -352,10 +360,10 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     }
   }
   if (tid == 0) {
-    p.header[0] = (int)min((long long)tot_items, p.max_items);
+    p.header[0] = overflow ? 0 : tot_items;
     p.header[1] = chunk;
     p.header[2] = tot_slots;
-    p.header[3] = flag;
+    p.header[3] = flag | (overflow ? 2 : 0);
   }
 }
 
@@ -478,6 +486,7 @@ mla_status_t launch_plan(const int32_t* seq_lens, int32_t s_q, const mla_decode_
   pp.max_keys = max_keys_of(desc);
   pp.forced_chunk = desc->split_keys;
   pp.max_items = ws.max_items;
+  pp.max_slots = ws.max_slots;
   hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(PLAN_THREADS),
                      static_cast<unsigned>(desc->batch) * sizeof(int32_t), st, pp);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;

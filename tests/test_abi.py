@@ -60,7 +60,7 @@ def test_workspace_size_is_host_only_and_monotone():
     big = mla.workspace_size(1, desc(batch=200))
     assert 0 < small < big and small % 256 == 0
     assert mla.workspace_size(1, desc(num_heads=129)) == 0
-    assert mla.workspace_size(17, desc()) == 0
+    assert mla.workspace_size(513, desc()) == 0
     assert mla.workspace_size(1, desc(block_size=32)) == 0
     assert mla.workspace_size(1, desc(split_keys=100)) == 0
 
@@ -77,7 +77,7 @@ def test_workspace_size_is_host_only_and_monotone():
     (dict(max_blocks_per_seq=0), 1, INVALID),
     (dict(split_keys=65), 1, INVALID),
     (dict(), 0, INVALID),
-    (dict(), 17, UNSUPPORTED),
+    (dict(), 513, UNSUPPORTED),
 ])
 def test_bad_descriptions_are_rejected(kw, s_q, code):
     assert call(desc(**kw), s_q=s_q) == code
@@ -174,9 +174,21 @@ def test_plan_stays_within_workspace_bound():
         lens = rng.integers(0, maxb * bs + 1, size=B)
         d = desc(batch=B, num_heads=H, block_size=bs, max_blocks_per_seq=maxb)
         items, rgs, _ = check_plan(lens, s_q, H, bs, maxb)
-        # partial slots and items both fit the workspace the library asked for
-        per_item = 32 + rgs * 4 + rgs * 512 * 4
-        assert len(items) * per_item < mla.workspace_size(s_q, d)
+        # items and partial slots both fit the workspace the library asked for
+        slots = int((items[:, 4] >= 0).sum())
+        need = len(items) * 32 + slots * (rgs * 4 + rgs * 512 * 4)
+        assert need < mla.workspace_size(s_q, d)
+        # the automatic split never needs more than 2048 partial slots
+        assert slots <= 2048
+
+
+@pytest.mark.parametrize("s_q,H", [(64, 16), (512, 1), (512, 128), (300, 3)])
+def test_long_query_blocks_plan_and_size(s_q, H):
+    # s_q up to the decode threshold: row groups tile s_q * H rows
+    lens = [s_q + 5, 2 * s_q + 100, 7, 4000]
+    items, rgs, _ = check_plan(lens, s_q, H, 64, 64)
+    assert rgs in (16, 64)
+    assert mla.workspace_size(s_q, desc(batch=4, num_heads=H, max_blocks_per_seq=64)) > 0
 
 
 def test_out_of_range_lengths_are_clamped():

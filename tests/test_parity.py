@@ -133,6 +133,12 @@ EDGE = [
     ("heads_128_sq16", 1, 16, 128, 64, "fp8", (700,)),
     ("non_causal_sq3", 2, 3, 16, 64, "bf16", (10, 90)),
     ("bs128_fp8_short", 3, 1, 16, 128, "fp8", (1, 128, 129)),
+    # query blocks up to the decode threshold of 512 tokens: many row groups,
+    # per-row causal limits, tokens that see no key when s_q > L
+    ("sq64_h16", 2, 64, 16, 64, "bf16", (64, 700)),
+    ("sq512_h1", 2, 512, 1, 64, "bf16", (512, 1300)),
+    ("sq300_h3_fp8", 3, 300, 3, 128, "fp8", (100, 300, 900)),
+    ("sq128_h128_fp8", 1, 128, 128, 64, "fp8", (1000,)),
 ]
 
 
