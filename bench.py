@@ -266,6 +266,43 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, flush: bool):
     return res
 
 
+def bench_append(n_tokens: int, kv_dtype: str, steps: int, warmup: int):
+    """mla_kv_append: n_tokens new rows scattered into a shuffled paged cache."""
+    import torch
+    import mla_paged_decode_04_amd as mla
+    dev = torch.device("cuda:0")
+    bs = 64
+    nb = (n_tokens + bs - 1) // bs + 8
+    rng = np.random.default_rng(21)
+    rows = torch.randn((n_tokens, 576), dtype=torch.float32, device=dev).to(torch.bfloat16)
+    slots = torch.from_numpy(rng.permutation(nb * bs)[:n_tokens].astype(np.int32)).to(dev)
+    tdt = torch.bfloat16 if kv_dtype == "bf16" else torch.float8_e4m3fn
+    kv = torch.zeros((nb, bs, 576), dtype=torch.uint8 if kv_dtype == "fp8" else torch.bfloat16,
+                     device=dev).view(tdt)
+    scale = 1.0 if kv_dtype == "bf16" else 0.0213
+    for _ in range(warmup):
+        mla.mla_kv_append(rows, slots, kv, scale)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        mla.mla_kv_append(rows, slots, kv, scale)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = n_tokens * (576 * 2 + 576 * (2 if kv_dtype == "bf16" else 1) + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": "paged cache append (mla_kv_append) GB/s", "value": round(gbs, 2),
+            "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": kv_dtype, "data": "synthetic",
+            "config": {"workload": f"append_{n_tokens}_{kv_dtype}", "tokens": n_tokens,
+                       "block_size": bs, "kv_dtype": kv_dtype},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+
+
 def copy_calibration(mib: int = 1024, reps: int = 3):
     """A plain device-to-device copy of known size (torch's copy kernel), to
     scale the FETCH_SIZE / WRITE_SIZE counters of a profile run."""
@@ -293,9 +330,16 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--append", action="store_true",
+                    help="only time the cache append (128 and 65536 new rows, bf16 and fp8)")
     a = ap.parse_args()
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.append:
+        for n in (128, 65536):
+            for dt in ("bf16", "fp8"):
+                print(json.dumps(bench_append(n, dt, a.steps, a.warmup)), flush=True)
         return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",

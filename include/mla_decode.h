@@ -129,6 +129,27 @@ int32_t mla_plan_host(const int32_t* seq_lens_host, int32_t s_q, const mla_decod
                       int32_t* items, int32_t max_items, int32_t* rows_per_item,
                       int32_t* chunk_keys);
 
+/*
+ * Write new latent rows into the paged cache (the step before decode; the
+ * cache dtype is torch.float8_e4m3fn in "[Attention] Blackwell FP8 MLA support
+ * with CUTLASS_MLA backend", Purpose and Test Plan).
+ *
+ *   rows          bf16 [n_tokens, 576], device, 16-byte aligned
+ *   slot_mapping  int32 [n_tokens], device: row n goes to cache slot
+ *                 slot_mapping[n] = page * block_size + offset; a negative slot
+ *                 (padding) or one >= num_blocks * block_size writes nothing
+ *   kv_cache      [num_blocks, block_size, 576] bf16 or e4m3fn, device, 16-byte aligned
+ * Each value is stored as y = x / kv_scale (float32, correctly rounded): for
+ * fp8 clamped to +-448 and rounded to the nearest e4m3fn value (ties to the
+ * even mantissa; NaN stays NaN), for bf16 rounded to nearest even. Decoding
+ * (mla_decode) multiplies by kv_scale again.
+ * Ownership and errors as for mla_decode; slots that repeat within one call
+ * race. n_tokens == 0 is a no-op.
+ */
+mla_status_t mla_kv_append(const void* rows, const int32_t* slot_mapping, int32_t n_tokens,
+                           float kv_scale, void* kv_cache, int32_t num_blocks, int32_t block_size,
+                           int32_t kv_dtype, void* stream);
+
 const char* mla_status_string(mla_status_t status);
 int32_t mla_abi_version(void);
 

@@ -13,8 +13,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["mla_decode", "mla_decode_plan", "mla_plan_host", "workspace_size", "library",
-           "MlaError", "D_QK", "D_V", "LIB_PATH"]
+__all__ = ["mla_decode", "mla_decode_plan", "mla_plan_host", "mla_kv_append", "workspace_size",
+           "library", "MlaError", "D_QK", "D_V", "LIB_PATH"]
 
 D_QK = 576
 D_V = 512
@@ -69,6 +69,8 @@ def library() -> ctypes.CDLL:
     lib.mla_decode_plan.restype = ctypes.c_int
     lib.mla_plan_host.argtypes = [vp, i32, pdesc, vp, i32, vp, vp]
     lib.mla_plan_host.restype = i32
+    lib.mla_kv_append.argtypes = [vp, vp, i32, f32, vp, i32, i32, i32, vp]
+    lib.mla_kv_append.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -212,3 +214,30 @@ def mla_plan_host(seq_lens, s_q: int, num_heads: int, block_size: int, max_block
     if n < 0:
         raise MlaError(1, "mla_plan_host")
     return buf[:n].copy(), rows.value, chunk.value
+
+
+def mla_kv_append(rows: torch.Tensor, slot_mapping: torch.Tensor, kv_cache: torch.Tensor,
+                  kv_scale: float = 1.0) -> torch.Tensor:
+    """Write rows (bf16 [n, 576]) into kv_cache ([num_blocks, bs, 576] or
+    [num_blocks, bs, 1, 576], bf16 or float8_e4m3fn) at slot_mapping (int32 [n],
+    slot = page * bs + offset; negative = skip), on the current torch stream.
+    fp8 values are stored as e4m3fn(x / kv_scale); returns kv_cache."""
+    kv = kv_cache
+    if kv.dim() == 4 and kv.shape[2] == 1:
+        kv = kv.view(kv.shape[0], kv.shape[1], kv.shape[3])
+    _check(rows, "rows", torch.bfloat16, 2)
+    _check(slot_mapping, "slot_mapping", torch.int32, 1)
+    _check(kv, "kv_cache", None, 3)
+    if rows.shape[1] != D_QK or kv.shape[2] != D_QK:
+        raise ValueError(f"rows and kv_cache rows must be {D_QK} wide")
+    if slot_mapping.shape[0] != rows.shape[0]:
+        raise ValueError("slot_mapping must have one entry per row")
+    for name, t in (("slot_mapping", slot_mapping), ("kv_cache", kv)):
+        if t.device != rows.device:
+            raise ValueError(f"{name} is on {t.device}, rows on {rows.device}")
+    st = library().mla_kv_append(rows.data_ptr(), slot_mapping.data_ptr(), rows.shape[0],
+                                 float(kv_scale), kv.data_ptr(), kv.shape[0], kv.shape[1],
+                                 _kv_dtype_code(kv), torch.cuda.current_stream(rows.device).cuda_stream)
+    if st != 0:
+        raise MlaError(st, "mla_kv_append")
+    return kv_cache

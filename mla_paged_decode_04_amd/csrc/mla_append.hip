@@ -1,0 +1,104 @@
+// Writing new latent rows into the paged cache (the step before decode):
+// "[Attention] Blackwell FP8 MLA support with CUTLASS_MLA backend", Purpose and
+// Test Plan -- the latent cache is kept in torch.float8_e4m3fn. A new bf16 row x
+// goes to slot s (page s / bs, row s % bs) as y = x / kv_scale (float32,
+// correctly rounded), encoded as OCP e4m3fn (clamped to +-448, nearest, ties to
+// even mantissa) or as bf16 (nearest, ties to even). Decoding multiplies by
+// kv_scale again.
+#include "mla_internal.h"
+
+using namespace mla_detail;
+
+namespace {
+
+constexpr int APPEND_THREADS = 256;
+constexpr int CHUNKS = D / 8;   // 72 chunks of 8 values per row
+
+// float32 -> OCP e4m3fn code: saturate to 448, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  float a = fabsf(y);
+  if (a != a) return 0x7Fu | sign;                 // NaN
+  a = fminf(a, 448.f);                               // saturate (infinities too)
+  if (a < 0.015625f) {                               // below 2^-6: steps of 2^-9
+    const float q = __builtin_rintf(a * 512.f);      // exact scaling, ties to even
+    return sign | static_cast<uint32_t>(q);          // 0..8 (8 encodes 2^-6)
+  }
+  const uint32_t b = __builtin_bit_cast(uint32_t, a);
+  const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);   // keep 3 mantissa bits, ties to even
+  const uint32_t e = (r >> 23) - 120u;                   // rebias 127 -> 7: 1..15
+  return sign | (e << 3) | ((r >> 20) & 7u);
+}
+
+struct AppendParams {
+  const uint16_t* rows;
+  const int32_t* slots;
+  uint8_t* kv;
+  long long n_slots;   // num_blocks * block_size
+  int n_tokens;
+  float kv_scale;
+};
+
+template <int KVT>
+__global__ __launch_bounds__(APPEND_THREADS) void mla_kv_append_kernel(AppendParams p) {
+  const long long gid = (long long)blockIdx.x * APPEND_THREADS + threadIdx.x;
+  if (gid >= (long long)p.n_tokens * CHUNKS) return;
+  const int n = static_cast<int>(gid / CHUNKS);
+  const int c = static_cast<int>(gid - (long long)n * CHUNKS);
+  const long long slot = p.slots[n];
+  if (slot < 0 || slot >= p.n_slots) return;        // padding or out of range: no write
+  const uint4 raw = *reinterpret_cast<const uint4*>(p.rows + (size_t)n * D + 8 * c);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float y[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    y[2 * k] = __builtin_bit_cast(float, w[k] << 16) / p.kv_scale;
+    y[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xFFFF0000u) / p.kv_scale;
+  }
+  if constexpr (KVT == MLA_DTYPE_FP8_E4M3FN) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lo |= f32_to_e4m3fn(y[k]) << (8 * k);
+      hi |= f32_to_e4m3fn(y[4 + k]) << (8 * k);
+    }
+    *reinterpret_cast<uint2*>(p.kv + (size_t)slot * D + 8 * c) = make_uint2(lo, hi);
+  } else {
+    *reinterpret_cast<uint4*>(p.kv + ((size_t)slot * D + 8 * c) * 2) =
+        make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                   pack_bf16x2(y[6], y[7]));
+  }
+}
+
+bool is_aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+}  // namespace
+
+extern "C" mla_status_t mla_kv_append(const void* rows, const int32_t* slot_mapping, int32_t n_tokens,
+                                      float kv_scale, void* kv_cache, int32_t num_blocks,
+                                      int32_t block_size, int32_t kv_dtype, void* stream) {
+  if (n_tokens < 0 || num_blocks < 1) return MLA_ERR_INVALID_ARGUMENT;
+  if (block_size != 64 && block_size != 128) return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype != MLA_DTYPE_BF16 && kv_dtype != MLA_DTYPE_FP8_E4M3FN) return MLA_ERR_UNSUPPORTED;
+  if (!(std::isfinite(kv_scale) && kv_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
+  if (n_tokens == 0) return MLA_OK;
+  if (rows == nullptr || slot_mapping == nullptr || kv_cache == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (!is_aligned(rows, 16) || !is_aligned(kv_cache, 16) || !is_aligned(slot_mapping, 4))
+    return MLA_ERR_INVALID_ARGUMENT;
+  AppendParams ap;
+  ap.rows = static_cast<const uint16_t*>(rows);
+  ap.slots = slot_mapping;
+  ap.kv = static_cast<uint8_t*>(kv_cache);
+  ap.n_slots = (long long)num_blocks * block_size;
+  ap.n_tokens = n_tokens;
+  ap.kv_scale = kv_scale;
+  const long long threads = (long long)n_tokens * CHUNKS;
+  const dim3 grid(static_cast<unsigned>((threads + APPEND_THREADS - 1) / APPEND_THREADS));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (kv_dtype == MLA_DTYPE_BF16)
+    hipLaunchKernelGGL(mla_kv_append_kernel<MLA_DTYPE_BF16>, grid, dim3(APPEND_THREADS), 0, st, ap);
+  else
+    hipLaunchKernelGGL(mla_kv_append_kernel<MLA_DTYPE_FP8_E4M3FN>, grid, dim3(APPEND_THREADS), 0, st, ap);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}

@@ -5,4 +5,5 @@ import this package. It shares no code with the HIP path.
 """
 from .mla_oracle import (D_QK, D_V, E4M3FN_TABLE, attend, bf16_bits_to_f64,  # noqa: F401
                          combine_partials, cos_diff, decode_rows, e4m3fn_to_f64,
-                         e4m3fn_value, gather_keys, mla_decode, rel_fro, visible_keys)
+                         e4m3fn_value, gather_keys, kv_append, mla_decode, quantize_e4m3fn,
+                         rel_fro, round_bf16, visible_keys)

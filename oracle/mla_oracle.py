@@ -195,3 +195,70 @@ def rel_fro(x: np.ndarray, ref: np.ndarray) -> float:
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
+
+
+# ---------------------------------------------------------------------------
+# writing new rows into the paged cache (the step before decode)
+# ---------------------------------------------------------------------------
+#
+# "[Attention] Blackwell FP8 MLA support with CUTLASS_MLA backend", Purpose
+# and Test Plan: the latent cache is kept in torch.float8_e4m3fn. Reading
+# used (the pages do not spell out the write): a new row x (bf16) is stored
+# in slot `slot` (page slot // bs, row slot % bs) as the code of
+# y = float32(x) / float32(kv_scale) -- for fp8 clamped to [-448, 448] and
+# rounded to the nearest e4m3fn value, ties to the even mantissa; for a bf16
+# cache rounded to the nearest bf16, ties to even. Decoding multiplies by
+# kv_scale again. Negative slots are padding and write nothing.
+
+_E4M3FN_POS = E4M3FN_TABLE[:0x7F]          # codes 0x00..0x7E: 0 .. 448, increasing
+
+
+def quantize_e4m3fn(y: np.ndarray) -> np.ndarray:
+    """float32 values -> e4m3fn codes by nearest value (ties: even mantissa)."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.minimum(np.abs(y.astype(np.float64)), 448.0)
+    hi = np.searchsorted(_E4M3FN_POS, a, side="left")          # first value >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.where(_E4M3FN_POS[hi] == a, hi, np.maximum(hi - 1, 0))
+    d_lo = a - _E4M3FN_POS[lo]
+    d_hi = _E4M3FN_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.signbit(y), code | np.uint8(0x80), code)
+    code = np.where(np.isnan(y), np.uint8(0x7F) | (np.signbit(y).astype(np.uint8) << 7), code)
+    return code.astype(np.uint8)
+
+
+def round_bf16(y: np.ndarray) -> np.ndarray:
+    """float32 values -> bf16 bit patterns, nearest with ties to even (NaN kept
+    as a quiet NaN). The two candidates are the value truncated to bf16 and
+    the next bf16 away from zero; the distances are compared in float64."""
+    y = np.asarray(y, dtype=np.float32)
+    u = y.view(np.uint32)
+    t = (u >> np.uint32(16)).astype(np.uint32)                 # truncated pattern
+    up = t + np.uint32(1)                                       # next magnitude up
+    vt = bf16_bits_to_f64(t.astype(np.uint16))
+    vu = bf16_bits_to_f64(up.astype(np.uint16))
+    x = y.astype(np.float64)
+    d_t = np.abs(x - vt)
+    d_u = np.abs(vu - x)
+    pick_up = (d_u < d_t) | ((d_u == d_t) & (t % 2 == 1))
+    out = np.where(pick_up, up, t).astype(np.uint16)
+    out = np.where(np.isnan(y), (t | np.uint32(0x40)).astype(np.uint16), out)
+    return out
+
+
+def kv_append(kv: np.ndarray, rows_bits: np.ndarray, slot_mapping: np.ndarray,
+              kv_scale: float, kv_dtype: str) -> np.ndarray:
+    """Copy of `kv` with row n of `rows_bits` (bf16 bits [N, 576]) written to
+    slot slot_mapping[n] in the cache encoding."""
+    kv = np.array(kv, copy=True)
+    nb, bs = kv.shape[0], kv.shape[1]
+    x = bf16_bits_to_f64(rows_bits).astype(np.float32)
+    y = x / np.float32(kv_scale)
+    for n, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0 or slot >= nb * bs:
+            continue
+        page, off = divmod(int(slot), bs)
+        kv[page, off] = quantize_e4m3fn(y[n]) if kv_dtype == "fp8" else round_bf16(y[n])
+    return kv

@@ -195,3 +195,30 @@ def test_out_of_range_lengths_are_clamped():
     items, _, _ = mla.mla_plan_host([-5, 10_000], 1, 16, 64, 2)
     ends = {(b, t1) for b, rg, t0, t1, *_ in items.tolist()}
     assert (0, 0) in ends and (1, 128) in ends
+
+
+# ---------------------------------------------------------------------------
+# cache append: argument checks (nothing is launched on an error)
+# ---------------------------------------------------------------------------
+
+def append_call(n=4, scale=1.0, nb=8, bs=64, dtype=0, ptrs=True):
+    lib = mla.library()
+    p = 4096 if ptrs else None
+    return lib.mla_kv_append(p, p, n, scale, p, nb, bs, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), INVALID),
+    (dict(nb=0), INVALID),
+    (dict(bs=32), UNSUPPORTED),
+    (dict(dtype=7), UNSUPPORTED),
+    (dict(scale=0.0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(ptrs=False), INVALID),
+])
+def test_kv_append_rejects_bad_arguments(kw, code):
+    assert append_call(**kw) == code
+
+
+def test_kv_append_zero_tokens_is_a_no_op():
+    assert append_call(n=0, ptrs=False) == 0

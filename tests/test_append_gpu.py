@@ -1,0 +1,92 @@
+"""GPU: writing new rows into the paged cache (mla_kv_append) against the
+oracle's encoder, byte for byte, and a decode over the appended cache."""
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+from oracle import mla_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_paged_decode_04_amd as m
+    m.library()
+    return m
+
+
+def rows_with_edge_values(rng, n, scale, fp8):
+    x = rng.standard_normal((n, 576)).astype(np.float32)
+    x[0, :64] *= 1e-3 * scale          # fp8 subnormals after division by the scale
+    x[1, :64] *= 1e3 * scale           # beyond 448 * scale: saturates
+    x[2, :8] = np.array([0.0, -0.0, 448.0, -448.0, 1e30, -1e30, 3.0, -3.0]) * scale
+    if fp8:
+        x[3, :2] = np.nan
+    return orc.round_bf16(x)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("bs", [64, 128])
+def test_kv_append_is_bit_exact(mla, kv_dtype, bs):
+    rng = np.random.default_rng(11 if kv_dtype == "bf16" else 12)
+    nb, n = 7, 300
+    scale = 1.0 if kv_dtype == "bf16" else 0.0213
+    rows = rows_with_edge_values(rng, n, scale, kv_dtype == "fp8")
+    slots = rng.permutation(nb * bs)[:n].astype(np.int32)
+    slots[5] = -1
+    slots[9] = nb * bs + 3            # out of range: no write
+    dt = np.uint16 if kv_dtype == "bf16" else np.uint8
+    kv0 = rng.integers(0, 1 << (16 if kv_dtype == "bf16" else 8), size=(nb, bs, 576)).astype(dt)
+    ref = orc.kv_append(kv0, rows, slots, scale, kv_dtype)
+
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if kv_dtype == "bf16" else torch.float8_e4m3fn
+    kv = torch.from_numpy(kv0.view(np.int16) if kv_dtype == "bf16" else kv0).to(dev).view(tdt)
+    r = torch.from_numpy(rows.view(np.int16)).to(dev).view(torch.bfloat16)
+    s = torch.from_numpy(slots).to(dev)
+    mla.mla_kv_append(r, s, kv, scale)
+    torch.cuda.synchronize()
+    got = kv.view(torch.int16 if kv_dtype == "bf16" else torch.uint8).cpu().numpy().view(dt)
+    if kv_dtype == "bf16":
+        np.testing.assert_array_equal(got, ref)
+    else:
+        np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_fp8"])
+def test_append_last_token_then_decode(mla, name):
+    # rebuild each sequence's newest cached row through the append kernel
+    wl = mi.WORKLOADS[name]
+    inp = mi.make_inputs(wl)
+    rng = np.random.default_rng(3)
+    B, bs = wl.batch, wl.block_size
+    new_rows = orc.round_bf16(rng.standard_normal((B, 576)).astype(np.float32))
+    slots = np.array([inp.block_table[b, (inp.seq_lens[b] - 1) // bs] * bs + (inp.seq_lens[b] - 1) % bs
+                      for b in range(B)], dtype=np.int32)
+    scale = inp.kv_scale
+    ref_kv = orc.kv_append(inp.kv, new_rows, slots, scale, wl.kv_dtype)
+
+    dev = torch.device("cuda:0")
+    if wl.kv_dtype == "bf16":
+        kv = torch.from_numpy(inp.kv.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        kv = torch.from_numpy(inp.kv).to(dev).view(torch.float8_e4m3fn)
+    mla.mla_kv_append(torch.from_numpy(new_rows.view(np.int16)).to(dev).view(torch.bfloat16),
+                      torch.from_numpy(slots).to(dev), kv, scale)
+    q = torch.from_numpy(inp.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    sl = torch.from_numpy(inp.seq_lens).to(dev)
+    out, lse = mla.mla_decode(q, kv, bt, sl, wl.softmax_scale, scale, causal=wl.causal)
+    torch.cuda.synchronize()
+    got_kv = kv.view(torch.int16 if wl.kv_dtype == "bf16" else torch.uint8).cpu().numpy()
+    np.testing.assert_array_equal(got_kv.view(ref_kv.dtype), ref_kv)
+    ro, rl = orc.mla_decode(inp.q_bits, ref_kv, inp.block_table, inp.seq_lens, wl.s_q,
+                            wl.softmax_scale, scale, wl.kv_dtype, wl.causal)
+    o = out.float().cpu().double().numpy()
+    tol = 5e-3 if wl.kv_dtype == "bf16" else 1e-2
+    assert orc.rel_fro(o, ro) <= tol
+    assert np.abs(lse.cpu().double().numpy() - rl).max() <= 1e-3

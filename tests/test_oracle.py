@@ -373,3 +373,76 @@ def test_planted_mistakes_are_caught(monkeypatch, mutant):
     o, l = run_oracle(inp)
     caught = not (np.allclose(o, ob, rtol=0, atol=1e-12) and np.allclose(l, lb, rtol=0, atol=1e-12))
     assert caught, mutant
+
+
+# ---------------------------------------------------------------------------
+# cache append: the e4m3fn / bf16 encoders and the slot writes
+# ---------------------------------------------------------------------------
+
+def test_quantize_e4m3fn_round_trips_every_code():
+    vals = orc.E4M3FN_TABLE.astype(np.float32)
+    codes = np.arange(256, dtype=np.uint8)
+    finite = ~np.isnan(vals)
+    np.testing.assert_array_equal(orc.quantize_e4m3fn(vals[finite]), codes[finite])
+
+
+def test_quantize_e4m3fn_ties_go_to_the_even_mantissa():
+    pos = orc.E4M3FN_TABLE[:0x7F]
+    for c in range(0x7E):
+        mid = np.float32((pos[c] + pos[c + 1]) / 2)
+        if float(mid) != (pos[c] + pos[c + 1]) / 2:
+            continue          # midpoint not representable in float32: no tie
+        want = c if c % 2 == 0 else c + 1
+        assert int(orc.quantize_e4m3fn(np.array([mid]))[0]) == want, c
+        assert int(orc.quantize_e4m3fn(np.array([-mid]))[0]) == want | 0x80, c
+
+
+def test_quantize_e4m3fn_saturates_and_keeps_nan():
+    got = orc.quantize_e4m3fn(np.array([448.0, 449.0, 1e9, -1e9, np.inf, -np.inf, np.nan],
+                                       dtype=np.float32))
+    np.testing.assert_array_equal(got, [0x7E, 0x7E, 0x7E, 0xFE, 0x7E, 0xFE, 0x7F])
+
+
+def test_quantize_e4m3fn_matches_torch_cast_in_range():
+    rng = np.random.default_rng(5)
+    y = np.concatenate([rng.standard_normal(20000) * 40, rng.standard_normal(20000) * 0.01,
+                        rng.uniform(-448, 448, 20000)]).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(orc.quantize_e4m3fn(y), ref)
+
+
+def test_round_bf16_matches_torch_and_ties_to_even():
+    rng = np.random.default_rng(6)
+    y = (rng.standard_normal(50000) * 7).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(orc.round_bf16(y), ref)
+    # exact ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7
+    tie = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8], dtype=np.float32)
+    np.testing.assert_array_equal(orc.round_bf16(tie), [0x3F80, 0x3F82])
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_kv_append_writes_exactly_the_mapped_slots(kv_dtype):
+    rng = np.random.default_rng(7)
+    nb, bs, n = 5, 64, 9
+    dt = np.uint16 if kv_dtype == "bf16" else np.uint8
+    kv = rng.integers(0, 100, size=(nb, bs, 576)).astype(dt)
+    rows = orc.round_bf16(rng.standard_normal((n, 576)).astype(np.float32))
+    slots = np.array([0, 63, 64, 200, -1, 319, -5, 130, 5 * 64], dtype=np.int32)  # -1, -5, 320: skipped
+    scale = 0.0173
+    out = orc.kv_append(kv, rows, slots, scale, kv_dtype)
+    written = {int(s) for s in slots if 0 <= s < nb * bs}
+    for page in range(nb):
+        for off in range(bs):
+            if page * bs + off not in written:
+                np.testing.assert_array_equal(out[page, off], kv[page, off])
+    x = orc.bf16_bits_to_f64(rows)
+    for k, s in enumerate(slots):
+        if not 0 <= s < nb * bs:
+            continue
+        back = orc.decode_rows(out[s // bs, s % bs], kv_dtype) * scale
+        # within half a step of the encoding at that magnitude (fp8: 3 mantissa
+        # bits, so 2^-4 relative; bf16: 2^-9 relative), plus the subnormal floor
+        rel = 2.0 ** -4 if kv_dtype == "fp8" else 2.0 ** -8
+        floor = 2.0 ** -10 * scale if kv_dtype == "fp8" else 0.0
+        assert np.all(np.abs(back - x[k]) <= rel * np.abs(x[k]) + floor + 1e-30), k
