@@ -303,6 +303,46 @@ def bench_append(n_tokens: int, kv_dtype: str, steps: int, warmup: int):
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
 
 
+def bench_absorb(T: int, H: int, d: int, steps: int, warmup: int):
+    """mla_absorb_q (d -> 512 per head, q_pe copied) and mla_absorb_out (512 -> d)."""
+    import torch
+    import mla_paged_decode_04_amd as mla
+    dev = torch.device("cuda:0")
+    qn = torch.randn((T, H, d), device=dev).to(torch.bfloat16)
+    pe = torch.randn((T, H, 64), device=dev).to(torch.bfloat16)
+    w_uk = (torch.randn((H, d, 512), device=dev) * d ** -0.5).to(torch.bfloat16)
+    o = torch.randn((T, H, 512), device=dev).to(torch.bfloat16)
+    w_uv = (torch.randn((H, 512, d), device=dev) * 512 ** -0.5).to(torch.bfloat16)
+    q = torch.empty((T, H, 576), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        mla.mla_absorb_q(qn, pe, w_uk, out=q)
+        mla.mla_absorb_out(o, w_uv, out=y)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2 * 2 * T * H * d * 512
+    tfs = flops / (ms * 1e-3) / 1e12
+    return {"metric": "absorbed projections (mla_absorb_q + mla_absorb_out) TFLOP/s",
+            "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"absorb_T{T}_H{H}_d{d}", "tokens": T, "heads": H, "d": d},
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                         "traffic": None}}
+
+
 def copy_calibration(mib: int = 1024, reps: int = 3):
     """A plain device-to-device copy of known size (torch's copy kernel), to
     scale the FETCH_SIZE / WRITE_SIZE counters of a profile run."""
@@ -330,11 +370,17 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--absorb", action="store_true",
+                    help="only time the absorbed projections (d = 128 per head)")
     ap.add_argument("--append", action="store_true",
                     help="only time the cache append (128 and 65536 new rows, bf16 and fp8)")
     a = ap.parse_args()
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.absorb:
+        for T, H in ((128, 16), (64, 128), (4096, 128)):
+            print(json.dumps(bench_absorb(T, H, 128, a.steps, a.warmup)), flush=True)
         return
     if a.append:
         for n in (128, 65536):

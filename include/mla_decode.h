@@ -150,6 +150,28 @@ mla_status_t mla_kv_append(const void* rows, const int32_t* slot_mapping, int32_
                            float kv_scale, void* kv_cache, int32_t num_blocks, int32_t block_size,
                            int32_t kv_dtype, void* stream);
 
+/*
+ * The absorbed projections around the decode MQA ("[WIP][Attention] FlashAttn
+ * MLA", description: MLA's decode step is computed as MQA over the latent
+ * cache, so the per-head up-projections move onto the query and the output).
+ * Reading used (the pages give no shapes): per token t and head h,
+ *   mla_absorb_q:   q_out[t][h][0:512]   = q_nope[t][h][0:d_nope] . w_uk[h]
+ *                   q_out[t][h][512:576] = q_pe[t][h][0:64]   (copied)
+ *   mla_absorb_out: out[t][h][0:d_v]     = o[t][h][0:512] . w_uv[h]
+ * All device pointers, bf16, row-major, 16-byte aligned:
+ *   q_nope [tokens, heads, d_nope]; q_pe [tokens, heads, 64];
+ *   w_uk [heads, d_nope, 512]; q_out [tokens, heads, 576] (the q of mla_decode);
+ *   o [tokens, heads, 512] (the out of mla_decode); w_uv [heads, 512, d_v];
+ *   out [tokens, heads, d_v].
+ * fp32 accumulation, bf16 result rounded to nearest even. d_nope: a multiple
+ * of 32; d_v: a multiple of 64 (both <= 4096); 1 <= heads <= 128. tokens == 0
+ * is a no-op. Errors as for mla_decode.
+ */
+mla_status_t mla_absorb_q(const void* q_nope, const void* q_pe, const void* w_uk, void* q_out,
+                          int32_t tokens, int32_t heads, int32_t d_nope, void* stream);
+mla_status_t mla_absorb_out(const void* o, const void* w_uv, void* out, int32_t tokens,
+                            int32_t heads, int32_t d_v, void* stream);
+
 const char* mla_status_string(mla_status_t status);
 int32_t mla_abi_version(void);
 

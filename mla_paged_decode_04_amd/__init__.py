@@ -13,7 +13,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["mla_decode", "mla_decode_plan", "mla_plan_host", "mla_kv_append", "workspace_size",
+__all__ = ["mla_decode", "mla_decode_plan", "mla_plan_host", "mla_kv_append", "mla_absorb_q",
+           "mla_absorb_out", "workspace_size",
            "library", "MlaError", "D_QK", "D_V", "LIB_PATH"]
 
 D_QK = 576
@@ -71,6 +72,10 @@ def library() -> ctypes.CDLL:
     lib.mla_plan_host.restype = i32
     lib.mla_kv_append.argtypes = [vp, vp, i32, f32, vp, i32, i32, i32, vp]
     lib.mla_kv_append.restype = ctypes.c_int
+    lib.mla_absorb_q.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.mla_absorb_q.restype = ctypes.c_int
+    lib.mla_absorb_out.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+    lib.mla_absorb_out.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -241,3 +246,42 @@ def mla_kv_append(rows: torch.Tensor, slot_mapping: torch.Tensor, kv_cache: torc
     if st != 0:
         raise MlaError(st, "mla_kv_append")
     return kv_cache
+
+
+def mla_absorb_q(q_nope: torch.Tensor, q_pe: torch.Tensor, w_uk: torch.Tensor,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q for mla_decode from the per-head parts: q_nope [T, H, d_nope] . w_uk
+    [H, d_nope, 512] -> latent 512, with q_pe [T, H, 64] appended. All bf16."""
+    _check(q_nope, "q_nope", torch.bfloat16, 3)
+    _check(q_pe, "q_pe", torch.bfloat16, 3)
+    _check(w_uk, "w_uk", torch.bfloat16, 3)
+    T, H, dn = q_nope.shape
+    if tuple(q_pe.shape) != (T, H, D_QK - D_V) or tuple(w_uk.shape) != (H, dn, D_V):
+        raise ValueError("shapes must be q_nope [T,H,d], q_pe [T,H,64], w_uk [H,d,512]")
+    if out is None:
+        out = torch.empty((T, H, D_QK), dtype=torch.bfloat16, device=q_nope.device)
+    _check(out, "out", torch.bfloat16, 3)
+    st = library().mla_absorb_q(q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(), out.data_ptr(),
+                                T, H, dn, torch.cuda.current_stream(q_nope.device).cuda_stream)
+    if st != 0:
+        raise MlaError(st, "mla_absorb_q")
+    return out
+
+
+def mla_absorb_out(o: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] = None
+                   ) -> torch.Tensor:
+    """Per-head output projection: o [T, H, 512] . w_uv [H, 512, d_v] -> [T, H, d_v]. bf16."""
+    _check(o, "o", torch.bfloat16, 3)
+    _check(w_uv, "w_uv", torch.bfloat16, 3)
+    T, H, dl = o.shape
+    if dl != D_V or w_uv.shape[0] != H or w_uv.shape[1] != D_V:
+        raise ValueError("shapes must be o [T,H,512], w_uv [H,512,d_v]")
+    dv = w_uv.shape[2]
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=torch.bfloat16, device=o.device)
+    _check(out, "out", torch.bfloat16, 3)
+    st = library().mla_absorb_out(o.data_ptr(), w_uv.data_ptr(), out.data_ptr(), T, H, dv,
+                                  torch.cuda.current_stream(o.device).cuda_stream)
+    if st != 0:
+        raise MlaError(st, "mla_absorb_out")
+    return out

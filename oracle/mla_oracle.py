@@ -262,3 +262,25 @@ def kv_append(kv: np.ndarray, rows_bits: np.ndarray, slot_mapping: np.ndarray,
         page, off = divmod(int(slot), bs)
         kv[page, off] = quantize_e4m3fn(y[n]) if kv_dtype == "fp8" else round_bf16(y[n])
     return kv
+
+
+# ---------------------------------------------------------------------------
+# the absorbed projections around the MQA
+# ---------------------------------------------------------------------------
+#
+# "[WIP][Attention] FlashAttn MLA", description: the decode step of MLA is
+# computed as MQA over the latent cache, so each head's up-projection of the
+# keys (W_UK) multiplies its query instead, and the value up-projection (W_UV)
+# is applied to the 512-wide latent output. Reading used: q_nope [T, H, d],
+# W_UK [H, d, 512], q_pe [T, H, 64] appended as the rotary part; W_UV
+# [H, 512, d_v]. Plain float64 products of the bf16 inputs.
+
+def absorb_q(q_nope_bits: np.ndarray, q_pe_bits: np.ndarray, w_uk_bits: np.ndarray) -> np.ndarray:
+    qn = bf16_bits_to_f64(q_nope_bits)                     # [T, H, d]
+    w = bf16_bits_to_f64(w_uk_bits)                        # [H, d, 512]
+    lat = np.einsum("thd,hdn->thn", qn, w)
+    return np.concatenate([lat, bf16_bits_to_f64(q_pe_bits)], axis=-1)
+
+
+def absorb_out(o_bits: np.ndarray, w_uv_bits: np.ndarray) -> np.ndarray:
+    return np.einsum("thn,hnv->thv", bf16_bits_to_f64(o_bits), bf16_bits_to_f64(w_uv_bits))

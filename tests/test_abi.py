@@ -222,3 +222,22 @@ def test_kv_append_rejects_bad_arguments(kw, code):
 
 def test_kv_append_zero_tokens_is_a_no_op():
     assert append_call(n=0, ptrs=False) == 0
+
+
+@pytest.mark.parametrize("fn,args,code", [
+    ("mla_absorb_q", (4096, 4096, 4096, 4096, 4, 16, 100, None), UNSUPPORTED),   # d_nope % 32
+    ("mla_absorb_q", (4096, 4096, 4096, 4096, 4, 0, 128, None), INVALID),
+    ("mla_absorb_q", (4096, 4096, 4096, 4096, -1, 16, 128, None), INVALID),
+    ("mla_absorb_q", (None, 4096, 4096, 4096, 4, 16, 128, None), INVALID),
+    ("mla_absorb_out", (4096, 4096, 4096, 4, 16, 100, None), UNSUPPORTED),      # d_v % 64
+    ("mla_absorb_out", (4096, 4096, 4096, 4, 129, 128, None), INVALID),
+    ("mla_absorb_out", (4096, None, 4096, 4, 16, 128, None), INVALID),
+])
+def test_absorb_rejects_bad_arguments(fn, args, code):
+    assert getattr(mla.library(), fn)(*args) == code
+
+
+def test_absorb_zero_tokens_is_a_no_op():
+    lib = mla.library()
+    assert lib.mla_absorb_q(None, None, None, None, 0, 16, 128, None) == 0
+    assert lib.mla_absorb_out(None, None, None, 0, 16, 128, None) == 0

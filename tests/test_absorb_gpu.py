@@ -1,0 +1,77 @@
+"""GPU: the absorbed projections (mla_absorb_q / mla_absorb_out) against the
+float64 oracle. bf16 results: relative Frobenius error <= 5e-3 (about twice
+the bf16 rounding of the output); the copied rotary part is bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_paged_decode_04_amd as m
+    m.library()
+    return m
+
+
+def bf16(rng, shape, scale=1.0):
+    return orc.round_bf16((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+def dev(bits):
+    return torch.from_numpy(bits.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("T,H,d", [(128, 16, 128), (64, 128, 128), (37, 3, 64), (1, 1, 32)])
+def test_absorb_q(mla, T, H, d):
+    rng = np.random.default_rng(T * 1000 + H)
+    qn, pe, w = bf16(rng, (T, H, d)), bf16(rng, (T, H, 64)), bf16(rng, (H, d, 512), d ** -0.5)
+    out = mla.mla_absorb_q(dev(qn), dev(pe), dev(w))
+    torch.cuda.synchronize()
+    got = out.float().cpu().double().numpy()
+    ref = orc.absorb_q(qn, pe, w)
+    assert orc.rel_fro(got[..., :512], ref[..., :512]) <= 5e-3
+    np.testing.assert_array_equal(got[..., 512:], ref[..., 512:])
+
+
+@pytest.mark.parametrize("T,H,dv", [(128, 16, 128), (64, 128, 128), (37, 3, 64), (5, 2, 192)])
+def test_absorb_out(mla, T, H, dv):
+    rng = np.random.default_rng(T * 1000 + H + 7)
+    o, w = bf16(rng, (T, H, 512)), bf16(rng, (H, 512, dv), 512 ** -0.5)
+    out = mla.mla_absorb_out(dev(o), dev(w))
+    torch.cuda.synchronize()
+    assert orc.rel_fro(out.float().cpu().double().numpy(), orc.absorb_out(o, w)) <= 5e-3
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_absorbed_decode_chain(mla, kv_dtype):
+    # q_nope . W_UK (+ q_pe) -> paged MQA decode -> o . W_UV, against the same
+    # chain in float64 with q rounded to bf16 where the GPU path stores it
+    import mla_inputs as mi
+    wl = mi.WORKLOADS["tiny" if kv_dtype == "bf16" else "tiny_fp8"]
+    inp = mi.make_inputs(wl)
+    rng = np.random.default_rng(31)
+    B, H, d, dv = wl.batch, wl.heads, 128, 128
+    qn, pe = bf16(rng, (B, H, d)), bf16(rng, (B, H, 64))
+    w_uk, w_uv = bf16(rng, (H, d, 512), d ** -0.5), bf16(rng, (H, 512, dv), 512 ** -0.5)
+    q = mla.mla_absorb_q(dev(qn), dev(pe), dev(w_uk))
+    if kv_dtype == "bf16":
+        kv = torch.from_numpy(inp.kv.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    else:
+        kv = torch.from_numpy(inp.kv).to("cuda:0").view(torch.float8_e4m3fn)
+    bt = torch.from_numpy(inp.block_table).to("cuda:0")
+    sl = torch.from_numpy(inp.seq_lens).to("cuda:0")
+    o, _ = mla.mla_decode(q.view(B, 1, H, 576), kv, bt, sl, wl.softmax_scale, inp.kv_scale)
+    out = mla.mla_absorb_out(o.view(B, H, 512), dev(w_uv))
+    torch.cuda.synchronize()
+
+    q_ref = orc.round_bf16(orc.absorb_q(qn, pe, w_uk).astype(np.float32)).reshape(B, 1, H, 576)
+    o_ref, _ = orc.mla_decode(q_ref, inp.kv, inp.block_table, inp.seq_lens, 1, wl.softmax_scale,
+                              inp.kv_scale, wl.kv_dtype, True)
+    ref = np.einsum("thn,hnv->thv", o_ref.reshape(B, H, 512), orc.bf16_bits_to_f64(w_uv))
+    assert orc.rel_fro(out.float().cpu().double().numpy(), ref) <= 1e-2

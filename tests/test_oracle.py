@@ -446,3 +446,43 @@ def test_kv_append_writes_exactly_the_mapped_slots(kv_dtype):
         rel = 2.0 ** -4 if kv_dtype == "fp8" else 2.0 ** -8
         floor = 2.0 ** -10 * scale if kv_dtype == "fp8" else 0.0
         assert np.all(np.abs(back - x[k]) <= rel * np.abs(x[k]) + floor + 1e-30), k
+
+
+# ---------------------------------------------------------------------------
+# absorbed projections
+# ---------------------------------------------------------------------------
+
+def test_absorb_matches_loops_on_tiny_shapes():
+    rng = np.random.default_rng(8)
+    T, H, d, N = 3, 2, 5, 7
+    qn = orc.round_bf16(rng.standard_normal((T, H, d)).astype(np.float32))
+    w = orc.round_bf16(rng.standard_normal((H, d, N)).astype(np.float32))
+    pe = orc.round_bf16(rng.standard_normal((T, H, 64)).astype(np.float32))
+    got = orc.absorb_q(qn, pe, w)
+    qf, wf = orc.bf16_bits_to_f64(qn), orc.bf16_bits_to_f64(w)
+    for t in range(T):
+        for h in range(H):
+            for n in range(N):
+                ref = sum(qf[t, h, k] * wf[h, k, n] for k in range(d))
+                assert abs(got[t, h, n] - ref) <= 1e-12 * (1 + abs(ref))
+            np.testing.assert_array_equal(got[t, h, N:], orc.bf16_bits_to_f64(pe[t, h]))
+    o = orc.round_bf16(rng.standard_normal((T, H, N)).astype(np.float32))
+    wv = orc.round_bf16(rng.standard_normal((H, N, 4)).astype(np.float32))
+    got = orc.absorb_out(o, wv)
+    of, wvf = orc.bf16_bits_to_f64(o), orc.bf16_bits_to_f64(wv)
+    for t in range(T):
+        for h in range(H):
+            for v in range(4):
+                ref = sum(of[t, h, k] * wvf[h, k, v] for k in range(N))
+                assert abs(got[t, h, v] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_absorb_with_identity_weights_is_a_copy():
+    rng = np.random.default_rng(9)
+    T, H = 4, 3
+    x = orc.round_bf16(rng.standard_normal((T, H, 512)).astype(np.float32))
+    eye = np.broadcast_to(orc.round_bf16(np.eye(512, dtype=np.float32)), (H, 512, 512))
+    np.testing.assert_array_equal(orc.absorb_out(x, eye), orc.bf16_bits_to_f64(x))
+    pe = orc.round_bf16(rng.standard_normal((T, H, 64)).astype(np.float32))
+    q = orc.absorb_q(x, pe, eye)
+    np.testing.assert_array_equal(q[..., :512], orc.bf16_bits_to_f64(x))
