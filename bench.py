@@ -39,6 +39,7 @@ CSRC = os.path.join(ROOT, "mla_paged_decode_04_amd", "csrc")
 KERNEL_SOURCES = {
     "mla_decode_narrow": ("mla_internal.h", "mla_narrow.hip"),
     "mla_decode_wide": ("mla_internal.h", "mla_wide.hip"),
+    "mla_decode_wide128": ("mla_internal.h", "mla_wide128.hip"),
 }
 
 
@@ -84,7 +85,9 @@ def source_digest(kernel: str) -> str:
 
 def decode_kernel_name(rows: int) -> str:
     """The decode kernel the library launches for this many query rows."""
-    return "mla_decode_narrow" if rows <= 16 else "mla_decode_wide"
+    if rows <= 16:
+        return "mla_decode_narrow"
+    return "mla_decode_wide" if rows <= 64 else "mla_decode_wide128"
 
 
 def traffic_from_profile(kernel: str, workload: str):

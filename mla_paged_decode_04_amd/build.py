@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 # host C ABI + planner + combine, one file per decode kernel, the cache append
 # and the absorbed projections
-SRCS = [os.path.join(CSRC, f) for f in ("mla_decode.hip", "mla_narrow.hip", "mla_wide.hip", "mla_append.hip",
+SRCS = [os.path.join(CSRC, f) for f in ("mla_decode.hip", "mla_narrow.hip", "mla_wide.hip", "mla_wide128.hip", "mla_append.hip",
                                         "mla_absorb.hip")]
 LIB = os.path.join(PKG, "libmla_decode.so")
 ARCH = "gfx950"

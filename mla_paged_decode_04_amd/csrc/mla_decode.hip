@@ -31,6 +31,8 @@ namespace {
 
 constexpr int TARGET_ITEMS = 256;    // automatic split: about one work item per CU
 constexpr int MIN_CHUNK = 256;       // shortest automatic split chunk (keys)
+constexpr int ITEM_OVERHEAD = 96;    // per-item cost of the chunk search, in keys
+constexpr int ITEM_OVERHEAD_WIDE128 = 320;
 constexpr int HEADER_BYTES = 256;
 
 // ---------------------------------------------------------------------------
@@ -38,22 +40,25 @@ constexpr int HEADER_BYTES = 256;
 // ---------------------------------------------------------------------------
 
 // Row grouping: kind 0 = narrow kernel (<= 16 rows), kind 1 = wide kernel
-// with 16 rows per wave (64-row items). (A wide variant with 32 rows per wave,
-// 128-row items, exists as a template but does not fit the register file
-// without spilling, so it is not selected.)
+// with 16 rows per wave (64-row items, up to 64 rows), kind 2 = wide kernel
+// with 32 rows per wave on 32x32 MFMAs (128-row items, more than 64 rows).
 struct RowCfg {
   int kind;
-  int rgs;     // query rows per work item
-  int nrg;     // row groups per sequence
-  int target;  // work items the automatic split aims for
+  int rgs;       // query rows per work item
+  int nrg;       // row groups per sequence
+  int target;    // work items the automatic split aims for
+  int overhead;  // per-item cost in key units for the chunk search (below)
 };
 
 __host__ __device__ inline RowCfg row_config(int rows) {
   RowCfg c;
-  c.kind = rows <= 16 ? 0 : 1;
-  c.rgs = c.kind == 0 ? 16 : 64;
+  c.kind = rows <= 16 ? 0 : rows <= 64 ? 1 : 2;
+  c.rgs = c.kind == 0 ? 16 : c.kind == 1 ? 64 : 128;
   c.nrg = (rows + c.rgs - 1) / c.rgs;
   c.target = TARGET_ITEMS;
+  // A 128-row item also loads 147 KB of q and writes a 256 KB fp32 partial
+  // that the combine reads back: several times the narrow kernel's overhead.
+  c.overhead = c.kind == 2 ? ITEM_OVERHEAD_WIDE128 : ITEM_OVERHEAD;
   return c;
 }
 
@@ -82,10 +87,10 @@ __host__ __device__ inline int chunk_from_work(long long work, int forced, int t
 // plan is a list schedule of work items on SLOTS workers. For few (sequence,
 // row group) pairs the chunk is chosen among CHUNK_CANDIDATES lengths between
 // work / (4 * SLOTS) and twice work / SLOTS by an estimate of the makespan in
-// key units: every item costs its keys plus ITEM_OVERHEAD (prologue, first
+// key units: every item costs its keys plus an overhead o (prologue, first
 // tile latency, partial write); with n items of at most mx keys and wk keys
 // in all,
-//   n <= SLOTS : mx + ITEM_OVERHEAD
+//   n <= SLOTS : mx + o
 //   otherwise  : max(mx + o, ceil((wk + n * o) / SLOTS) + (mx + o) / 2).
 // Ties go to the longer chunk (fewer partials). With many pairs the split
 // from the average (work / SLOTS) is kept. All integer, so the host mirror
@@ -93,7 +98,6 @@ __host__ __device__ inline int chunk_from_work(long long work, int forced, int t
 // average split: every item then has the same length.)
 constexpr int SLOTS = 256;
 constexpr int CHUNK_CANDIDATES = 32;
-constexpr int ITEM_OVERHEAD = 96;
 constexpr int SEARCH_MAX_PAIRS = 1024;
 
 struct ChunkRange {
@@ -126,8 +130,7 @@ __host__ __device__ inline int chunk_candidate(const ChunkRange& r, int step, in
 }
 
 __host__ __device__ inline unsigned long long plan_cost(unsigned long long n, unsigned long long mx,
-                                                        unsigned long long wk) {
-  const unsigned long long o = ITEM_OVERHEAD;
+                                                        unsigned long long wk, unsigned long long o) {
   if (n <= SLOTS) return mx + o;
   const unsigned long long avg = ((wk + n * o + SLOTS - 1) >> 8) + ((mx + o) >> 1);
   static_assert(SLOTS == 256, "the shift above divides by SLOTS");
@@ -187,7 +190,7 @@ struct PlanParams {
   int32_t* header;       // [0] items [1] chunk [2] slots [3] clamp flag
   int32_t* items;        // ITEM_INTS per item
   int32_t* pairs;        // per (b, row group): first slot, number of splits
-  int batch, nrg, max_keys, forced_chunk, target;
+  int batch, nrg, max_keys, forced_chunk, target, overhead;
   long long max_items, max_slots;
 };
 
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     unsigned long long cost = ~0ull;
     int kb = lane;
     if (lane < CHUNK_CANDIDATES)
-      cost = plan_cost((unsigned long long)s_cnt[lane] * p.nrg, s_mx[lane], total_keys);
+      cost = plan_cost((unsigned long long)s_cnt[lane] * p.nrg, s_mx[lane], total_keys, p.overhead);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       const unsigned long long oc = __shfl_xor(cost, off);
@@ -345,19 +348,23 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     int n, len;
     seq_split(L, chunk, &n, &len);
     if (overflow) n = 1;
+    // pair (b, rg) owns the partial slots slot + rg * n .. + n - 1; items go
+    // chunk-major, so the row groups of one chunk are consecutive (they run
+    // side by side on one XCD and share its L2 for the cache rows)
     for (int rg = 0; rg < p.nrg; ++rg) {
-      p.pairs[2 * (b * p.nrg + rg)] = n > 1 ? slot : -1;
+      p.pairs[2 * (b * p.nrg + rg)] = n > 1 ? slot + rg * n : -1;
       p.pairs[2 * (b * p.nrg + rg) + 1] = n;
-      for (int s = 0; s < n; ++s) {
+    }
+    for (int s = 0; s < n; ++s)
+      for (int rg = 0; rg < p.nrg; ++rg) {
         if (item < p.max_items) {
           int4* it = reinterpret_cast<int4*>(p.items + (size_t)item * ITEM_INTS);
           it[0] = make_int4(b, rg, s * len, min(L, (s + 1) * len));
-          it[1] = make_int4(n > 1 ? slot + s : -1, 0, 0, 0);
+          it[1] = make_int4(n > 1 ? slot + rg * n + s : -1, 0, 0, 0);
         }
         ++item;
       }
-      if (n > 1) slot += n;
-    }
+    if (n > 1) slot += p.nrg * n;
   }
   if (tid == 0) {
     p.header[0] = overflow ? 0 : tot_items;
@@ -467,8 +474,10 @@ int max_keys_of(const mla_decode_desc_t* d) { return d->max_blocks_per_seq * d->
 void launch_decode(int kv_dtype, int kind, dim3 grid, hipStream_t st, const FwdParams& fp) {
   if (kind == 0)
     launch_narrow(kv_dtype, grid, st, fp);
+  else if (kind == 1)
+    launch_wide(kv_dtype, grid, st, fp);
   else
-    launch_wide(kv_dtype, kind, grid, st, fp);
+    launch_wide128(kv_dtype, grid, st, fp);
 }
 
 mla_status_t launch_plan(const int32_t* seq_lens, int32_t s_q, const mla_decode_desc_t* desc,
@@ -483,6 +492,7 @@ mla_status_t launch_plan(const int32_t* seq_lens, int32_t s_q, const mla_decode_
   pp.batch = desc->batch;
   pp.nrg = rc.nrg;
   pp.target = rc.target;
+  pp.overhead = rc.overhead;
   pp.max_keys = max_keys_of(desc);
   pp.forced_chunk = desc->split_keys;
   pp.max_items = ws.max_items;
@@ -658,7 +668,7 @@ int32_t mla_plan_host(const int32_t* seq_lens_host, int32_t s_q, const mla_decod
         n += nb;
         mx = std::max(mx, std::min(len, L));
       }
-      const unsigned long long cost = plan_cost((unsigned long long)n * rc.nrg, mx, keys);
+      const unsigned long long cost = plan_cost((unsigned long long)n * rc.nrg, mx, keys, rc.overhead);
       if (cost <= best) {
         best = cost;
         chunk = c;
@@ -672,18 +682,17 @@ int32_t mla_plan_host(const int32_t* seq_lens_host, int32_t s_q, const mla_decod
     int L = std::min(std::max(seq_lens_host[b], 0), max_keys);
     int n, len;
     seq_split(L, chunk, &n, &len);
-    for (int rg = 0; rg < rc.nrg; ++rg) {
-      for (int s = 0; s < n; ++s) {
+    for (int s = 0; s < n; ++s)
+      for (int rg = 0; rg < rc.nrg; ++rg) {
         if (item >= max_items) return -1;
         if (items) {
           int32_t* it = items + (size_t)item * ITEM_INTS;
           it[0] = b; it[1] = rg; it[2] = s * len; it[3] = std::min(L, (s + 1) * len);
-          it[4] = n > 1 ? slot + s : -1; it[5] = 0; it[6] = 0; it[7] = 0;
+          it[4] = n > 1 ? slot + rg * n + s : -1; it[5] = 0; it[6] = 0; it[7] = 0;
         }
         ++item;
       }
-      if (n > 1) slot += n;
-    }
+    if (n > 1) slot += rc.nrg * n;
   }
   return item;
 }

@@ -145,6 +145,7 @@ struct FwdParams {
 // Decode-kernel launchers (one per translation unit); the grid is one
 // workgroup per potential work item.
 void launch_narrow(int kv_dtype, dim3 grid, hipStream_t st, const FwdParams& fp);
-void launch_wide(int kv_dtype, int kind, dim3 grid, hipStream_t st, const FwdParams& fp);
+void launch_wide(int kv_dtype, dim3 grid, hipStream_t st, const FwdParams& fp);
+void launch_wide128(int kv_dtype, dim3 grid, hipStream_t st, const FwdParams& fp);
 
 }  // namespace mla_detail

@@ -364,8 +364,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
 
 namespace mla_detail {
 
-void launch_wide(int kv_dtype, int kind, dim3 grid, hipStream_t st, const FwdParams& fp) {
-  (void)kind;
+void launch_wide(int kv_dtype, dim3 grid, hipStream_t st, const FwdParams& fp) {
   if (kv_dtype == MLA_DTYPE_BF16)
     hipLaunchKernelGGL((mla_decode_wide<MLA_DTYPE_BF16, 1>), grid, dim3(NTHREADS), 0, st, fp);
   else

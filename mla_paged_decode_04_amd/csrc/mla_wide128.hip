@@ -1,0 +1,496 @@
+// Paged MLA decode, > 64 query rows per sequence (the 128-head cases):
+// decode attention of MLA in its MQA form ("[WIP][Attention] FlashAttn MLA",
+// description) with 128 query rows per work item, 32 per wave, on gfx950's
+// 32x32x16 bf16 MFMA. A 32-row MFMA tile feeds each LDS byte of K or V to 32
+// rows (twice the 16-row tiles), and issues at full rate with one wave per
+// SIMD. fp8 e4m3fn caches ("[Attention] Blackwell FP8 MLA support with
+// CUTLASS_MLA backend", Test Plan) are widened to bf16 in registers, right
+// before each MFMA.
+#include <type_traits>
+
+#include "mla_internal.h"
+
+using namespace mla_detail;
+
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// The ring: 4 slots of 36864 bytes (32 bf16 keys or 64 fp8 keys of 576
+// dims), three in flight while one is computed, one workgroup barrier per
+// slot. Each wave issues 9 of the 36 wave-wide 1 KB transfers of a slot.
+constexpr int X_TILE = 36864;
+constexpr int X_SLOTS = 4;
+constexpr int X_NDMA = 9;
+constexpr int X_GSTRIDE = 4096;   // bytes per 64-dim column group (both layouts)
+constexpr int X_RGS = 128;        // query rows per work item
+constexpr int X_STEP = 32;        // keys per compute step (one 32x32 S block)
+#ifndef QK_AHEAD
+#define QK_AHEAD 4                // k-steps whose K reads are issued ahead
+#endif
+#ifndef PV_AHEAD
+#define PV_AHEAD 4                // PV MFMAs whose V^T reads are issued ahead
+#endif
+
+// bf16 slot layout: [9 column groups][32 keys][8 x 16-byte chunks], chunk c of
+// key k at position c ^ swz16(k). The swizzle is a bijection of key bits 1-3
+// (for either parity of bit 0), so the 16-byte K reads of 16 consecutive keys
+// hit 16 distinct bank groups; and it flips bit 2 between keys k and k + 2, so
+// the transposed V reads (4 keys x 32 dims per 32 lanes) are conflict-free too.
+__device__ __forceinline__ int swz16(int k) {
+  return (((k >> 1) & 1) << 2) | (((k >> 3) & 1) << 1) | ((k >> 2) & 1);
+}
+// fp8 slot layout: [9 column groups][64 keys][4 x 16-byte chunks], chunk c of
+// key k at position c ^ ((k >> 2) & 3).
+__device__ __forceinline__ int swz8(int k) { return (k >> 2) & 3; }
+
+// Lanes l and l ^ 32 hold the two halves of one row's 32 scores: combine them
+// with gfx950's v_permlane32_swap (see the wide kernel for why inline asm).
+__device__ __forceinline__ float halves_max(float v) {
+  float y = v;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(v), "+v"(y));
+  return fmaxf(v, y);
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  float y = v;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(v), "+v"(y));
+  return v + y;
+}
+
+// The S^T accumulation chain is issued from inline asm so that S lives in
+// VGPRs: through the builtin the compiler gives every MFMA accumulator an
+// AGPR, and S (16) next to O (256) overflows the 256 AGPRs into spills. The
+// asm carries the hazard waits the compiler would otherwise add: a chained
+// MFMA reading exactly the previous one's result needs none; an operand
+// written by a VALU instruction needs 2 wait states before the MFMA reads it
+// (the _v forms); and VALU reads of the result wait for the last MFMA's
+// passes (qk_done, which also orders those reads after it).
+__device__ __forceinline__ void qk_first(f32x16_t& s, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_next(f32x16_t& s, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_first_v(f32x16_t& s, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_next_v(f32x16_t& s, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_done(f32x16_t& s) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
+}
+
+// LDS reads by 32-bit LDS byte address. The per-lane operand offsets are
+// formed as (slot base + lane offset) ^ (swizzle flip): the slot base is a
+// multiple of 1024, so the XOR only touches the lane offset's chunk bits, and
+// the result changes every step, which keeps the compiler from hoisting the
+// flipped variants out of the loop as extra live registers.
+__device__ __forceinline__ bf16x8_t lds_b128(uint32_t a) {
+  return *(const __attribute__((address_space(3))) bf16x8_t*)(a);
+}
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t lds_u128(uint32_t a) {
+  return *(const __attribute__((address_space(3))) u32x4_t*)(a);
+}
+__device__ __forceinline__ s16x4_t lds_tr16(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a));
+}
+__device__ __forceinline__ uint2 lds_tr8(uint32_t a) {
+  return __builtin_bit_cast(
+      uint2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(a)));
+}
+
+// MFMA operand layouts (32x32x16): A[m][k] and B[k][n] put m (or n) = lane & 31
+// and k = 8 * (lane >> 5) + i in element i; C[m][n] puts n = lane & 31 and
+// m = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3) in element e.
+//   S^T (32 keys x 32 rows) = K (A, from LDS) . Q^T (B, registers)
+//   O^T (512 dims x 32 rows) += V^T (A, transposed LDS reads) . P^T (B)
+// The C layout of S^T gives lane (row n, half h) the keys 8q + 4h + r; packed
+// in that order they are exactly the P^T operand of the two 16-key PV steps
+// once the V^T operand of step s takes keys 16s + 4h + (0..3) and
+// 16s + 8 + 4h + (0..3), which two 4-key transposed reads deliver.
+template <int KVT>
+__global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
+  constexpr bool F8 = KVT == MLA_DTYPE_FP8_E4M3FN;
+  constexpr int KT = F8 ? 64 : 32;                  // keys per ring slot
+  constexpr int ROWB = F8 ? D : D * 2;              // bytes per cached row
+  __shared__ __attribute__((aligned(1024))) char smem[X_SLOTS * X_TILE];   // 147456 bytes
+  // the rope part of Q (the last 4 k-steps), 128 rows x 128 bytes: in LDS
+  // rather than in registers, which keeps the fast loop free of spills
+  __shared__ __attribute__((aligned(1024))) char qrope[X_RGS * 128];        // 16384 bytes
+
+  // XCD-aware item order (consecutive workgroups go to different XCDs): each
+  // XCD takes a contiguous run of items. The grid is a multiple of 8.
+  const int n_items = p.header[0];
+  const int per_xcd = (n_items + 7) >> 3;
+  const int xw = blockIdx.x;
+  if ((xw >> 3) >= per_xcd) return;
+  const int item_id = (xw & 7) * per_xcd + (xw >> 3);
+  if (item_id >= n_items) return;
+  const int32_t* it = p.items + (size_t)item_id * ITEM_INTS;
+  const int b = __builtin_amdgcn_readfirstlane(it[0]);
+  const int rg = __builtin_amdgcn_readfirstlane(it[1]);
+  const int t0 = __builtin_amdgcn_readfirstlane(it[2]);
+  const int t1 = __builtin_amdgcn_readfirstlane(it[3]);
+  const int slot = __builtin_amdgcn_readfirstlane(it[4]);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n32 = lane & 31;
+  const int hi = lane >> 5;
+  const int L = __builtin_amdgcn_readfirstlane(min(max(p.seq_lens[b], 0), p.max_keys));
+  // a cache read by one row group only streams past the caches; with several
+  // row groups per sequence the other groups re-read it from L2
+  const bool stream_once = p.rows <= X_RGS;
+
+  const int row_local = 32 * w + n32;
+  const int row = rg * X_RGS + row_local;
+  const bool row_ok = row < p.rows;
+  const bool wave_active = rg * X_RGS + 32 * w < p.rows;   // wave-uniform
+  int limit = 0;
+  if (row_ok) {
+    const int tok = row / p.heads;
+    const int vis = p.causal ? L - p.s_q + 1 + tok : L;
+    limit = min(vis, t1);
+  }
+
+  // Q^T operand: k-step t holds dims 16t + 8h .. +7 (bf16), or for fp8 (whose
+  // K reads take 16 dims per lane at once) 32(t >> 1) + 16h + 8(t & 1) .. +7.
+  // Any fixed assignment of dims to k-steps gives the same dot products.
+  // k-steps 32..35 (dims 512..575 either way) go to qrope: chunk 2(t - 32) + h
+  // of row r at position (2(t - 32) + h) ^ swz16(r) of its 128 bytes. Each
+  // wave writes and reads only its own rows.
+  constexpr int QREG = D / 16 - 4;
+  bf16x8_t qb[QREG];
+  const int qr_off = row_local * 128;
+  const int qr_swz = swz16(row_local);
+  {
+    const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      const int d = F8 ? 32 * (t >> 1) + 16 * hi + 8 * (t & 1) : 16 * t + 8 * hi;
+      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + d) : make_uint4(0, 0, 0, 0);
+      if (t < QREG)
+        qb[t] = __builtin_bit_cast(bf16x8_t, v);
+      else
+        *reinterpret_cast<uint4*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4)) = v;
+    }
+  }
+  // q loads complete here, before the first (compiler-invisible) DMA
+#pragma unroll
+  for (int t = 0; t < QREG; ++t) asm volatile("" ::"v"(qb[t]));
+  auto q_operand = [&](int t) -> bf16x8_t {
+    if (t < QREG) return qb[t];
+    return *reinterpret_cast<const bf16x8_t*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4));
+  };
+
+  f32x16_t o[DV / 32];
+#pragma unroll
+  for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // ---- lane constants (byte offsets) ----
+  // DMA: lane l of transfer n lands at slot byte n * 1024 + 16 l. bf16:
+  // column group n >> 2, key 8(n & 3) + (l >> 3), position l & 7; fp8: column
+  // group n >> 2, key 16(n & 3) + (l >> 2), position l & 3. The lane fetches
+  // the global chunk that belongs at that position.
+  uint32_t dma_lane[2];
+  // K operand (key n32), bf16 k-step t: (slot + kb0) ^ ((t & 3) << 5), plus
+  // (t >> 2) * X_GSTRIDE; fp8 k-step pair u: (slot + kb0) ^ ((u & 1) << 5),
+  // plus (u >> 1) * X_GSTRIDE + 2048 * (32-key half of the slot)
+  uint32_t kb0;
+  // V^T operand, bf16 dim block db, 16-key step s, 4-key read x:
+  // (slot + vt0) ^ (64 (db & 1) + 32 x), plus (db >> 1) * X_GSTRIDE + 2048 s
+  // + 1024 x; fp8: (slot + vt0) ^ (32 (db & 1)), plus (db >> 1) * X_GSTRIDE
+  // + 2048 * half + 1024 s
+  uint32_t vt0;
+  {
+    const int g16 = (lane >> 4) & 1, ig = lane & 15;
+    if constexpr (!F8) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int key = 8 * h + (lane >> 3);   // key bits 1..3 as in transfer parity h
+        dma_lane[h] = (lane >> 3) * ROWB + (((lane & 7) ^ swz16(key)) << 4);
+      }
+      kb0 = n32 * 128 + ((hi ^ swz16(n32)) << 4);
+      const int j = ig >> 2, r = ig & 3;
+      vt0 = (4 * hi + j) * 128 + (((2 * g16 + (r >> 1)) ^ swz16(4 * hi + j)) << 4) + 8 * (r & 1);
+    } else {
+      dma_lane[0] = dma_lane[1] = (lane >> 2) * ROWB + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+      kb0 = n32 * 64 + ((hi ^ swz8(n32)) << 4);
+      const int jj = ig >> 1, q = ig & 1;
+      const int key = 4 * hi + (jj & 3) + 8 * (jj >> 2);
+      vt0 = key * 64 + ((g16 ^ swz8(key)) << 4) + 8 * q;
+    }
+  }
+
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32* bt = (const_i32*)(p.block_table + (size_t)b * p.max_blocks);
+  const int nsteps = (t1 - t0 + X_STEP - 1) / X_STEP;
+  const int ntiles = (t1 - t0 + KT - 1) / KT;
+
+  // Issue this wave's X_NDMA transfers of slot-tile j (exactly X_NDMA VMEM
+  // instructions; the vmcnt arithmetic relies on it). A tile never crosses a
+  // page: items start on 64-key boundaries and pages hold 64 or 128 keys.
+  auto issue = [&](int j) {
+    const int ts = t0 + KT * j;
+    int page = bt[ts / p.bs];
+    if (page < 0 || page >= p.num_blocks) page = 0;
+    const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts % p.bs)) * ROWB;
+    const uint32_t l0 = lds_addr(smem + (j & 3) * X_TILE);
+    auto one = [&](int i, auto nt_tag) {
+      const int n = w * X_NDMA + i;
+      const char* g = F8 ? src + (n & 3) * 16 * ROWB + (n >> 2) * 64 : src + (n & 3) * 8 * ROWB + (n >> 2) * 128;
+      const uint32_t v = F8 ? dma_lane[0] : dma_lane[n & 1];
+      if constexpr (decltype(nt_tag)::value)
+        lds_dma16_nt(g, v, l0 + n * 1024);
+      else
+        lds_dma16(g, v, l0 + n * 1024);
+    };
+    if (stream_once) {
+#pragma unroll
+      for (int i = 0; i < X_NDMA; ++i) one(i, std::true_type{});
+    } else {
+#pragma unroll
+      for (int i = 0; i < X_NDMA; ++i) one(i, std::false_type{});
+    }
+  };
+  auto valid_keys = [&](int j) {
+    const int ts = t0 + KT * j;
+    int page = bt[ts / p.bs];
+    if (page < 0 || page >= p.num_blocks) return 0;
+    return min(KT, t1 - ts);
+  };
+
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    if (k < ntiles) issue(k);
+
+  // Make slot-tile j resident for every wave: wait for this wave's transfers,
+  // zero its slots of keys past the end, barrier (tile j complete everywhere;
+  // tile j - 1 consumed by every wave), then issue tile j + 3 into the slot
+  // of tile j - 1.
+  auto prepare = [&](int j) -> const char* {
+    mem_fence_compiler();
+    const int ahead = min(2, ntiles - 1 - j);
+    if (ahead >= 2)
+      wait_vmcnt<2 * X_NDMA>();
+    else if (ahead == 1)
+      wait_vmcnt<X_NDMA>();
+    else
+      wait_vmcnt<0>();
+    mem_fence_compiler();
+    char* cur = smem + (j & 3) * X_TILE;
+    const int nv = valid_keys(j);
+    if (nv < KT) {
+      const int lk = F8 ? (lane >> 2) : (lane >> 3);   // key within the transfer
+#pragma unroll
+      for (int i = 0; i < X_NDMA; ++i) {
+        const int n = w * X_NDMA + i;
+        if (lk >= nv - (F8 ? 16 : 8) * (n & 3))
+          *reinterpret_cast<uint4*>(cur + n * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    if (j + 3 < ntiles) issue(j + 3);
+    return cur;
+  };
+
+  // One 32-key step k (slot-tile cur). The fast variant never touches the
+  // accumulators with VALU code and returns false (before consuming the
+  // step) if a row's max jumped more than BIG_SLACK above its reference.
+  auto compute = [&](const char* cur, int k, auto slow_tag) -> bool {
+    constexpr bool SLOW = decltype(slow_tag)::value;
+    if (!wave_active) return true;
+    const int ts = t0 + X_STEP * k;
+    const int half = F8 ? (k & 1) : 0;   // fp8: which 32 keys of the 64-key slot
+
+    // ---- S^T: 32 keys x this wave's 32 rows ----
+    // The K reads are software-pipelined QK_AHEAD k-steps ahead by hand: the
+    // asm MFMAs look cheap to the scheduler, which would otherwise issue each
+    // read just before its use and expose the LDS latency on every k-step.
+    f32x16_t sacc;
+    const uint32_t kbase = lds_addr(cur) + kb0;
+    if constexpr (!F8) {
+      auto kaddr = [&](int t) { return (kbase ^ ((t & 3) << 5)) + (t >> 2) * X_GSTRIDE; };
+      bf16x8_t kr[QK_AHEAD];
+#pragma unroll
+      for (int t = 0; t < QK_AHEAD; ++t) kr[t] = lds_b128(kaddr(t));
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const bf16x8_t a = kr[t % QK_AHEAD];
+        if (t + QK_AHEAD < D / 16) kr[t % QK_AHEAD] = lds_b128(kaddr(t + QK_AHEAD));
+        if (t == 0)
+          qk_first(sacc, a, q_operand(0));
+        else
+          qk_next(sacc, a, q_operand(t));
+      }
+    } else {
+      auto kaddr = [&](int u) { return (kbase ^ ((u & 1) << 5)) + (u >> 1) * X_GSTRIDE + 2048 * half; };
+      constexpr int AH = (QK_AHEAD + 1) / 2;   // reads cover two k-steps each
+      u32x4_t kr[AH];
+#pragma unroll
+      for (int u = 0; u < AH; ++u) kr[u] = lds_u128(kaddr(u));
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u) {
+        const u32x4_t v = kr[u % AH];
+        if (u + AH < D / 32) kr[u % AH] = lds_u128(kaddr(u + AH));
+        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(v[0], v[1]));
+        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(v[2], v[3]));
+        if (u == 0)
+          qk_first_v(sacc, a0, q_operand(0));
+        else
+          qk_next_v(sacc, a0, q_operand(2 * u));
+        qk_next_v(sacc, a1, q_operand(2 * u + 1));
+      }
+    }
+    qk_done(sacc);
+
+    // ---- online softmax on the raw scores (scale folded into max and FMA) ----
+    float x[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = sacc[e];
+    if (__builtin_amdgcn_ballot_w64(ts + X_STEP > limit)) {   // a step that reaches a row's limit
+      const int rel = limit - ts - 4 * hi;   // element e is visible iff 8(e >> 2) + (e & 3) < rel
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] = 8 * (e >> 2) + (e & 3) < rel ? x[e] : -INFINITY;
+    }
+    float tmax = x[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, x[e]);
+    tmax = halves_max(tmax) * p.scale_log2;
+    if constexpr (!SLOW) {
+      if (m_run == -INFINITY) m_run = tmax;   // o and l of this row are still zero
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + BIG_SLACK)) return false;
+    } else {
+      // unconditional (alpha = 1 for rows whose max did not move): a
+      // conditional rescale merges two versions of O and makes the compiler
+      // hold all of O in VGPRs; one block at a time needs 16 temporaries
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);   // m_run = -inf gives 0
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d) {
+        o[d] *= alpha;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // rows without any key so far keep m = -inf: a finite stand-in makes
+    // their masked scores give exp2(-inf) = 0, never NaN
+    const float neg_m = -fmaxf(m_run, -1e30f);
+    float pe[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], p.scale_log2, neg_m));
+      l_run += pe[e];
+    }
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      pb[s] = __builtin_bit_cast(
+          bf16x8_t, make_uint4(pack_bf16x2(pe[8 * s], pe[8 * s + 1]), pack_bf16x2(pe[8 * s + 2], pe[8 * s + 3]),
+                               pack_bf16x2(pe[8 * s + 4], pe[8 * s + 5]), pack_bf16x2(pe[8 * s + 6], pe[8 * s + 7])));
+
+    // keep the V^T reads of the PV loop out of the softmax code above (their
+    // registers would stay live across it)
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- O^T += V^T P^T over the two 16-key steps ----
+    const uint32_t vbase = lds_addr(cur) + vt0;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db) {
+        bf16x8_t a;
+        if constexpr (!F8) {
+          const uint32_t off = (db >> 1) * X_GSTRIDE + 2048 * s;
+          const s16x4_t a0 = lds_tr16((vbase ^ (64 * (db & 1))) + off);
+          const s16x4_t a1 = lds_tr16((vbase ^ (64 * (db & 1) + 32)) + off + 1024);
+          a = __builtin_bit_cast(
+              bf16x8_t, make_uint4(__builtin_bit_cast(uint2, a0).x, __builtin_bit_cast(uint2, a0).y,
+                                   __builtin_bit_cast(uint2, a1).x, __builtin_bit_cast(uint2, a1).y));
+        } else {
+          const uint2 v = lds_tr8((vbase ^ (32 * (db & 1))) + (db >> 1) * X_GSTRIDE + 2048 * half + 1024 * s);
+          a = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(v.x, v.y));
+        }
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], o[db], 0, 0, 0);
+      }
+    }
+    // Interleave the PV reads and MFMAs with a bounded read-ahead: left to
+    // itself the scheduler issues nearly all 64 reads first, and the
+    // registers they hold push the loop's lane constants out to scratch.
+    {
+      constexpr int RPM = F8 ? 1 : 2;   // LDS reads per MFMA
+#pragma unroll
+      for (int i = 0; i < PV_AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * (DV / 32) - PV_AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < PV_AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    return true;
+  };
+
+  int k = 0;
+  const char* cur = nullptr;
+  for (; k < nsteps; ++k) {
+    if (!F8 || (k & 1) == 0) cur = prepare(F8 ? (k >> 1) : k);
+    if (!compute(cur, k, std::false_type{})) break;
+  }
+  if (k < nsteps) {   // rare: finish with rescaling, starting at the resident step k
+    compute(cur, k, std::true_type{});
+    for (++k; k < nsteps; ++k) {
+      if (!F8 || (k & 1) == 0) cur = prepare(F8 ? (k >> 1) : k);
+      compute(cur, k, std::true_type{});
+    }
+  }
+
+  // ---- write this wave's rows: final (slot < 0) or split partial ----
+  const float l_row = halves_sum(l_run);
+  if (row_ok) {
+    const bool empty = !(l_row > 0.f);
+    const float inv = empty ? 0.f : p.out_scale / l_row;
+    const float lse2 = empty ? -INFINITY : m_run + log2f(l_row);
+    const size_t orow = (size_t)b * p.rows + row;
+    if (slot < 0) {
+      uint16_t* dst = p.out + orow * DV + 4 * hi;
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint2*>(dst + 32 * db + 8 * q) =
+              make_uint2(pack_bf16x2(o[db][4 * q] * inv, o[db][4 * q + 1] * inv),
+                         pack_bf16x2(o[db][4 * q + 2] * inv, o[db][4 * q + 3] * inv));
+      if (p.lse != nullptr && hi == 0) p.lse[orow] = lse2 * LN2;
+    } else {
+      float* dst = p.part_o + ((size_t)slot * X_RGS + row_local) * DV + 4 * hi;
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4_t*>(dst + 32 * db + 8 * q) =
+              f32x4_t{o[db][4 * q], o[db][4 * q + 1], o[db][4 * q + 2], o[db][4 * q + 3]} * inv;
+      if (hi == 0) p.part_lse[(size_t)slot * X_RGS + row_local] = lse2;
+    }
+  }
+}
+
+}  // namespace
+
+namespace mla_detail {
+
+void launch_wide128(int kv_dtype, dim3 grid, hipStream_t st, const FwdParams& fp) {
+  if (kv_dtype == MLA_DTYPE_BF16)
+    hipLaunchKernelGGL((mla_decode_wide128<MLA_DTYPE_BF16>), grid, dim3(NTHREADS), 0, st, fp);
+  else
+    hipLaunchKernelGGL((mla_decode_wide128<MLA_DTYPE_FP8_E4M3FN>), grid, dim3(NTHREADS), 0, st, fp);
+}
+
+}  // namespace mla_detail
