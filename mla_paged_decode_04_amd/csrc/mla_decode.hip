@@ -13,11 +13,12 @@
 //                          O^T += V^T P^T on bf16 MFMA with a base-2 online
 //                          softmax; writes the final rows or a split partial
 //                          (fp32 normalised o, base-2 lse):
-//        mla_decode_narrow  <= 16 query rows per sequence (HBM-bound): every
-//                           wave streams its own key tiles HBM -> LDS
-//        mla_decode_wide    32 / 64 / 128 rows per item (MFMA-heavy): two
-//                           wave pairs share the key tiles; the waves of a
-//                           pair split the head dimensions
+//        mla_decode_narrow   <= 16 query rows per sequence (HBM-bound): every
+//                            wave streams its own key tiles HBM -> LDS
+//        mla_decode_wide     17..64 rows: 64-row items, 16 rows per wave on
+//                            16x16x32 MFMA, the waves share the key tiles
+//        mla_decode_wide128  > 64 rows: 128-row items, 32 rows per wave on
+//                            32x32x16 MFMA
 //   3. mla_combine_kernel  merges the partials of split (sequence, row group)
 //                          pairs with log-sum-exp weights
 #include <algorithm>
