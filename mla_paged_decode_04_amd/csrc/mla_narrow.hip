@@ -165,20 +165,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
     limit = min(vis, t1);
   }
 
-  bf16x8_t qb[D / 32];
-  {
-    const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
-                       : make_uint4(0, 0, 0, 0);
-      qb[s] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
-  // Consume the q loads here, so the compiler's own vmcnt wait for them sits
-  // before the first DMA and not inside the tile loop (it cannot see the DMAs).
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s) asm volatile("" ::"v"(qb[s]));
+  bf16x8_t qb[D / 32];   // loaded below, after this wave's first tile was requested
 
   f32x4_t o[DV / 16];
 #pragma unroll
@@ -366,6 +353,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
   int j = w, itn = 0;
   const char* cur = nullptr;
   if (w < ntiles) issue(w, wbuf);
+  // q is loaded while the first tile is in flight. Its loads are consumed
+  // here, so the compiler's own vmcnt wait for them (which also covers the
+  // older tile transfers) sits before the tile loop, not inside it (it cannot
+  // see the DMAs).
+  {
+    const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
+                       : make_uint4(0, 0, 0, 0);
+      qb[s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) asm volatile("" ::"v"(qb[s]));
   for (; j < ntiles; j += 4, ++itn) {
     cur = prepare(j, itn);
     if (!compute(cur, t0 + KT * j, std::false_type{})) break;

@@ -156,43 +156,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
     limit = min(vis, t1);
   }
 
-  // Q^T operand: k-step t holds dims 16t + 8h .. +7 (bf16), or for fp8 (whose
-  // K reads take 16 dims per lane at once) 32(t >> 1) + 16h + 8(t & 1) .. +7.
-  // Any fixed assignment of dims to k-steps gives the same dot products.
-  // k-steps 32..35 (dims 512..575 either way) go to qrope: chunk 2(t - 32) + h
-  // of row r at position (2(t - 32) + h) ^ swz16(r) of its 128 bytes. Each
-  // wave writes and reads only its own rows.
-  constexpr int QREG = D / 16 - 4;
-  bf16x8_t qb[QREG];
-  const int qr_off = row_local * 128;
-  const int qr_swz = swz16(row_local);
-  {
-    const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      const int d = F8 ? 32 * (t >> 1) + 16 * hi + 8 * (t & 1) : 16 * t + 8 * hi;
-      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + d) : make_uint4(0, 0, 0, 0);
-      if (t < QREG)
-        qb[t] = __builtin_bit_cast(bf16x8_t, v);
-      else
-        *reinterpret_cast<uint4*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4)) = v;
-    }
-  }
-  // q loads complete here, before the first (compiler-invisible) DMA
-#pragma unroll
-  for (int t = 0; t < QREG; ++t) asm volatile("" ::"v"(qb[t]));
-  auto q_operand = [&](int t) -> bf16x8_t {
-    if (t < QREG) return qb[t];
-    return *reinterpret_cast<const bf16x8_t*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4));
-  };
-
-  f32x16_t o[DV / 32];
-#pragma unroll
-  for (int d = 0; d < DV / 32; ++d)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
   // ---- lane constants (byte offsets) ----
   // DMA: lane l of transfer n lands at slot byte n * 1024 + 16 l. bf16:
   // column group n >> 2, key 8(n & 3) + (l >> 3), position l & 7; fp8: column
@@ -266,9 +229,52 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
     return min(KT, t1 - ts);
   };
 
+  // The first three tiles are requested before q is loaded, so their
+  // latency overlaps the q loads (the compiler's own wait for q below also
+  // covers them; they were issued first).
 #pragma unroll
   for (int k = 0; k < 3; ++k)
     if (k < ntiles) issue(k);
+
+  // Q^T operand: k-step t holds dims 16t + 8h .. +7 (bf16), or for fp8 (whose
+  // K reads take 16 dims per lane at once) 32(t >> 1) + 16h + 8(t & 1) .. +7.
+  // Any fixed assignment of dims to k-steps gives the same dot products.
+  // k-steps 32..35 (dims 512..575 either way) go to qrope: chunk 2(t - 32) + h
+  // of row r at position (2(t - 32) + h) ^ swz16(r) of its 128 bytes. Each
+  // wave writes and reads only its own rows.
+  constexpr int QREG = D / 16 - 4;
+  bf16x8_t qb[QREG];
+  const int qr_off = row_local * 128;
+  const int qr_swz = swz16(row_local);
+  {
+    const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      const int d = F8 ? 32 * (t >> 1) + 16 * hi + 8 * (t & 1) : 16 * t + 8 * hi;
+      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + d) : make_uint4(0, 0, 0, 0);
+      if (t < QREG)
+        qb[t] = __builtin_bit_cast(bf16x8_t, v);
+      else
+        *reinterpret_cast<uint4*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4)) = v;
+    }
+  }
+  // q loads (and with them the three tiles issued before) complete here, so
+  // the compiler places no wait for them inside the tile loop (it cannot see
+  // the DMAs)
+#pragma unroll
+  for (int t = 0; t < QREG; ++t) asm volatile("" ::"v"(qb[t]));
+  auto q_operand = [&](int t) -> bf16x8_t {
+    if (t < QREG) return qb[t];
+    return *reinterpret_cast<const bf16x8_t*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4));
+  };
+
+  f32x16_t o[DV / 32];
+#pragma unroll
+  for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
 
   // Make slot-tile j resident for every wave: wait for this wave's transfers,
   // zero its slots of keys past the end, barrier (tile j complete everywhere;
@@ -453,31 +459,47 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   }
 
   // ---- write this wave's rows: final (slot < 0) or split partial ----
+  // The rows leave through LDS (the ring is free once every wave is past its
+  // last step): a wave stages its 32 rows x 256 dims at a time, then writes
+  // whole row segments, so each store instruction covers 1 KB (fp32) or 512 B
+  // (bf16) of one row instead of scattered 16-byte pieces.
   const float l_row = halves_sum(l_run);
-  if (row_ok) {
-    const bool empty = !(l_row > 0.f);
-    const float inv = empty ? 0.f : p.out_scale / l_row;
-    const float lse2 = empty ? -INFINITY : m_run + log2f(l_row);
-    const size_t orow = (size_t)b * p.rows + row;
+  const bool empty = !(l_row > 0.f);
+  const float inv = empty ? 0.f : p.out_scale / l_row;
+  const float lse2 = empty ? -INFINITY : m_run + log2f(l_row);
+  if (row_ok && hi == 0) {
     if (slot < 0) {
-      uint16_t* dst = p.out + orow * DV + 4 * hi;
-#pragma unroll
-      for (int db = 0; db < DV / 32; ++db)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<uint2*>(dst + 32 * db + 8 * q) =
-              make_uint2(pack_bf16x2(o[db][4 * q] * inv, o[db][4 * q + 1] * inv),
-                         pack_bf16x2(o[db][4 * q + 2] * inv, o[db][4 * q + 3] * inv));
-      if (p.lse != nullptr && hi == 0) p.lse[orow] = lse2 * LN2;
+      if (p.lse != nullptr) p.lse[(size_t)b * p.rows + row] = lse2 * LN2;
     } else {
-      float* dst = p.part_o + ((size_t)slot * X_RGS + row_local) * DV + 4 * hi;
+      p.part_lse[(size_t)slot * X_RGS + row_local] = lse2;
+    }
+  }
+  __syncthreads();   // every wave is done with the ring
+  constexpr int SROW = 260;   // floats per staged row: 256 + 4 (rows 16 bytes apart in the banks)
+  static_assert(4 * 32 * SROW * 4 <= X_SLOTS * X_TILE, "staging fits in the ring");
+  float* stage = reinterpret_cast<float*>(smem) + w * 32 * SROW;
+  const int nrow = min(32, p.rows - (rg * X_RGS + 32 * w));   // this wave's valid rows (wave-uniform)
 #pragma unroll
-      for (int db = 0; db < DV / 32; ++db)
+  for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f32x4_t*>(dst + 32 * db + 8 * q) =
-              f32x4_t{o[db][4 * q], o[db][4 * q + 1], o[db][4 * q + 2], o[db][4 * q + 3]} * inv;
-      if (hi == 0) p.part_lse[(size_t)slot * X_RGS + row_local] = lse2;
+    for (int db = 0; db < DV / 64; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x16_t& a = o[(DV / 64) * hf + db];
+        *reinterpret_cast<f32x4_t*>(stage + n32 * SROW + 32 * db + 8 * q + 4 * hi) =
+            f32x4_t{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]} * inv;
+      }
+    // a wave's LDS accesses complete in order: the reads below see the writes
+    for (int r = 0; r < nrow; ++r) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + r * SROW + 4 * lane);
+      const int rl = 32 * w + r;
+      if (slot < 0) {
+        uint16_t* dst = p.out + ((size_t)b * p.rows + rg * X_RGS + rl) * DV + (DV / 2) * hf + 4 * lane;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      } else {
+        float* dst = p.part_o + ((size_t)slot * X_RGS + rl) * DV + (DV / 2) * hf + 4 * lane;
+        *reinterpret_cast<f32x4_t*>(dst) = v;
+      }
     }
   }
 }
