@@ -336,14 +336,26 @@ def bench_absorb(T: int, H: int, d: int, steps: int, warmup: int):
     ms = e0.elapsed_time(e1) / steps
     flops = 2 * 2 * T * H * d * 512
     tfs = flops / (ms * 1e-3) / 1e12
+    # algorithmic bytes: every operand read once, every result written once
+    nbytes = 2 * (T * H * d + T * H * 64 + H * d * 512 + T * H * 576      # absorb_q
+                  + T * H * 512 + H * 512 * d + T * H * d)                # absorb_out
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFS * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
+    roof["traffic"] = None
     return {"metric": "absorbed projections (mla_absorb_q + mla_absorb_out) TFLOP/s",
             "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
             "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": f"absorb_T{T}_H{H}_d{d}", "tokens": T, "heads": H, "d": d},
-            "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
-                         "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
-                         "traffic": None}}
+            "gbs": round(gbs, 1), "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "roofline": roof}
 
 
 def copy_calibration(mib: int = 1024, reps: int = 3):

@@ -14,9 +14,8 @@ namespace {
 
 constexpr int G_THREADS = 256;                  // 4 waves
 constexpr int G_TM = 64;                        // tokens per tile (16 per wave)
-constexpr int G_TN = 64;                        // output columns per tile
 constexpr int G_TK = 32;                        // k per step
-constexpr int G_BROW = G_TN * 2 + 8;            // LDS row of the B tile: 136 bytes
+constexpr int G_TN_MAX = 512;                   // output columns per tile (at most)
 
 struct GemmParams {
   const uint16_t* a;       // A(t, h, k) = a[(t * H + h) * lda + k]
@@ -32,11 +31,22 @@ __device__ __forceinline__ s16x4_t gemm_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(p));
 }
 
+// One workgroup: 64 tokens x TN output columns of one head. The B tile of
+// every k-step (32 x TN) is staged in LDS (double-buffered, one barrier per
+// step); the lane's A fragment comes from global memory one step ahead. With
+// TN covering a whole output row (512 for absorb_q, d_v for absorb_out), the
+// C tile is staged in LDS at the end and every row leaves as one contiguous
+// run (the output is the larger part of the traffic).
+template <int TN>
 __global__ __launch_bounds__(G_THREADS) void mla_bgemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) char bt[2][G_TK * G_BROW];
+  constexpr int BROW = TN * 2 + 8;              // LDS row of the B tile (bytes)
+  constexpr int CROW = TN * 2 + 16;             // LDS row of the staged C tile (bytes)
+  constexpr int B_BYTES = 2 * G_TK * BROW;
+  constexpr int C_BYTES = G_TM * CROW;
+  __shared__ __attribute__((aligned(16))) char lds[B_BYTES > C_BYTES ? B_BYTES : C_BYTES];
   const int h = blockIdx.z;
   const int t0 = blockIdx.y * G_TM;
-  const int n0 = blockIdx.x * G_TN;
+  const int n0 = blockIdx.x * TN;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
 
@@ -54,31 +64,49 @@ __global__ __launch_bounds__(G_THREADS) void mla_bgemm_kernel(GemmParams p) {
   const bool t_ok = t < p.T;
   const uint16_t* arow = p.a + ((size_t)(t_ok ? t : 0) * p.H + h) * p.lda;
   const uint16_t* bmat = p.b + (size_t)h * p.K * p.N + n0;
-  // B tile loads: thread -> (k row tid >> 3, 8 columns at 8 * (tid & 7))
-  const int bk = tid >> 3, bn = 8 * (tid & 7);
+  // B tile loads: 16-byte chunk i of the step's 32 x TN tile is k row
+  // i / (TN / 8), columns 8 (i % (TN / 8)); each thread takes chunks tid + 256 m
+  constexpr int BCH = G_TK * TN / 8 / G_THREADS;        // chunks per thread
   // B^T operand of column tile nt: lane 4j + q of each 16-lane group supplies
   // columns 16nt + 4q .. +3 of k row 8g + j (+ 4 for the second read)
   const int jj = (lane >> 2) & 3, qq = lane & 3;
 
-  f32x4_t acc[G_TN / 16];
+  f32x4_t acc[TN / 16];
 #pragma unroll
-  for (int nt = 0; nt < G_TN / 16; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < TN / 16; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int steps = p.K / G_TK;
-  uint4 bnext = *reinterpret_cast<const uint4*>(bmat + (size_t)bk * p.N + bn);
-  for (int s = 0; s < steps; ++s) {
-    char* buf = bt[s & 1];
-    *reinterpret_cast<uint4*>(buf + bk * G_BROW + bn * 2) = bnext;
-    if (s + 1 < steps)
-      bnext = *reinterpret_cast<const uint4*>(bmat + (size_t)((s + 1) * G_TK + bk) * p.N + bn);
-    const uint4 av = t_ok ? *reinterpret_cast<const uint4*>(arow + s * G_TK + 8 * g) : make_uint4(0, 0, 0, 0);
-    __syncthreads();   // B tile s in LDS (buffer s & 1 was last read in step s - 2)
-    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+  uint4 bnext[BCH];
+  auto load_b = [&](int s) {
 #pragma unroll
-    for (int nt = 0; nt < G_TN / 16; ++nt) {
-      const char* src = buf + (8 * g + jj) * G_BROW + (16 * nt + 4 * qq) * 2;
+    for (int m = 0; m < BCH; ++m) {
+      const int i = tid + G_THREADS * m;
+      bnext[m] = *reinterpret_cast<const uint4*>(bmat + (size_t)(s * G_TK + i / (TN / 8)) * p.N + 8 * (i % (TN / 8)));
+    }
+  };
+  auto load_a = [&](int s) {
+    return t_ok ? *reinterpret_cast<const uint4*>(arow + s * G_TK + 8 * g) : make_uint4(0, 0, 0, 0);
+  };
+  load_b(0);
+  uint4 anext = load_a(0);
+  for (int s = 0; s < steps; ++s) {
+    char* buf = lds + (s & 1) * G_TK * BROW;
+#pragma unroll
+    for (int m = 0; m < BCH; ++m) {
+      const int i = tid + G_THREADS * m;
+      *reinterpret_cast<uint4*>(buf + (i / (TN / 8)) * BROW + (i % (TN / 8)) * 16) = bnext[m];
+    }
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, anext);
+    if (s + 1 < steps) {
+      load_b(s + 1);
+      anext = load_a(s + 1);
+    }
+    __syncthreads();   // B tile s in LDS (buffer s & 1 was last read in step s - 2)
+#pragma unroll
+    for (int nt = 0; nt < TN / 16; ++nt) {
+      const char* src = buf + (8 * g + jj) * BROW + (16 * nt + 4 * qq) * 2;
       const s16x4_t b0 = gemm_read_tr(src);
-      const s16x4_t b1 = gemm_read_tr(src + 4 * G_BROW);
+      const s16x4_t b1 = gemm_read_tr(src + 4 * BROW);
       const bf16x8_t bf = __builtin_bit_cast(
           bf16x8_t, make_uint4(__builtin_bit_cast(uint2, b0).x, __builtin_bit_cast(uint2, b0).y,
                                __builtin_bit_cast(uint2, b1).x, __builtin_bit_cast(uint2, b1).y));
@@ -86,13 +114,125 @@ __global__ __launch_bounds__(G_THREADS) void mla_bgemm_kernel(GemmParams p) {
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, a, acc[nt], 0, 0, 0);
     }
   }
-  // acc[nt] lane (c16 = token, g) holds C[t][n0 + 16nt + 4g + j], j = 0..3
-  if (t_ok) {
-    uint16_t* crow = p.c + ((size_t)t * p.H + h) * p.ldc + n0;
+  // acc[nt] lane (c16 = token, g) holds C[t][n0 + 16nt + 4g + j], j = 0..3:
+  // stage the 64 x TN tile as bf16, then write whole row runs
+  __syncthreads();   // every wave is done with the B buffers
+  {
+    char* crow = lds + (16 * w + c16) * CROW;
 #pragma unroll
-    for (int nt = 0; nt < G_TN / 16; ++nt)
-      *reinterpret_cast<uint2*>(crow + 16 * nt + 4 * g) =
+    for (int nt = 0; nt < TN / 16; ++nt)
+      *reinterpret_cast<uint2*>(crow + (16 * nt + 4 * g) * 2) =
           make_uint2(pack_bf16x2(acc[nt][0], acc[nt][1]), pack_bf16x2(acc[nt][2], acc[nt][3]));
+  }
+  __syncthreads();
+  constexpr int CCH = TN / 8;                            // 16-byte chunks per row
+  for (int i = tid; i < G_TM * CCH; i += G_THREADS) {
+    const int r = i / CCH, c = i % CCH;
+    const int tt = t0 + r;
+    if (tt < p.T)
+      *reinterpret_cast<uint4*>(p.c + ((size_t)tt * p.H + h) * p.ldc + n0 + 8 * c) =
+          *reinterpret_cast<const uint4*>(lds + r * CROW + c * 16);
+  }
+}
+
+// Weight-stationary variant for many tokens: the workgroup keeps its head's
+// K x TN slice of B in LDS for the whole launch and runs TPW token tiles of 64
+// through it, so B is read once per workgroup instead of once per 64 tokens.
+// A fragments are read from global memory AH k-steps ahead (a register ring
+// whose slot for flat k-step f is f % AH; AH divides the k-steps per tile),
+// which keeps enough reads in flight with one workgroup per CU. No barrier is
+// needed inside a tile: B does not change.
+template <int TN, int KMAX, int WS_AHEAD, int WS_TPW>   // WS_TPW: token tiles per workgroup
+__global__ __launch_bounds__(G_THREADS) void mla_bgemm_ws_kernel(GemmParams p) {
+  constexpr int BROW = TN * 2 + 8;
+  constexpr int CROW = TN * 2 + 16;
+  __shared__ __attribute__((aligned(16))) char bsm[KMAX * BROW];
+  __shared__ __attribute__((aligned(16))) char csm[G_TM * CROW];
+  const int h = blockIdx.z;
+  const int n0 = blockIdx.x * TN;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int jj = (lane >> 2) & 3, qq = lane & 3;
+  const int K = p.K;
+  const int steps = K / G_TK;
+
+  // B slice: K rows x TN columns, 16-byte chunks spread over all threads
+  {
+    const uint16_t* bmat = p.b + (size_t)h * K * p.N + n0;
+    for (int i = tid; i < K * (TN / 8); i += G_THREADS) {
+      const int r = i / (TN / 8), c = i % (TN / 8);
+      *reinterpret_cast<uint4*>(bsm + r * BROW + c * 16) =
+          *reinterpret_cast<const uint4*>(bmat + (size_t)r * p.N + 8 * c);
+    }
+  }
+  __syncthreads();
+
+  const int tile0 = blockIdx.y * WS_TPW;
+  const int ntile = min(WS_TPW, (p.T + G_TM - 1) / G_TM - tile0);
+  // the flat k-step sequence of this workgroup: tile u, step s -> u * steps + s
+  const int total = ntile * steps;
+  auto load_a = [&](int f) {
+    const int u = f / steps, s = f - u * steps;
+    const int t = (tile0 + u) * G_TM + 16 * w + c16;
+    if (t >= p.T) return make_uint4(0, 0, 0, 0);
+    return *reinterpret_cast<const uint4*>(p.a + ((size_t)t * p.H + h) * p.lda + s * G_TK + 8 * g);
+  };
+  uint4 ring[WS_AHEAD];
+#pragma unroll
+  for (int i = 0; i < WS_AHEAD; ++i) ring[i] = i < total ? load_a(i) : make_uint4(0, 0, 0, 0);
+
+  for (int u = 0; u < ntile; ++u) {
+    const int t0 = (tile0 + u) * G_TM;
+    if (p.pe != nullptr && blockIdx.x == 0) {   // the rotary part of q
+      for (int i = tid; i < G_TM * 8; i += G_THREADS) {
+        const int t = t0 + (i >> 3), c = i & 7;
+        if (t < p.T)
+          *reinterpret_cast<uint4*>(p.c + ((size_t)t * p.H + h) * p.ldc + 512 + 8 * c) =
+              *reinterpret_cast<const uint4*>(p.pe + ((size_t)t * p.H + h) * 64 + 8 * c);
+      }
+    }
+    f32x4_t acc[TN / 16];
+#pragma unroll
+    for (int nt = 0; nt < TN / 16; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < steps; s += WS_AHEAD) {
+#pragma unroll
+      for (int i = 0; i < WS_AHEAD; ++i) {
+        {
+          const int f = u * steps + s + i;
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ring[i]);
+          if (f + WS_AHEAD < total) ring[i] = load_a(f + WS_AHEAD);
+          const char* bk = bsm + (s + i) * G_TK * BROW;
+#pragma unroll
+          for (int nt = 0; nt < TN / 16; ++nt) {
+            const char* src = bk + (8 * g + jj) * BROW + (16 * nt + 4 * qq) * 2;
+            const s16x4_t b0 = gemm_read_tr(src);
+            const s16x4_t b1 = gemm_read_tr(src + 4 * BROW);
+            const bf16x8_t bf = __builtin_bit_cast(
+                bf16x8_t, make_uint4(__builtin_bit_cast(uint2, b0).x, __builtin_bit_cast(uint2, b0).y,
+                                     __builtin_bit_cast(uint2, b1).x, __builtin_bit_cast(uint2, b1).y));
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, a, acc[nt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // stage the 64 x TN tile as bf16, then write whole row runs
+    {
+      char* crow = csm + (16 * w + c16) * CROW;
+#pragma unroll
+      for (int nt = 0; nt < TN / 16; ++nt)
+        *reinterpret_cast<uint2*>(crow + (16 * nt + 4 * g) * 2) =
+            make_uint2(pack_bf16x2(acc[nt][0], acc[nt][1]), pack_bf16x2(acc[nt][2], acc[nt][3]));
+    }
+    __syncthreads();
+    constexpr int CCH = TN / 8;
+    for (int i = tid; i < G_TM * CCH; i += G_THREADS) {
+      const int r = i / CCH, c = i % CCH;
+      const int tt = t0 + r;
+      if (tt < p.T)
+        *reinterpret_cast<uint4*>(p.c + ((size_t)tt * p.H + h) * p.ldc + n0 + 8 * c) =
+            *reinterpret_cast<const uint4*>(csm + r * CROW + c * 16);
+    }
+    __syncthreads();   // csm is rewritten by the next tile
   }
 }
 
@@ -100,8 +240,30 @@ bool al(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % 
 
 mla_status_t launch_bgemm(const GemmParams& gp, void* stream) {
   if (gp.T == 0) return MLA_OK;
-  const dim3 grid(gp.N / G_TN, (gp.T + G_TM - 1) / G_TM, gp.H);
-  hipLaunchKernelGGL(mla_bgemm_kernel, grid, dim3(G_THREADS), 0, static_cast<hipStream_t>(stream), gp);
+  hipStream_t st0 = static_cast<hipStream_t>(stream);
+  const int tiles = (gp.T + G_TM - 1) / G_TM;
+  // many tokens: weight-stationary. Narrow column slices keep the LDS per
+  // workgroup small enough for two or more workgroups per CU (measured faster
+  // than wider slices, which read A fewer times).
+  if (gp.N == 512 && gp.K == 128 && tiles >= 32) {   // absorb_q, d_nope = 128: 128-column slices
+    const unsigned ty = (unsigned)((tiles + 15) / 16);
+    hipLaunchKernelGGL((mla_bgemm_ws_kernel<128, 128, 4, 16>), dim3(4, ty, gp.H), dim3(G_THREADS), 0, st0, gp);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
+  if (gp.K == 512 && gp.N % 64 == 0 && tiles >= 64) {   // absorb_out: 64-column slices
+    const unsigned ty = (unsigned)((tiles + 31) / 32);
+    hipLaunchKernelGGL((mla_bgemm_ws_kernel<64, 512, 8, 32>), dim3(gp.N / 64, ty, gp.H), dim3(G_THREADS), 0, st0, gp);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
+  // absorb_q (N = 512, K = d_nope): whole 512-column rows per tile; otherwise
+  // 64-column tiles, which keep more workgroups in flight over the long K
+  const int tn = gp.N == 512 && tiles * gp.H >= 512 ? 512 : 64;
+  const dim3 grid(gp.N / tn, (gp.T + G_TM - 1) / G_TM, gp.H);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (tn) {
+    case 512: hipLaunchKernelGGL(mla_bgemm_kernel<512>, grid, dim3(G_THREADS), 0, st, gp); break;
+    default: hipLaunchKernelGGL(mla_bgemm_kernel<64>, grid, dim3(G_THREADS), 0, st, gp); break;
+  }
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -130,8 +292,8 @@ extern "C" mla_status_t mla_absorb_q(const void* q_nope, const void* q_pe, const
 
 extern "C" mla_status_t mla_absorb_out(const void* o, const void* w_uv, void* out, int32_t tokens,
                                        int32_t heads, int32_t d_v, void* stream) {
-  if (tokens < 0 || heads < 1 || heads > MLA_MAX_HEADS || d_v < G_TN) return MLA_ERR_INVALID_ARGUMENT;
-  if (d_v % G_TN != 0 || d_v > 4096) return MLA_ERR_UNSUPPORTED;
+  if (tokens < 0 || heads < 1 || heads > MLA_MAX_HEADS || d_v < 64) return MLA_ERR_INVALID_ARGUMENT;
+  if (d_v % 64 != 0 || d_v > 4096) return MLA_ERR_UNSUPPORTED;
   if (tokens == 0) return MLA_OK;
   if (o == nullptr || w_uv == nullptr || out == nullptr) return MLA_ERR_INVALID_ARGUMENT;
   if (!al(o, 16) || !al(w_uv, 16) || !al(out, 16)) return MLA_ERR_INVALID_ARGUMENT;

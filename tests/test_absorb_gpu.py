@@ -27,7 +27,9 @@ def dev(bits):
     return torch.from_numpy(bits.view(np.int16)).to("cuda:0").view(torch.bfloat16)
 
 
-@pytest.mark.parametrize("T,H,d", [(128, 16, 128), (64, 128, 128), (37, 3, 64), (1, 1, 32)])
+# 2100 tokens: absorb_q takes the weight-stationary path (33 token tiles: 16 + 16 + 1,
+# the last one ragged); 4200 tokens do the same for absorb_out (66 tiles: 32 + 32 + 2)
+@pytest.mark.parametrize("T,H,d", [(128, 16, 128), (64, 128, 128), (37, 3, 64), (1, 1, 32), (2100, 2, 128)])
 def test_absorb_q(mla, T, H, d):
     rng = np.random.default_rng(T * 1000 + H)
     qn, pe, w = bf16(rng, (T, H, d)), bf16(rng, (T, H, 64)), bf16(rng, (H, d, 512), d ** -0.5)
@@ -39,7 +41,8 @@ def test_absorb_q(mla, T, H, d):
     np.testing.assert_array_equal(got[..., 512:], ref[..., 512:])
 
 
-@pytest.mark.parametrize("T,H,dv", [(128, 16, 128), (64, 128, 128), (37, 3, 64), (5, 2, 192)])
+@pytest.mark.parametrize("T,H,dv", [(128, 16, 128), (64, 128, 128), (37, 3, 64), (5, 2, 192),
+                                    (4200, 2, 128), (4200, 3, 64)])
 def test_absorb_out(mla, T, H, dv):
     rng = np.random.default_rng(T * 1000 + H + 7)
     o, w = bf16(rng, (T, H, 512)), bf16(rng, (H, 512, dv), 512 ** -0.5)
