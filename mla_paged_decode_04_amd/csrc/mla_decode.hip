@@ -405,41 +405,46 @@ __global__ __launch_bounds__(NTHREADS) void mla_combine_kernel(CombineParams p) 
   const int grow = rg * p.rgs + rr;
   if (rr >= p.rgs || grow >= p.rows) return;
 
+  // Splits are taken four at a time with all their loads issued together (one
+  // memory round trip per four splits), merged with a running max: the sum
+  // is rescaled by 2^(M_old - M_new) whenever a group raises the max.
+  constexpr int CB = 4;
   const float* lse_s = p.part_lse + (size_t)first * p.rgs + rr;
-  float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, lse_s[(size_t)s * p.rgs]);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
   const float* src = p.part_o + ((size_t)first * p.rgs + rr) * DV + d0;
   const size_t sstride = (size_t)p.rgs * DV;
-  int s = 0;
-  for (; s + 2 <= n; s += 2) {   // two splits per step: four 16-byte loads in flight
-    const float l0 = lse_s[(size_t)s * p.rgs], l1 = lse_s[(size_t)(s + 1) * p.rgs];
-    const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(src + s * sstride);
-    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(src + s * sstride + 4);
-    const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(src + (s + 1) * sstride);
-    const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(src + (s + 1) * sstride + 4);
-    const float w0 = l0 == -INFINITY ? 0.f : exp2f(l0 - M);
-    const float w1 = l1 == -INFINITY ? 0.f : exp2f(l1 - M);
-    den += w0 + w1;
+  float M = -INFINITY, den = 0.f;
+  f32x4_t acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  for (int s0 = 0; s0 < n; s0 += CB) {
+    float l[CB];
+    f32x4_t a[CB], c[CB];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] += w0 * a0[e] + w1 * c0[e];
-      acc[4 + e] += w0 * a1[e] + w1 * c1[e];
+    for (int i = 0; i < CB; ++i) {
+      if (s0 + i < n) {
+        l[i] = lse_s[(size_t)(s0 + i) * p.rgs];
+        a[i] = *reinterpret_cast<const f32x4_t*>(src + (s0 + i) * sstride);
+        c[i] = *reinterpret_cast<const f32x4_t*>(src + (s0 + i) * sstride + 4);
+      } else {
+        l[i] = -INFINITY;
+        a[i] = c[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
     }
-  }
-  if (s < n) {
-    const float l0 = lse_s[(size_t)s * p.rgs];
-    const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(src + s * sstride);
-    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(src + s * sstride + 4);
-    const float w0 = l0 == -INFINITY ? 0.f : exp2f(l0 - M);
-    den += w0;
+    float Mc = M;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] += w0 * a0[e];
-      acc[4 + e] += w0 * a1[e];
+    for (int i = 0; i < CB; ++i) Mc = fmaxf(Mc, l[i]);
+    const float sc = M == -INFINITY ? 0.f : exp2f(M - Mc);   // the sum so far is 0 while M = -inf
+    den *= sc;
+    acc0 *= sc;
+    acc1 *= sc;
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const float w = l[i] == -INFINITY ? 0.f : exp2f(l[i] - Mc);
+      den += w;
+      acc0 += w * a[i];
+      acc1 += w * c[i];
     }
+    M = Mc;
   }
+  float acc[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
   const bool empty = !(den > 0.f);
   const float inv = empty ? 0.f : 1.f / den;
   const size_t orow = (size_t)b * p.rows + grow;
