@@ -65,14 +65,28 @@ __host__ __device__ inline RowCfg row_config(int rows) {
 
 __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
+// ceil(a / b) for 0 <= a <= 2^25 and 1 <= b <= 2^25, without an integer
+// divide (the planner's candidate search makes many of these): the float
+// quotient of two exact operands is within one of the true one, and the two
+// corrections make it exact, on the host and on the device alike.
+__host__ __device__ inline int ceil_div_small(int a, int b) {
+  int q = static_cast<int>(static_cast<float>(a) / static_cast<float>(b));
+  if (q * b > a) --q;
+  if ((q + 1) * b <= a) ++q;   // q = floor(a / b)
+  return q * b == a ? q : q + 1;
+}
+
 // Split of one sequence's key range [0, keys) into n chunks of `len` keys
 // (len a multiple of the tile); keys == 0 still yields one (empty) chunk.
+// Computed in 64-key units (chunk is a multiple of 64, keys <= 2^30), where
+// ceil(keys / x) = ceil(ceil(keys / 64) / (x / 64)).
 __host__ __device__ inline void seq_split(int keys, int chunk, int* n, int* len) {
   if (keys <= 0) { *n = 1; *len = 0; return; }
-  int n0 = (keys + chunk - 1) / chunk;
-  int l = round_up((keys + n0 - 1) / n0, NT);
-  *len = l;
-  *n = (keys + l - 1) / l;
+  const int k64 = (keys + NT - 1) / NT;
+  const int n0 = ceil_div_small(k64, chunk / NT);
+  const int l64 = ceil_div_small(k64, n0);
+  *len = l64 * NT;
+  *n = ceil_div_small(k64, l64);
 }
 
 __host__ __device__ inline int chunk_from_work(long long work, int forced, int target) {

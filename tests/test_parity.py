@@ -139,6 +139,10 @@ EDGE = [
     ("sq512_h1", 2, 512, 1, 64, "bf16", (512, 1300)),
     ("sq300_h3_fp8", 3, 300, 3, 128, "fp8", (100, 300, 900)),
     ("sq128_h128_fp8", 1, 128, 128, 64, "fp8", (1000,)),
+    # 128-row items that are only partly filled: 96 rows (three waves of 32)
+    # and 80 rows (two and a half)
+    ("heads_96", 2, 1, 96, 64, "bf16", (500, 1000)),
+    ("sq5_h16_fp8", 2, 5, 16, 128, "fp8", (40, 2000)),
 ]
 
 
