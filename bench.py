@@ -377,7 +377,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(mi.WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--flush", action="store_true",

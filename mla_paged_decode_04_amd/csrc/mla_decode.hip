@@ -233,7 +233,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
   __shared__ long long s_work[PLAN_WAVES], s_keys[PLAN_WAVES];
   __shared__ int s_min[PLAN_WAVES], s_max[PLAN_WAVES];
   __shared__ int s_cnt[CHUNK_CANDIDATES], s_mx[CHUNK_CANDIDATES];
-  __shared__ int s_items[PLAN_WAVES], s_slots[PLAN_WAVES], s_flag[PLAN_WAVES];
+  __shared__ int s_long[PLAN_WAVES], s_tail[PLAN_WAVES], s_slots[PLAN_WAVES], s_flag[PLAN_WAVES];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
 
   int clamped = 0;
@@ -329,32 +329,38 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     chunk = chunk_candidate(cr, step, kb);
   }
 
-  int my_items = 0, my_slots = 0;
+  int my_long = 0, my_tail = 0, my_slots = 0;
   for (int b = b0; b < b1; ++b) {
     int n, len;
     seq_split(s_len[b], chunk, &n, &len);
-    my_items += p.nrg * n;
+    my_long += p.nrg * (n - 1);
+    my_tail += p.nrg;
     if (n > 1) my_slots += p.nrg * n;
   }
-  const int inc_items = wave_inclusive_scan(my_items);
+  const int inc_long = wave_inclusive_scan(my_long);
+  const int inc_tail = wave_inclusive_scan(my_tail);
   const int inc_slots = wave_inclusive_scan(my_slots);
   if (lane == 63) {
-    s_items[wv] = inc_items;
+    s_long[wv] = inc_long;
+    s_tail[wv] = inc_tail;
     s_slots[wv] = inc_slots;
   }
   __syncthreads();
-  int item = inc_items - my_items, slot = inc_slots - my_slots;
-  int tot_items = 0, tot_slots = 0;
+  int litem = inc_long - my_long, titem = inc_tail - my_tail, slot = inc_slots - my_slots;
+  int tot_long = 0, tot_tail = 0, tot_slots = 0;
 #pragma unroll
   for (int i = 0; i < PLAN_WAVES; ++i) {
     if (i < wv) {
-      item += s_items[i];
+      litem += s_long[i];
+      titem += s_tail[i];
       slot += s_slots[i];
     }
-    tot_items += s_items[i];
+    tot_long += s_long[i];
+    tot_tail += s_tail[i];
     tot_slots += s_slots[i];
   }
-
+  titem += tot_long;
+  const int tot_items = tot_long + tot_tail;
   // Cannot happen within the workspace bounds; if it did, no item runs and
   // the header says so (bit 1 of the flag word).
   const bool overflow = tot_items > p.max_items || tot_slots > p.max_slots;
@@ -363,15 +369,18 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     int n, len;
     seq_split(L, chunk, &n, &len);
     if (overflow) n = 1;
-    // pair (b, rg) owns the partial slots slot + rg * n .. + n - 1; items go
-    // chunk-major, so the row groups of one chunk are consecutive (they run
-    // side by side on one XCD and share its L2 for the cache rows)
+    // pair (b, rg) owns the partial slots slot + rg * n .. + n - 1. Items go
+    // longest first: every chunk but a sequence's last (all of full length)
+    // before the last chunks, chunk-major within each class, so the row
+    // groups of one chunk stay consecutive (side by side on one XCD, sharing
+    // its L2 for the cache rows).
     for (int rg = 0; rg < p.nrg; ++rg) {
       p.pairs[2 * (b * p.nrg + rg)] = n > 1 ? slot + rg * n : -1;
       p.pairs[2 * (b * p.nrg + rg) + 1] = n;
     }
     for (int s = 0; s < n; ++s)
       for (int rg = 0; rg < p.nrg; ++rg) {
+        int& item = s < n - 1 ? litem : titem;
         if (item < p.max_items) {
           int4* it = reinterpret_cast<int4*>(p.items + (size_t)item * ITEM_INTS);
           it[0] = make_int4(b, rg, s * len, min(L, (s + 1) * len));
@@ -697,22 +706,27 @@ int32_t mla_plan_host(const int32_t* seq_lens_host, int32_t s_q, const mla_decod
   }
   if (rows_per_item) *rows_per_item = rc.rgs;
   if (chunk_keys) *chunk_keys = chunk;
-  int item = 0, slot = 0;
-  for (int b = 0; b < desc->batch; ++b) {
-    int L = std::min(std::max(seq_lens_host[b], 0), max_keys);
-    int n, len;
-    seq_split(L, chunk, &n, &len);
-    for (int s = 0; s < n; ++s)
-      for (int rg = 0; rg < rc.nrg; ++rg) {
-        if (item >= max_items) return -1;
-        if (items) {
-          int32_t* it = items + (size_t)item * ITEM_INTS;
-          it[0] = b; it[1] = rg; it[2] = s * len; it[3] = std::min(L, (s + 1) * len);
-          it[4] = n > 1 ? slot + rg * n + s : -1; it[5] = 0; it[6] = 0; it[7] = 0;
+  // two passes, as on the device: every chunk but the last of each sequence,
+  // then the last chunks; slots per (b, row group) pair as on the device
+  int item = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    int slot = 0;
+    for (int b = 0; b < desc->batch; ++b) {
+      int L = std::min(std::max(seq_lens_host[b], 0), max_keys);
+      int n, len;
+      seq_split(L, chunk, &n, &len);
+      for (int s = pass == 0 ? 0 : n - 1; s < (pass == 0 ? n - 1 : n); ++s)
+        for (int rg = 0; rg < rc.nrg; ++rg) {
+          if (item >= max_items) return -1;
+          if (items) {
+            int32_t* it = items + (size_t)item * ITEM_INTS;
+            it[0] = b; it[1] = rg; it[2] = s * len; it[3] = std::min(L, (s + 1) * len);
+            it[4] = n > 1 ? slot + rg * n + s : -1; it[5] = 0; it[6] = 0; it[7] = 0;
+          }
+          ++item;
         }
-        ++item;
-      }
-    if (n > 1) slot += rc.nrg * n;
+      if (n > 1) slot += rc.nrg * n;
+    }
   }
   return item;
 }
