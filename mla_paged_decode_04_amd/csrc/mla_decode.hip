@@ -289,7 +289,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     // items and longest item for every candidate chunk (8 threads per
     // candidate, all candidates at once), then the cheapest
     constexpr int TPC = PLAN_THREADS / CHUNK_CANDIDATES;
-    static_assert(TPC == 8, "three xor steps below");
+    static_assert(TPC <= 64 && (TPC & (TPC - 1)) == 0, "the xor steps below stay inside a wave");
     const int step = chunk_step(cr);
     {
       const int k = tid / TPC, sub = tid % TPC;

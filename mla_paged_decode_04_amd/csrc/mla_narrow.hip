@@ -138,16 +138,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
   static_assert(TILE == H16_TILE, "same LDS budget for both caches");
   __shared__ __attribute__((aligned(1024))) char smem[4 * 2 * H16_TILE];   // 147456 bytes
 
-  const int n_items = p.header[0];
+  // The item count and this workgroup's item are read in one memory round
+  // trip: the grid never exceeds the item array's capacity (rounded up to 8
+  // items, within its 256-byte-aligned region), so the item read is in bounds
+  // even for a workgroup that then finds it has no item.
   const int item_id = blockIdx.x;
-  if (item_id >= n_items) return;
   const int32_t* it = p.items + (size_t)item_id * ITEM_INTS;
+  const int n_items = p.header[0];
   // work-item fields are uniform: keep them (and all tile addressing derived
   // from them) in SGPRs, so no vector load ever enters the DMA vmcnt queue
   const int b = __builtin_amdgcn_readfirstlane(it[0]);
   const int t0 = __builtin_amdgcn_readfirstlane(it[2]);
   const int t1 = __builtin_amdgcn_readfirstlane(it[3]);
   const int slot = __builtin_amdgcn_readfirstlane(it[4]);
+  // (the asm pins the loads, and the launch fields the first block-table read
+  // needs, ahead of the branch)
+  asm volatile("" ::"s"(n_items), "s"(b), "s"(t0), "s"(t1), "s"(slot), "s"(p.bs), "s"(p.max_blocks),
+               "s"(p.block_table), "s"(p.seq_lens));
+  if (item_id >= n_items) return;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -155,15 +163,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
   const int g = lane >> 4;
   const int c16 = lane & 15;
 
-  const int L = __builtin_amdgcn_readfirstlane(min(max(p.seq_lens[b], 0), p.max_keys));
+  // The block table and seq_lens are read-only for the whole kernel: reading
+  // them through the constant address space keeps these uniform loads on the
+  // scalar unit, so they never enter the vmcnt queue the DMA waits below count
+  // on. The length is requested here and used only after the first tile was
+  // issued, so its load shares a round trip with the first block-table read.
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const int L_raw = ((const_i32*)p.seq_lens)[b];
   const int row = c16;
   const bool row_ok = row < p.rows;
-  int limit = 0;
-  if (row_ok) {
-    int tok = row / p.heads;
-    int vis = p.causal ? L - p.s_q + 1 + tok : L;
-    limit = min(vis, t1);
-  }
+  int limit = 0;   // keys this row sees, set once the first tile is in flight
 
   bf16x8_t qb[D / 32];   // loaded below, after this wave's first tile was requested
 
@@ -210,11 +219,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
   }
   constexpr int GSTRIDE = F8 ? F8_GSTRIDE : H16_GSTRIDE;
 
-  // The block table is read-only for the whole kernel: reading it through the
-  // constant address space keeps these uniform loads on the scalar unit, so
-  // they never enter the vmcnt queue the DMA waits below count on.
-  typedef const __attribute__((address_space(4))) int32_t const_i32;
   const_i32* bt = (const_i32*)(p.block_table + (size_t)b * p.max_blocks);
+  // the block size is 64 or 128 (checked on the host): page and row offset
+  // are a shift and a mask
+  const int bsh = p.bs == 128 ? 7 : 6;
   char* wbuf = smem + w * 2 * H16_TILE;
   const int ntiles = (t1 - t0 + KT - 1) / KT;
 
@@ -223,9 +231,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
   // are fetched from a valid row of the page and zeroed after arrival.
   auto issue = [&](int j, char* dst) {
     const int ts = t0 + KT * j;
-    int page = bt[ts / p.bs];
+    int page = bt[ts >> bsh];
     if (page < 0 || page >= p.num_blocks) page = 0;
-    const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts % p.bs)) * ROWB;
+    const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts & (p.bs - 1))) * ROWB;
     const uint32_t l0 = lds_addr(dst);
 #pragma unroll
     for (int n = 0; n < NDMA; ++n) {
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
   };
   auto valid_keys = [&](int j) {
     const int ts = t0 + KT * j;
-    int page = bt[ts / p.bs];
+    int page = bt[ts >> bsh];
     if (page < 0 || page >= p.num_blocks) return 0;
     return min(KT, t1 - ts);
   };
@@ -353,6 +361,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
   int j = w, itn = 0;
   const char* cur = nullptr;
   if (w < ntiles) issue(w, wbuf);
+  const int L = min(max(L_raw, 0), p.max_keys);
+  if (row_ok) {
+    const int tok = row / p.heads;
+    const int vis = p.causal ? L - p.s_q + 1 + tok : L;
+    limit = min(vis, t1);
+  }
   // q is loaded while the first tile is in flight. Its loads are consumed
   // here, so the compiler's own vmcnt wait for them (which also covers the
   // older tile transfers) sits before the tile loop, not inside it (it cannot

@@ -132,6 +132,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
 
   typedef const __attribute__((address_space(4))) int32_t const_i32;
   const_i32* bt = (const_i32*)(p.block_table + (size_t)b * p.max_blocks);
+  // the block size is 64 or 128 (checked on the host): page and row offset
+  // are a shift and a mask
+  const int bsh = p.bs == 128 ? 7 : 6;
   const int ntiles = (t1 - t0 + W_NTK - 1) / W_NTK;
   // fp8 tiles are fetched by waves 0 and 1 only (18 transfers per tile)
   const bool dma_wave = !F8 || w < 2;
@@ -140,9 +143,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
   // instructions per participating wave; vmcnt arithmetic relies on it).
   auto issue = [&](int j) {
     const int ts = t0 + W_NTK * j;
-    int page = bt[ts / p.bs];
+    int page = bt[ts >> bsh];
     if (page < 0 || page >= p.num_blocks) page = 0;
-    const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts % p.bs)) * ROWB;
+    const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts & (p.bs - 1))) * ROWB;
     if constexpr (!F8) {
       const uint32_t l0 = lds_addr(smem + (j & 3) * W_TILE);
 #pragma unroll
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
   };
   auto valid_keys = [&](int j) {
     const int ts = t0 + W_NTK * j;
-    int page = bt[ts / p.bs];
+    int page = bt[ts >> bsh];
     if (page < 0 || page >= p.num_blocks) return 0;
     return min(W_NTK, t1 - ts);
   };

@@ -193,6 +193,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
 
   typedef const __attribute__((address_space(4))) int32_t const_i32;
   const_i32* bt = (const_i32*)(p.block_table + (size_t)b * p.max_blocks);
+  // the block size is 64 or 128 (checked on the host): page and row offset
+  // are a shift and a mask
+  const int bsh = p.bs == 128 ? 7 : 6;
   const int nsteps = (t1 - t0 + X_STEP - 1) / X_STEP;
   const int ntiles = (t1 - t0 + KT - 1) / KT;
 
@@ -201,9 +204,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   // page: items start on 64-key boundaries and pages hold 64 or 128 keys.
   auto issue = [&](int j) {
     const int ts = t0 + KT * j;
-    int page = bt[ts / p.bs];
+    int page = bt[ts >> bsh];
     if (page < 0 || page >= p.num_blocks) page = 0;
-    const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts % p.bs)) * ROWB;
+    const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts & (p.bs - 1))) * ROWB;
     const uint32_t l0 = lds_addr(smem + (j & 3) * X_TILE);
     auto one = [&](int i, auto nt_tag) {
       const int n = w * X_NDMA + i;
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   };
   auto valid_keys = [&](int j) {
     const int ts = t0 + KT * j;
-    int page = bt[ts / p.bs];
+    int page = bt[ts >> bsh];
     if (page < 0 || page >= p.num_blocks) return 0;
     return min(KT, t1 - ts);
   };
