@@ -172,7 +172,7 @@ inline long long max_items_bound(int batch, int rows, int max_keys, int forced) 
 }
 
 struct WsLayout {
-  size_t items, pairs, part_lse, part_o, total;
+  size_t items, pairs, part_lse, part_scale, part_o, total;
   long long max_items, max_slots;
 };
 
@@ -191,6 +191,7 @@ inline WsLayout ws_layout(int batch, int s_q, int heads, int max_keys, int force
   w.items = off;   off = align256(off + (size_t)w.max_items * ITEM_INTS * 4);
   w.pairs = off;   off = align256(off + (size_t)batch * rc.nrg * 2 * 4);
   w.part_lse = off; off = align256(off + (size_t)w.max_slots * rc.rgs * 4);
+  w.part_scale = off; off = align256(off + (size_t)w.max_slots * rc.rgs * 4);
   w.part_o = off;  off = align256(off + (size_t)w.max_slots * rc.rgs * DV * 4);
   w.total = off;
   return w;
@@ -406,6 +407,7 @@ struct CombineParams {
   const int32_t* pairs;
   const float* part_o;
   const float* part_lse;
+  const int32_t* part_scale;
   uint16_t* out;
   float* lse;
   int rows, rgs, nrg, n_pairs;
@@ -413,9 +415,12 @@ struct CombineParams {
 
 // Grid (pair, chunk): thread (row, 8-dim slice) of one (sequence, row group)
 // pair; only pairs that were split do work. Merge of the pair's n partials:
-// lse = log2(sum_s 2^lse_s), out = sum_s 2^(lse_s - lse) o_s.
+// lse = log2(sum_s 2^lse_s), out = sum_s 2^(lse_s - lse) o_s. F16: the
+// partial rows are fp16 values of o_s * 2^k_s with a per-row exponent k_s
+// (the 128-row items' format), else fp32 o_s.
 constexpr int COMBINE_SLICES = DV / 8;   // 64 threads per row
 
+template <bool F16>
 __global__ __launch_bounds__(NTHREADS) void mla_combine_kernel(CombineParams p) {
   const int pair = blockIdx.x;
   const int first = p.pairs[2 * pair];
@@ -433,21 +438,33 @@ __global__ __launch_bounds__(NTHREADS) void mla_combine_kernel(CombineParams p) 
   // is rescaled by 2^(M_old - M_new) whenever a group raises the max.
   constexpr int CB = 4;
   const float* lse_s = p.part_lse + (size_t)first * p.rgs + rr;
-  const float* src = p.part_o + ((size_t)first * p.rgs + rr) * DV + d0;
+  const int32_t* k_s = p.part_scale + (size_t)first * p.rgs + rr;
+  const size_t elem = ((size_t)first * p.rgs + rr) * DV + d0;   // element offset of split 0
   const size_t sstride = (size_t)p.rgs * DV;
   float M = -INFINITY, den = 0.f;
   f32x4_t acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
   for (int s0 = 0; s0 < n; s0 += CB) {
     float l[CB];
+    int ks[CB];
     f32x4_t a[CB], c[CB];
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       if (s0 + i < n) {
         l[i] = lse_s[(size_t)(s0 + i) * p.rgs];
-        a[i] = *reinterpret_cast<const f32x4_t*>(src + (s0 + i) * sstride);
-        c[i] = *reinterpret_cast<const f32x4_t*>(src + (s0 + i) * sstride + 4);
+        if constexpr (F16) {
+          ks[i] = k_s[(size_t)(s0 + i) * p.rgs];
+          const f16x8_t h = *reinterpret_cast<const f16x8_t*>(
+              reinterpret_cast<const _Float16*>(p.part_o) + elem + (s0 + i) * sstride);
+          a[i] = f32x4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+          c[i] = f32x4_t{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+        } else {
+          ks[i] = 0;
+          a[i] = *reinterpret_cast<const f32x4_t*>(p.part_o + elem + (s0 + i) * sstride);
+          c[i] = *reinterpret_cast<const f32x4_t*>(p.part_o + elem + (s0 + i) * sstride + 4);
+        }
       } else {
         l[i] = -INFINITY;
+        ks[i] = 0;
         a[i] = c[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
@@ -462,8 +479,9 @@ __global__ __launch_bounds__(NTHREADS) void mla_combine_kernel(CombineParams p) 
     for (int i = 0; i < CB; ++i) {
       const float w = l[i] == -INFINITY ? 0.f : exp2f(l[i] - Mc);
       den += w;
-      acc0 += w * a[i];
-      acc1 += w * c[i];
+      const float wo = F16 ? ldexpf(w, -ks[i]) : w;   // undo the row's 2^k
+      acc0 += wo * a[i];
+      acc1 += wo * c[i];
     }
     M = Mc;
   }
@@ -598,6 +616,7 @@ mla_status_t launch_decode_kernel(const void* q, const void* kv_cache,
   fp.items = reinterpret_cast<const int32_t*>(base + ws.items);
   fp.part_o = reinterpret_cast<float*>(base + ws.part_o);
   fp.part_lse = reinterpret_cast<float*>(base + ws.part_lse);
+  fp.part_scale = reinterpret_cast<int32_t*>(base + ws.part_scale);
   fp.heads = desc->num_heads;
   fp.s_q = s_q;
   fp.rows = rows;
@@ -618,6 +637,7 @@ mla_status_t launch_decode_kernel(const void* q, const void* kv_cache,
   cp.pairs = reinterpret_cast<const int32_t*>(base + ws.pairs);
   cp.part_o = fp.part_o;
   cp.part_lse = fp.part_lse;
+  cp.part_scale = fp.part_scale;
   cp.out = fp.out;
   cp.lse = lse;
   cp.rows = rows;
@@ -625,7 +645,10 @@ mla_status_t launch_decode_kernel(const void* q, const void* kv_cache,
   cp.nrg = rc.nrg;
   cp.n_pairs = desc->batch * rc.nrg;
   const unsigned chunks = (unsigned)((rc.rgs * COMBINE_SLICES + NTHREADS - 1) / NTHREADS);
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(cp.n_pairs, chunks), dim3(NTHREADS), 0, hs, cp);
+  if (rc.kind == 2)
+    hipLaunchKernelGGL(mla_combine_kernel<true>, dim3(cp.n_pairs, chunks), dim3(NTHREADS), 0, hs, cp);
+  else
+    hipLaunchKernelGGL(mla_combine_kernel<false>, dim3(cp.n_pairs, chunks), dim3(NTHREADS), 0, hs, cp);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

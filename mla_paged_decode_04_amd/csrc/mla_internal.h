@@ -30,6 +30,8 @@ constexpr float BIG_SLACK = 64.0f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
@@ -135,8 +137,9 @@ struct FwdParams {
   float* lse;
   const int32_t* header;
   const int32_t* items;
-  float* part_o;
+  float* part_o;      // split partials: fp32, or for 128-row items fp16 scaled by 2^part_scale
   float* part_lse;
+  int32_t* part_scale;
   int heads, s_q, rows, bs, max_blocks, max_keys, causal, num_blocks;
   float scale_log2;   // softmax_scale * kv_scale * log2(e)
   float out_scale;    // kv_scale

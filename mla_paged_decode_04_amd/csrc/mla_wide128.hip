@@ -464,17 +464,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   // ---- write this wave's rows: final (slot < 0) or split partial ----
   // The rows leave through LDS (the ring is free once every wave is past its
   // last step): a wave stages its 32 rows x 256 dims at a time, then writes
-  // whole row segments, so each store instruction covers 1 KB (fp32) or 512 B
-  // (bf16) of one row instead of scattered 16-byte pieces.
+  // whole row segments, so each store instruction covers 512 B of one row
+  // (bf16 out or fp16 partial) instead of scattered 16-byte pieces.
   const float l_row = halves_sum(l_run);
   const bool empty = !(l_row > 0.f);
   const float inv = empty ? 0.f : p.out_scale / l_row;
   const float lse2 = empty ? -INFINITY : m_run + log2f(l_row);
+  // A split partial row leaves as fp16 values of o * 2^k, with k chosen per
+  // row so that its largest magnitude lands in [2^14, 2^15): every element
+  // keeps 11 bits relative to the row maximum, nothing overflows, and the
+  // partial traffic (written here, read back by the combine) is half that of
+  // fp32. k is capped so that the folded factor inv * 2^k stays finite,
+  // which only matters for rows whose values are all far below 2^-100.
+  int kexp = 0;
+  if (slot >= 0) {
+    float amax = 0.f;
+#pragma unroll
+    for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[db][e]));
+    amax = halves_max(amax) * inv;   // this row's largest |o| after normalisation
+    if (amax > 0.f && amax < INFINITY)
+      kexp = min(15 - __builtin_amdgcn_frexp_expf(amax), 127 - __builtin_amdgcn_frexp_expf(inv));
+  }
+  const float fs = __builtin_ldexpf(inv, kexp);   // normalisation and 2^k in one factor
   if (row_ok && hi == 0) {
     if (slot < 0) {
       if (p.lse != nullptr) p.lse[(size_t)b * p.rows + row] = lse2 * LN2;
     } else {
       p.part_lse[(size_t)slot * X_RGS + row_local] = lse2;
+      p.part_scale[(size_t)slot * X_RGS + row_local] = kexp;
     }
   }
   __syncthreads();   // every wave is done with the ring
@@ -490,7 +509,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
       for (int q = 0; q < 4; ++q) {
         const f32x16_t& a = o[(DV / 64) * hf + db];
         *reinterpret_cast<f32x4_t*>(stage + n32 * SROW + 32 * db + 8 * q + 4 * hi) =
-            f32x4_t{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]} * inv;
+            f32x4_t{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]} * fs;
       }
     // a wave's LDS accesses complete in order: the reads below see the writes
     for (int r = 0; r < nrow; ++r) {
@@ -500,8 +519,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
         uint16_t* dst = p.out + ((size_t)b * p.rows + rg * X_RGS + rl) * DV + (DV / 2) * hf + 4 * lane;
         *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       } else {
-        float* dst = p.part_o + ((size_t)slot * X_RGS + rl) * DV + (DV / 2) * hf + 4 * lane;
-        *reinterpret_cast<f32x4_t*>(dst) = v;
+        _Float16* dst = reinterpret_cast<_Float16*>(p.part_o) + ((size_t)slot * X_RGS + rl) * DV + (DV / 2) * hf +
+                        4 * lane;
+        *reinterpret_cast<f16x4_t*>(dst) = __builtin_convertvector(v, f16x4_t);
       }
     }
   }

@@ -202,6 +202,33 @@ def test_score_jumps_rescale(mla, case, split):
     assert_parity(o, l, ro, rl, dtype, f"{tag} split={split}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("shift", [40, -40])
+def test_split_partials_at_extreme_magnitudes(mla, dtype, shift):
+    """128-row items keep split partials as fp16 with a per-row power-of-two
+    scale. Values scaled by 2^40 (past fp16's range) or 2^-40 (below its
+    normal range) must come through at the usual tolerance: kv_scale times
+    2^shift and softmax_scale times 2^-shift leave every score unchanged and
+    scale the exact output by 2^shift."""
+    wl = mi.Workload(f"mag{shift}_{dtype}", 2, 1, 128, 64, dtype, "fixed", (700, 1500), seed=23)
+    inp = mi.make_inputs(wl)
+    q, kv, bt, sl = to_device(inp)
+    kv_scale = float(inp.kv_scale) * 2.0 ** shift
+    sm = wl.softmax_scale * 2.0 ** -shift
+    out = torch.full((wl.batch, 1, 128, 512), float("nan"), dtype=torch.bfloat16, device=q.device)
+    lse = torch.full((wl.batch, 1, 128), float("nan"), dtype=torch.float32, device=q.device)
+    mla.mla_decode(q, kv, bt, sl, sm, kv_scale, out=out, lse=lse, split_keys=128)
+    torch.cuda.synchronize()
+    o, l = out.float().cpu().double().numpy(), lse.cpu().double().numpy()
+    ro, rl = orc.mla_decode(inp.q_bits, inp.kv, inp.block_table, inp.seq_lens, 1, sm, kv_scale, dtype,
+                            True)
+    assert np.abs(ro).max() > 2.0 ** (shift - 8) and np.abs(ro).max() < 2.0 ** (shift + 8)
+    # the kernel-test metric has an absolute floor in its denominator: compare
+    # at unit scale (exact: a power of two), the relative error is unaffected
+    unit = 2.0 ** -shift
+    assert_parity(o * unit, l, ro * unit, rl, dtype, f"magnitude 2^{shift} {dtype}")
+
+
 def test_page_permutation_is_bit_identical_on_gpu(mla):
     wl = mi.shrink(mi.WORKLOADS["b64_h128_L1k2k_bs128_bf16"], 6)
     inp = mi.make_inputs(wl)
@@ -248,3 +275,24 @@ def test_device_plan_matches_host_mirror(mla, lens, s_q, H, bs, maxb, split):
     host, rows, chunk = mla.mla_plan_host(lens, s_q, H, bs, maxb, split_keys=split)
     assert int(header[0]) == len(host) and int(header[1]) == chunk and int(header[3]) == 0
     np.testing.assert_array_equal(items.cpu().numpy(), host)
+
+
+def test_device_plan_matches_host_mirror_random_batches(mla):
+    # the device planner divides with a reciprocal estimate, the host with a
+    # float division; both correct to the exact quotient, so the plans agree
+    # on every batch, including very long sequences and the 1M-key range
+    rng = np.random.default_rng(7)
+    for case in range(24):
+        B = int(rng.integers(1, 400))
+        H = int(rng.choice([1, 16, 64, 128]))
+        s_q = int(rng.integers(1, 4))
+        bs = int(rng.choice([64, 128]))
+        maxb = int(rng.choice([4, 64, 1024, 8192]))
+        lens = rng.integers(0, maxb * bs + 1, size=B)
+        if case % 3 == 0:
+            lens[: B // 2] = rng.integers(0, 65, size=B // 2)   # a mix of tiny and long
+        sl = torch.tensor(lens, dtype=torch.int32, device="cuda:0")
+        header, items = mla.mla_decode_plan(sl, s_q, H, bs, maxb)
+        host, _, chunk = mla.mla_plan_host(lens, s_q, H, bs, maxb)
+        assert int(header[0]) == len(host) and int(header[1]) == chunk, (case, B, H, s_q, bs, maxb)
+        np.testing.assert_array_equal(items.cpu().numpy(), host)
