@@ -110,8 +110,8 @@ mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* bloc
  * kernel on its own: `workspace` must already hold the plan of a preceding
  * mla_decode or mla_decode_plan call with the same seq_lens and description.
  * Rows of work items that were split get their partials in the workspace
- * instead of out/lse (fp32, or for more than 64 rows per sequence fp16 rows
- * scaled by a per-row power of two). Same arguments, checks and errors as mla_decode. */
+ * instead of out/lse (fp16 rows scaled by a per-row power of two, with a
+ * base-2 lse per row). Same arguments, checks and errors as mla_decode. */
 mla_status_t mla_decode_fwd_only(const void* q, const void* kv_cache, const int32_t* block_table,
                                  const int32_t* seq_lens, int32_t s_q, float softmax_scale,
                                  float kv_scale, void* out, float* lse,

@@ -192,7 +192,7 @@ inline WsLayout ws_layout(int batch, int s_q, int heads, int max_keys, int force
   w.pairs = off;   off = align256(off + (size_t)batch * rc.nrg * 2 * 4);
   w.part_lse = off; off = align256(off + (size_t)w.max_slots * rc.rgs * 4);
   w.part_scale = off; off = align256(off + (size_t)w.max_slots * rc.rgs * 4);
-  w.part_o = off;  off = align256(off + (size_t)w.max_slots * rc.rgs * DV * 4);
+  w.part_o = off;  off = align256(off + (size_t)w.max_slots * rc.rgs * DV * 2);   // fp16
   w.total = off;
   return w;
 }
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
 
 struct CombineParams {
   const int32_t* pairs;
-  const float* part_o;
+  const _Float16* part_o;
   const float* part_lse;
   const int32_t* part_scale;
   uint16_t* out;
@@ -415,12 +415,10 @@ struct CombineParams {
 
 // Grid (pair, chunk): thread (row, 8-dim slice) of one (sequence, row group)
 // pair; only pairs that were split do work. Merge of the pair's n partials:
-// lse = log2(sum_s 2^lse_s), out = sum_s 2^(lse_s - lse) o_s. F16: the
-// partial rows are fp16 values of o_s * 2^k_s with a per-row exponent k_s
-// (the 128-row items' format), else fp32 o_s.
+// lse = log2(sum_s 2^lse_s), out = sum_s 2^(lse_s - lse) o_s, where the
+// partial rows hold fp16 values of o_s * 2^k_s with a per-row exponent k_s.
 constexpr int COMBINE_SLICES = DV / 8;   // 64 threads per row
 
-template <bool F16>
 __global__ __launch_bounds__(NTHREADS) void mla_combine_kernel(CombineParams p) {
   const int pair = blockIdx.x;
   const int first = p.pairs[2 * pair];
@@ -451,17 +449,10 @@ __global__ __launch_bounds__(NTHREADS) void mla_combine_kernel(CombineParams p) 
     for (int i = 0; i < CB; ++i) {
       if (s0 + i < n) {
         l[i] = lse_s[(size_t)(s0 + i) * p.rgs];
-        if constexpr (F16) {
-          ks[i] = k_s[(size_t)(s0 + i) * p.rgs];
-          const f16x8_t h = *reinterpret_cast<const f16x8_t*>(
-              reinterpret_cast<const _Float16*>(p.part_o) + elem + (s0 + i) * sstride);
-          a[i] = f32x4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-          c[i] = f32x4_t{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
-        } else {
-          ks[i] = 0;
-          a[i] = *reinterpret_cast<const f32x4_t*>(p.part_o + elem + (s0 + i) * sstride);
-          c[i] = *reinterpret_cast<const f32x4_t*>(p.part_o + elem + (s0 + i) * sstride + 4);
-        }
+        ks[i] = k_s[(size_t)(s0 + i) * p.rgs];
+        const f16x8_t h = *reinterpret_cast<const f16x8_t*>(p.part_o + elem + (s0 + i) * sstride);
+        a[i] = f32x4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+        c[i] = f32x4_t{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
       } else {
         l[i] = -INFINITY;
         ks[i] = 0;
@@ -479,7 +470,7 @@ __global__ __launch_bounds__(NTHREADS) void mla_combine_kernel(CombineParams p) 
     for (int i = 0; i < CB; ++i) {
       const float w = l[i] == -INFINITY ? 0.f : exp2f(l[i] - Mc);
       den += w;
-      const float wo = F16 ? ldexpf(w, -ks[i]) : w;   // undo the row's 2^k
+      const float wo = __builtin_ldexpf(w, -ks[i]);   // undo the row's 2^k
       acc0 += wo * a[i];
       acc1 += wo * c[i];
     }
@@ -614,7 +605,7 @@ mla_status_t launch_decode_kernel(const void* q, const void* kv_cache,
   fp.lse = lse;
   fp.header = reinterpret_cast<const int32_t*>(base);
   fp.items = reinterpret_cast<const int32_t*>(base + ws.items);
-  fp.part_o = reinterpret_cast<float*>(base + ws.part_o);
+  fp.part_o = reinterpret_cast<_Float16*>(base + ws.part_o);
   fp.part_lse = reinterpret_cast<float*>(base + ws.part_lse);
   fp.part_scale = reinterpret_cast<int32_t*>(base + ws.part_scale);
   fp.heads = desc->num_heads;
@@ -645,10 +636,7 @@ mla_status_t launch_decode_kernel(const void* q, const void* kv_cache,
   cp.nrg = rc.nrg;
   cp.n_pairs = desc->batch * rc.nrg;
   const unsigned chunks = (unsigned)((rc.rgs * COMBINE_SLICES + NTHREADS - 1) / NTHREADS);
-  if (rc.kind == 2)
-    hipLaunchKernelGGL(mla_combine_kernel<true>, dim3(cp.n_pairs, chunks), dim3(NTHREADS), 0, hs, cp);
-  else
-    hipLaunchKernelGGL(mla_combine_kernel<false>, dim3(cp.n_pairs, chunks), dim3(NTHREADS), 0, hs, cp);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(cp.n_pairs, chunks), dim3(NTHREADS), 0, hs, cp);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -128,6 +128,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Split partials leave as fp16 values of o * 2^k, with a per-row k that puts
+// the row's largest |o| in [2^14, 2^15): every element keeps 11 bits relative
+// to the row maximum, nothing overflows, and the partial traffic (written by
+// the decode kernels, read back by the combine) is half that of fp32.
+__device__ __forceinline__ int partial_exponent(float amax) {
+  return amax > 0.f && amax < INFINITY ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
+}
+
 struct FwdParams {
   const uint16_t* q;
   const uint8_t* kv;
@@ -137,9 +145,9 @@ struct FwdParams {
   float* lse;
   const int32_t* header;
   const int32_t* items;
-  float* part_o;      // split partials: fp32, or for 128-row items fp16 scaled by 2^part_scale
-  float* part_lse;
-  int32_t* part_scale;
+  _Float16* part_o;   // split partials: fp16 rows of o * 2^part_scale
+  float* part_lse;     // base-2 lse per partial row
+  int32_t* part_scale; // per partial row
   int heads, s_q, rows, bs, max_blocks, max_keys, causal, num_blocks;
   float scale_log2;   // softmax_scale * kv_scale * log2(e)
   float out_scale;    // kv_scale

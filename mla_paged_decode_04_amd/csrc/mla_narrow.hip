@@ -16,7 +16,7 @@ namespace {
 // m (base 2), its share of the running sum, and unnormalised O^T. The KS
 // waves that share a row tile are merged through LDS (weights 2^(m_k - M)),
 // then the rows are written as final bf16 out + natural-log lse (slot < 0), or
-// as an fp32 split partial (normalised o and base-2 lse). Every wave must be
+// as a split partial (fp16 normalised o * 2^k and base-2 lse). Every wave must be
 // done with `smem` before the call.
 template <int KS>
 __device__ __forceinline__ void merge_and_store(const FwdParams& p, char* smem,
@@ -85,10 +85,27 @@ __device__ __forceinline__ void merge_and_store(const FwdParams& p, char* smem,
           make_uint2(pack_bf16x2(acc[i][0], acc[i][1]), pack_bf16x2(acc[i][2], acc[i][3]));
     if (p.lse != nullptr && c4 == 0) p.lse[orow] = lse2 * LN2;
   } else {
-    float* dst = p.part_o + ((size_t)slot * RGS + rr) * DV + c4;
+    // fp16 o * 2^k (partial_exponent); the row's 512 dims are spread over 16
+    // consecutive lanes
+    float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < DV / 64; ++i) *reinterpret_cast<f32x4_t*>(dst + 64 * i) = acc[i];
-    if (c4 == 0) p.part_lse[(size_t)slot * RGS + rr] = lse2;
+    for (int i = 0; i < DV / 64; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(acc[i][e]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const int kexp = partial_exponent(amax);
+    _Float16* dst = p.part_o + ((size_t)slot * RGS + rr) * DV + c4;
+#pragma unroll
+    for (int i = 0; i < DV / 64; ++i) {
+      const f32x4_t sv = f32x4_t{__builtin_ldexpf(acc[i][0], kexp), __builtin_ldexpf(acc[i][1], kexp),
+                                 __builtin_ldexpf(acc[i][2], kexp), __builtin_ldexpf(acc[i][3], kexp)};
+      *reinterpret_cast<f16x4_t*>(dst + 64 * i) = __builtin_convertvector(sv, f16x4_t);
+    }
+    if (c4 == 0) {
+      p.part_lse[(size_t)slot * RGS + rr] = lse2;
+      p.part_scale[(size_t)slot * RGS + rr] = kexp;
+    }
   }
 }
 

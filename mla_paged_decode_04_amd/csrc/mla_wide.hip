@@ -339,6 +339,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
 
   // ---- write this wave's rows: final (slot < 0) or split partial ----
   const float l_row = wave_sum_across_groups(l_run);
+  int kexp = 0;   // split partials: fp16 o * 2^k (partial_exponent)
+  if (slot >= 0) {
+    float amax = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(o[dt][e]));
+    const bool empty = !(l_row > 0.f);
+    kexp = partial_exponent(wave_max_across_groups(amax) * (empty ? 0.f : p.out_scale / l_row));
+  }
   if (row_ok) {
     const bool empty = !(l_row > 0.f);
     const float inv = empty ? 0.f : p.out_scale / l_row;
@@ -354,11 +364,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
       }
       if (p.lse != nullptr && g == 0) p.lse[orow] = lse2 * LN2;
     } else {
-      float* dst = p.part_o + ((size_t)slot * RGS + row_local) * DV + 4 * g;
+      _Float16* dst = p.part_o + ((size_t)slot * RGS + row_local) * DV + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt)
-        *reinterpret_cast<f32x4_t*>(dst + 16 * dt) = o[dt] * inv;
-      if (g == 0) p.part_lse[(size_t)slot * RGS + row_local] = lse2;
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        const f32x4_t v = o[dt] * inv;
+        const f32x4_t sv = f32x4_t{__builtin_ldexpf(v[0], kexp), __builtin_ldexpf(v[1], kexp),
+                                   __builtin_ldexpf(v[2], kexp), __builtin_ldexpf(v[3], kexp)};
+        *reinterpret_cast<f16x4_t*>(dst + 16 * dt) = __builtin_convertvector(sv, f16x4_t);
+      }
+      if (g == 0) {
+        p.part_lse[(size_t)slot * RGS + row_local] = lse2;
+        p.part_scale[(size_t)slot * RGS + row_local] = kexp;
+      }
     }
   }
 }

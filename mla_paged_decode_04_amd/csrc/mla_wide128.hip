@@ -470,12 +470,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   const bool empty = !(l_row > 0.f);
   const float inv = empty ? 0.f : p.out_scale / l_row;
   const float lse2 = empty ? -INFINITY : m_run + log2f(l_row);
-  // A split partial row leaves as fp16 values of o * 2^k, with k chosen per
-  // row so that its largest magnitude lands in [2^14, 2^15): every element
-  // keeps 11 bits relative to the row maximum, nothing overflows, and the
-  // partial traffic (written here, read back by the combine) is half that of
-  // fp32. k is capped so that the folded factor inv * 2^k stays finite,
-  // which only matters for rows whose values are all far below 2^-100.
+  // A split partial row leaves as fp16 o * 2^k (partial_exponent). Here 2^k
+  // is folded into the normalisation factor, with k capped so that inv * 2^k
+  // stays finite (which only matters for rows whose values are all far below
+  // 2^-100).
   int kexp = 0;
   if (slot >= 0) {
     float amax = 0.f;
@@ -484,8 +482,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[db][e]));
     amax = halves_max(amax) * inv;   // this row's largest |o| after normalisation
-    if (amax > 0.f && amax < INFINITY)
-      kexp = min(15 - __builtin_amdgcn_frexp_expf(amax), 127 - __builtin_amdgcn_frexp_expf(inv));
+    kexp = min(partial_exponent(amax), 127 - __builtin_amdgcn_frexp_expf(inv));
   }
   const float fs = __builtin_ldexpf(inv, kexp);   // normalisation and 2^k in one factor
   if (row_ok && hi == 0) {
@@ -519,8 +516,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
         uint16_t* dst = p.out + ((size_t)b * p.rows + rg * X_RGS + rl) * DV + (DV / 2) * hf + 4 * lane;
         *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       } else {
-        _Float16* dst = reinterpret_cast<_Float16*>(p.part_o) + ((size_t)slot * X_RGS + rl) * DV + (DV / 2) * hf +
-                        4 * lane;
+        _Float16* dst = p.part_o + ((size_t)slot * X_RGS + rl) * DV + (DV / 2) * hf + 4 * lane;
         *reinterpret_cast<f16x4_t*>(dst) = __builtin_convertvector(v, f16x4_t);
       }
     }
