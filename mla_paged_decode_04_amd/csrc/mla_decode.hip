@@ -106,8 +106,11 @@ __host__ __device__ inline int chunk_from_work(long long work, int forced, int t
 // tile latency, partial write); with n items of at most mx keys and wk keys
 // in all,
 //   n <= SLOTS : mx + o
-//   otherwise  : max(mx + o, ceil((wk + n * o) / SLOTS) + (mx + o) / 2).
-// Ties go to the longer chunk (fewer partials). With many pairs the split
+//   otherwise  : max(mx + o, ceil((wk + n * o) / SLOTS) + (mx + o) / 4).
+// The last term is the tail of the schedule: items are issued roughly longest
+// first, so the last workers to finish overrun the average by a fraction of
+// one item; a simulated list schedule of the skewed 128-head batches gives
+// about a fifth of an item. Ties go to the longer chunk (fewer partials). With many pairs the split
 // from the average (work / SLOTS) is kept. All integer, so the host mirror
 // reproduces the device plan exactly. (A batch of equal lengths keeps the
 // average split: every item then has the same length.)
@@ -147,7 +150,7 @@ __host__ __device__ inline int chunk_candidate(const ChunkRange& r, int step, in
 __host__ __device__ inline unsigned long long plan_cost(unsigned long long n, unsigned long long mx,
                                                         unsigned long long wk, unsigned long long o) {
   if (n <= SLOTS) return mx + o;
-  const unsigned long long avg = ((wk + n * o + SLOTS - 1) >> 8) + ((mx + o) >> 1);
+  const unsigned long long avg = ((wk + n * o + SLOTS - 1) >> 8) + ((mx + o) >> 2);
   static_assert(SLOTS == 256, "the shift above divides by SLOTS");
   return avg > mx + o ? avg : mx + o;
 }
