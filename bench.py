@@ -34,12 +34,13 @@ METRIC = "paged MLA decode: HBM GB/s + TFLOP/s (fraction of roofline), seqs/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2516.6    # dense bf16 MFMA
 CSRC = os.path.join(ROOT, "mla_paged_decode_04_amd", "csrc")
-# the sources each decode kernel is compiled from (a counter summary is only
-# used while these are unchanged)
+# Sources whose digest a counter summary must match to be used: the kernel
+# itself and the host file with the split planner, whose items decide how
+# many partials the kernel writes.
 KERNEL_SOURCES = {
-    "mla_decode_narrow": ("mla_internal.h", "mla_narrow.hip"),
-    "mla_decode_wide": ("mla_internal.h", "mla_wide.hip"),
-    "mla_decode_wide128": ("mla_internal.h", "mla_wide128.hip"),
+    "mla_decode_narrow": ("mla_internal.h", "mla_narrow.hip", "mla_decode.hip"),
+    "mla_decode_wide": ("mla_internal.h", "mla_wide.hip", "mla_decode.hip"),
+    "mla_decode_wide128": ("mla_internal.h", "mla_wide128.hip", "mla_decode.hip"),
 }
 
 
