@@ -270,6 +270,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
     if (t < QREG) return qb[t];
     return *reinterpret_cast<const bf16x8_t*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4));
   };
+  // The slow loop reads the register part of q from memory at every use, so
+  // the q registers die at the fast loop's exit instead of being saved to
+  // scratch there for a loop that rarely runs.
+  const uint16_t* qrow_g = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
+  auto q_operand_mem = [&](int t) -> bf16x8_t {
+    if (t < QREG) {
+      const int d = F8 ? 32 * (t >> 1) + 16 * hi + 8 * (t & 1) : 16 * t + 8 * hi;
+      const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow_g + d) : make_uint4(0, 0, 0, 0);
+      return __builtin_bit_cast(bf16x8_t, v);
+    }
+    return q_operand(t);
+  };
 
   f32x16_t o[DV / 32];
 #pragma unroll
@@ -333,10 +345,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
       for (int t = 0; t < D / 16; ++t) {
         const bf16x8_t a = kr[t % QK_AHEAD];
         if (t + QK_AHEAD < D / 16) kr[t % QK_AHEAD] = lds_b128(kaddr(t + QK_AHEAD));
+        const bf16x8_t qv = SLOW ? q_operand_mem(t) : q_operand(t);
         if (t == 0)
-          qk_first(sacc, a, q_operand(0));
+          qk_first(sacc, a, qv);
         else
-          qk_next(sacc, a, q_operand(t));
+          qk_next(sacc, a, qv);
       }
     } else {
       auto kaddr = [&](int u) { return (kbase ^ ((u & 1) << 5)) + (u >> 1) * X_GSTRIDE + 2048 * half; };
@@ -350,11 +363,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
         if (u + AH < D / 32) kr[u % AH] = lds_u128(kaddr(u + AH));
         const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(v[0], v[1]));
         const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(v[2], v[3]));
+        const bf16x8_t qv0 = SLOW ? q_operand_mem(2 * u) : q_operand(2 * u);
+        const bf16x8_t qv1 = SLOW ? q_operand_mem(2 * u + 1) : q_operand(2 * u + 1);
         if (u == 0)
-          qk_first_v(sacc, a0, q_operand(0));
+          qk_first_v(sacc, a0, qv0);
         else
-          qk_next_v(sacc, a0, q_operand(2 * u));
-        qk_next_v(sacc, a1, q_operand(2 * u + 1));
+          qk_next_v(sacc, a0, qv0);
+        qk_next_v(sacc, a1, qv1);
       }
     }
     qk_done(sacc);
