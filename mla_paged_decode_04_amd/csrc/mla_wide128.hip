@@ -481,6 +481,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   // last step): a wave stages its 32 rows x 256 dims at a time, then writes
   // whole row segments, so each store instruction covers 512 B of one row
   // (bf16 out or fp16 partial) instead of scattered 16-byte pieces.
+  // Lane-derived values are derived afresh here, from the lane id, rather
+  // than kept from the prologue: kept, they stay live across the tile loop
+  // and come back as scratch reloads, each a memory round trip.
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int n32_e = lane_e & 31, hi_e = lane_e >> 5;
+  const int row_local_e = 32 * w + n32_e;
+  const int row_e = rg * X_RGS + row_local_e;
+  const bool row_ok_e = row_e < p.rows;
   const float l_row = halves_sum(l_run);
   const bool empty = !(l_row > 0.f);
   const float inv = empty ? 0.f : p.out_scale / l_row;
@@ -500,12 +508,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
     kexp = min(partial_exponent(amax), 127 - __builtin_amdgcn_frexp_expf(inv));
   }
   const float fs = __builtin_ldexpf(inv, kexp);   // normalisation and 2^k in one factor
-  if (row_ok && hi == 0) {
+  if (row_ok_e && hi_e == 0) {
     if (slot < 0) {
-      if (p.lse != nullptr) p.lse[(size_t)b * p.rows + row] = lse2 * LN2;
+      if (p.lse != nullptr) p.lse[(size_t)b * p.rows + row_e] = lse2 * LN2;
     } else {
-      p.part_lse[(size_t)slot * X_RGS + row_local] = lse2;
-      p.part_scale[(size_t)slot * X_RGS + row_local] = kexp;
+      p.part_lse[(size_t)slot * X_RGS + row_local_e] = lse2;
+      p.part_scale[(size_t)slot * X_RGS + row_local_e] = kexp;
     }
   }
   __syncthreads();   // every wave is done with the ring
@@ -520,18 +528,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x16_t& a = o[(DV / 64) * hf + db];
-        *reinterpret_cast<f32x4_t*>(stage + n32 * SROW + 32 * db + 8 * q + 4 * hi) =
+        *reinterpret_cast<f32x4_t*>(stage + n32_e * SROW + 32 * db + 8 * q + 4 * hi_e) =
             f32x4_t{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]} * fs;
       }
     // a wave's LDS accesses complete in order: the reads below see the writes
     for (int r = 0; r < nrow; ++r) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + r * SROW + 4 * lane);
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + r * SROW + 4 * lane_e);
       const int rl = 32 * w + r;
       if (slot < 0) {
-        uint16_t* dst = p.out + ((size_t)b * p.rows + rg * X_RGS + rl) * DV + (DV / 2) * hf + 4 * lane;
+        uint16_t* dst = p.out + ((size_t)b * p.rows + rg * X_RGS + rl) * DV + (DV / 2) * hf + 4 * lane_e;
         *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       } else {
-        _Float16* dst = p.part_o + ((size_t)slot * X_RGS + rl) * DV + (DV / 2) * hf + 4 * lane;
+        _Float16* dst = p.part_o + ((size_t)slot * X_RGS + rl) * DV + (DV / 2) * hf + 4 * lane_e;
         *reinterpret_cast<f16x4_t*>(dst) = __builtin_convertvector(v, f16x4_t);
       }
     }
