@@ -242,3 +242,32 @@ def test_absorb_zero_tokens_is_a_no_op():
     lib = mla.library()
     assert lib.mla_absorb_q(None, None, None, None, 0, 16, 128, None) == 0
     assert lib.mla_absorb_out(None, None, None, 0, 16, 128, None) == 0
+
+
+def list_schedule_makespan(items, overhead, workers=256):
+    """Makespan, in key units, of the items run in plan order on `workers`
+    single-workgroup CUs, each item costing its keys plus `overhead`."""
+    import heapq
+    free = [0] * workers
+    for it in items:
+        t = heapq.heappop(free)
+        heapq.heappush(free, t + int(it[3] - it[2]) + overhead)
+    return max(free)
+
+
+@pytest.mark.parametrize("name", ["b64_h128_L1k2k_bs128_bf16", "b32_sq4_h128_L512_16k_fp8"])
+def test_automatic_chunk_is_near_the_best_list_schedule(name):
+    """For the skewed 128-head batches the planner's chunk gives a simulated
+    list-schedule makespan within 3 % of the best forced chunk (64-key steps,
+    same per-item overhead as the planner's model: 320 keys for 128-row items)."""
+    import mla_inputs as mi
+    wl = mi.WORKLOADS[name]
+    lens = mi.draw_seq_lens(wl, np.random.default_rng(wl.seed))
+    maxb = int(max(1, (lens.max() + wl.block_size - 1) // wl.block_size))
+    items, rgs, _ = mla.mla_plan_host(lens, wl.s_q, wl.heads, wl.block_size, maxb)
+    assert rgs == 128
+    auto = list_schedule_makespan(items, 320)
+    best = min(list_schedule_makespan(mla.mla_plan_host(lens, wl.s_q, wl.heads, wl.block_size, maxb,
+                                                        split_keys=c)[0], 320)
+               for c in range(256, 8192, 64))
+    assert auto <= 1.03 * best, (auto, best)
