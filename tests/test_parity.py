@@ -157,6 +157,41 @@ def test_edge_cases(mla, case):
     assert_parity(o, l, ro, rl, dtype, tag)
 
 
+def random_cases(n, seed=2026):
+    """Seeded random descriptions across all three decode kernels: head counts
+    from 1 to 128 (one, two or several row groups), s_q up to 8, both block
+    sizes and caches, causal or not, lengths from 0 (no key) up to ~2500 with
+    ragged last pages and tiles, automatic or forced splits."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        H = int(rng.choice([1, 3, 8, 16, 20, 32, 64, 100, 128]))
+        s_q = int(rng.choice([1, 1, 2, 3, 4, 8]))
+        bs = int(rng.choice([64, 128]))
+        dtype = str(rng.choice(["bf16", "fp8"]))
+        B = int(rng.integers(1, 6))
+        lens = tuple(int(rng.integers(0, 10)) if rng.random() < 0.15 else int(rng.integers(10, 2500))
+                     for _ in range(B))
+        split = int(rng.choice([0, 0, 64, 320]))
+        causal = bool(rng.random() < 0.8)
+        tag = f"r{i}_B{B}_sq{s_q}_H{H}_bs{bs}_{dtype}_split{split}" + ("" if causal else "_nc")
+        cases.append((tag, B, s_q, H, bs, dtype, lens, split, causal))
+    return cases
+
+
+RANDOM = random_cases(16)
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_descriptions(mla, case):
+    tag, B, s_q, H, bs, dtype, lens, split, causal = case
+    wl = mi.Workload(tag, B, s_q, H, bs, dtype, "fixed", lens, causal=causal, seed=B * 1000 + H)
+    inp = mi.make_inputs(wl)
+    o, l = run_gpu(mla, inp, split_keys=split)
+    ro, rl = run_oracle(inp)
+    assert_parity(o, l, ro, rl, dtype, tag)
+
+
 # Score jumps: a key aligned with one query row lifts that row's running max by
 # far more than any ordinary tile does, after some tiles have been accumulated
 # (and again later), so the kernels must rescale what they already summed.
