@@ -57,6 +57,30 @@ def test_kv_append_is_bit_exact(mla, kv_dtype, bs):
         np.testing.assert_array_equal(got, ref)
 
 
+def test_kv_append_fp8_every_code_and_tie(mla):
+    """Every positive e4m3fn value, every midpoint between neighbouring values
+    (exact ties: the even mantissa wins), the bf16 values just below and above
+    each midpoint, values past 448 (saturation), both signs; scale 1, so the
+    row values reach the encoder unchanged. Byte for byte against the oracle."""
+    pos = orc.E4M3FN_TABLE[:0x7F].astype(np.float32)              # 0 .. 448
+    mid_bits = orc.round_bf16((pos[:-1] + pos[1:]) / np.float32(2))   # exact in bf16
+    vals = np.concatenate([orc.round_bf16(pos), mid_bits, mid_bits - 1, mid_bits + 1,
+                           orc.round_bf16(np.float32([464.0, 480.0, 1e4, 2.0 ** -10, 3 * 2.0 ** -11]))])
+    vals = np.concatenate([vals, vals | np.uint16(0x8000)]).astype(np.uint16)
+    n_rows = -(-len(vals) // 576)
+    rows = np.zeros((n_rows, 576), dtype=np.uint16)
+    rows.flat[:len(vals)] = vals
+    slots = np.arange(n_rows, dtype=np.int32)
+    kv0 = np.zeros((1, 64, 576), dtype=np.uint8)
+    ref = orc.kv_append(kv0, rows, slots, 1.0, "fp8")
+    dev = torch.device("cuda:0")
+    kv = torch.from_numpy(kv0).to(dev).view(torch.float8_e4m3fn)
+    r = torch.from_numpy(rows.view(np.int16)).to(dev).view(torch.bfloat16)
+    mla.mla_kv_append(r, torch.from_numpy(slots).to(dev), kv, 1.0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kv.view(torch.uint8).cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("name", ["tiny", "tiny_fp8"])
 def test_append_last_token_then_decode(mla, name):
     # rebuild each sequence's newest cached row through the append kernel
