@@ -53,9 +53,16 @@ struct AppendParams {
   uint8_t* kv;
   long long n_slots;   // num_blocks * block_size
   int n_tokens;
-  float kv_scale;
+  double inv_scale;    // 1 / kv_scale, rounded once to double on the host
 };
 
+// y = x / kv_scale, correctly rounded to float32, as one double product
+// rounded to float: for a bf16 x (8 significant bits) and a float32 scale the
+// exact quotient is never a float32 rounding midpoint (that would need x to
+// have 25 or more significant bits), and its distance to one is at least
+// about 2^-49 relative, against at most about 2^-52 of error in
+// double(x) * double(1 / kv_scale). So rounding the product gives the same
+// float as the division (also for overflow, zero, infinities and NaN).
 template <int KVT>
 __global__ __launch_bounds__(APPEND_THREADS) void mla_kv_append_kernel(AppendParams p) {
   const long long gid = (long long)blockIdx.x * APPEND_THREADS + threadIdx.x;
@@ -69,8 +76,8 @@ __global__ __launch_bounds__(APPEND_THREADS) void mla_kv_append_kernel(AppendPar
   float y[8];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    y[2 * k] = __builtin_bit_cast(float, w[k] << 16) / p.kv_scale;
-    y[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xFFFF0000u) / p.kv_scale;
+    y[2 * k] = static_cast<float>(static_cast<double>(__builtin_bit_cast(float, w[k] << 16)) * p.inv_scale);
+    y[2 * k + 1] = static_cast<float>(static_cast<double>(__builtin_bit_cast(float, w[k] & 0xFFFF0000u)) * p.inv_scale);
   }
   if constexpr (KVT == MLA_DTYPE_FP8_E4M3FN) {
     *reinterpret_cast<uint2*>(p.kv + (size_t)slot * D + 8 * c) =
@@ -103,7 +110,7 @@ extern "C" mla_status_t mla_kv_append(const void* rows, const int32_t* slot_mapp
   ap.kv = static_cast<uint8_t*>(kv_cache);
   ap.n_slots = (long long)num_blocks * block_size;
   ap.n_tokens = n_tokens;
-  ap.kv_scale = kv_scale;
+  ap.inv_scale = 1.0 / static_cast<double>(kv_scale);
   const long long threads = (long long)n_tokens * CHUNKS;
   const dim3 grid(static_cast<unsigned>((threads + APPEND_THREADS - 1) / APPEND_THREADS));
   hipStream_t st = static_cast<hipStream_t>(stream);

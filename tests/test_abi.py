@@ -221,6 +221,25 @@ def test_kv_append_rejects_bad_arguments(kw, code):
     assert append_call(**kw) == code
 
 
+def test_append_scale_product_equals_float32_division():
+    """The append kernel forms x / kv_scale as float(double(x) * (1 / double(kv_scale))).
+    For every bf16 x and a spread of float32 scales (powers of two, the
+    workloads' amax / 448 scales, extremes that overflow or give float32
+    subnormals, random magnitudes and random bit patterns) that equals the
+    correctly rounded float32 division bit for bit."""
+    x = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    rng = np.random.default_rng(5)
+    scales = [1.0, 0.5, 448.0, 1 / 448, 0.0213, 0.013029, 3.0, 0.1, 1e-30, 1e30, 2.0 ** -126, 3.4e38]
+    scales += list(np.exp(rng.uniform(np.log(1e-6), np.log(1e6), 40)))
+    scales += list(rng.integers(0x00800000, 0x7F7FFFFF, 40, dtype=np.uint32).view(np.float32))
+    with np.errstate(all="ignore"):
+        for s in np.asarray(scales, dtype=np.float32):
+            ref = x / s
+            got = (x.astype(np.float64) * (1.0 / np.float64(s))).astype(np.float32)
+            same = (ref.view(np.uint32) == got.view(np.uint32)) | (np.isnan(ref) & np.isnan(got))
+            assert same.all(), (float(s), x[~same][:4])
+
+
 def test_kv_append_zero_tokens_is_a_no_op():
     assert append_call(n=0, ptrs=False) == 0
 
