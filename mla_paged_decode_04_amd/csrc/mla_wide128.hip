@@ -232,12 +232,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
     return min(KT, t1 - ts);
   };
 
-  // The first three tiles are requested before q is loaded, so their
-  // latency overlaps the q loads (the compiler's own wait for q below also
-  // covers them; they were issued first).
-#pragma unroll
-  for (int k = 0; k < 3; ++k)
-    if (k < ntiles) issue(k);
+  // Tile 0 is requested before q is loaded, so its latency overlaps the q
+  // loads (the compiler's own wait for q below also covers it: it was issued
+  // first); tiles 1 and 2 go out once q is resident, so that wait does not
+  // include them while every workgroup starts at once.
+  if (ntiles > 0) issue(0);
 
   // Q^T operand: k-step t holds dims 16t + 8h .. +7 (bf16), or for fp8 (whose
   // K reads take 16 dims per lane at once) 32(t >> 1) + 16h + 8(t & 1) .. +7.
@@ -266,6 +265,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   // the DMAs)
 #pragma unroll
   for (int t = 0; t < QREG; ++t) asm volatile("" ::"v"(qb[t]));
+  // tiles 1 and 2 go out once q and tile 0 are resident
+#pragma unroll
+  for (int k = 1; k < 3; ++k)
+    if (k < ntiles) issue(k);
   auto q_operand = [&](int t) -> bf16x8_t {
     if (t < QREG) return qb[t];
     return *reinterpret_cast<const bf16x8_t*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4));
