@@ -110,8 +110,8 @@ __host__ __device__ inline int chunk_from_work(long long work, int forced, int t
 // The last term is the tail of the schedule: items are issued roughly longest
 // first, so the last workers to finish overrun the average by a fraction of
 // one item; a simulated list schedule of the skewed 128-head batches gives
-// about a fifth of an item. Ties go to the longer chunk (fewer partials). With many pairs the split
-// from the average (work / SLOTS) is kept. All integer, so the host mirror
+// about a fifth of an item. Ties go to the longer chunk (fewer partials).
+// With many pairs the split from the average (work / SLOTS) is kept. All integer, so the host mirror
 // reproduces the device plan exactly. (A batch of equal lengths keeps the
 // average split: every item then has the same length.)
 constexpr int SLOTS = 256;

@@ -260,9 +260,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
         *reinterpret_cast<uint4*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4)) = v;
     }
   }
-  // q loads (and with them the three tiles issued before) complete here, so
-  // the compiler places no wait for them inside the tile loop (it cannot see
-  // the DMAs)
+  // q loads (and with them tile 0, issued before) complete here, so the
+  // compiler places no wait for them inside the tile loop (it cannot see the
+  // DMAs)
 #pragma unroll
   for (int t = 0; t < QREG; ++t) asm volatile("" ::"v"(qb[t]));
   // tiles 1 and 2 go out once q and tile 0 are resident
