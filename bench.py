@@ -1,15 +1,20 @@
 """Benchmark of paged MLA decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+                    [--only] [--no-flush] [--no-cpu]
 
 One step is one ``mla_decode`` call — split planner, decode kernel, LSE
-combine — over one synthetic batch already resident in HBM. The default
+combine — over one synthetic batch already resident in HBM. The headline
 workload is the kernel-test shape of the CUTLASS_MLA fp8 review thread in bf16
-(B=128, s_q=1, H=16, 4096-token contexts, page size 64). Rank 0 prints one
-JSON line with the whole-job algorithmic HBM throughput (value, GB/s), the
-decode kernel's roofline fraction measured with HIP events on the stream it
-runs on, and the float64 CPU oracle timed on a bounded sample of the same
-workload (``cpu_baseline``).
+(B=128, s_q=1, H=16, 4096-token contexts, page size 64). One JSON line carries:
+  * value / ms_per_step: whole-call algorithmic GB/s of that workload;
+  * roofline: the decode kernel alone against its bound (HBM or bf16 MFMA),
+    with the whole call's and the reused-plan call's fractions beside it;
+  * workloads: the same figures for the four bench workloads (16 heads bf16 and
+    fp8, 128 heads bf16, 128 heads x 4 query tokens fp8), warm and with the
+    256 MB Infinity Cache evicted before each call;
+  * cpu_baseline: the float64 oracle on the host cores over a bounded sample
+    of the headline workload, plus a one-thread figure for the 16-head ones.
 """
 from __future__ import annotations
 
@@ -135,7 +140,52 @@ def cpu_baseline(inp, budget_s: float = 12.0):
             "seqs_per_s": round(n * passes / el, 3)}
 
 
-def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, flush: bool):
+def cpu_baseline_one_thread(names=("tiny", "b128_h16_L4096_bf16", "b128_h16_L4096_fp8"),
+                            n_seqs: int = 4):
+    """The oracle with one BLAS thread on the first `n_seqs` sequences of each
+    workload (the tiny one whole): seqs/s and GB/s of algorithmic bytes."""
+    from oracle import mla_oracle as orc
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:   # pragma: no cover
+        return None
+    res = {}
+    with threadpool_limits(limits=1):
+        for name in names:
+            wl = mi.WORKLOADS[name]
+            inp = mi.make_inputs(wl)
+            n = min(n_seqs, wl.batch)
+            t0 = time.perf_counter()
+            orc.mla_decode(inp.q_bits[:n], inp.kv, inp.block_table[:n], inp.seq_lens[:n], wl.s_q,
+                           wl.softmax_scale, inp.kv_scale, wl.kv_dtype, wl.causal)
+            el = time.perf_counter() - t0
+            gbs = algorithmic_bytes(inp) * (n / wl.batch) / el / 1e9
+            res[name] = {"seqs_per_s": round(n / el, 3), "GB/s": round(gbs, 4), "seconds": round(el, 3),
+                         "sequences": n}
+    return {"cores": 1, "kind": "oracle", "workloads": res}
+
+
+BENCH_WORKLOADS = ("b128_h16_L4096_bf16", "b128_h16_L4096_fp8", "b64_h128_L1k2k_bs128_bf16",
+                   "b32_sq4_h128_L512_16k_fp8")
+
+
+def roofline_of(nbytes: int, nflops: int, ms: float) -> dict:
+    """Fraction of the bound (HBM or bf16 MFMA) the algorithmic work sets."""
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfs = nflops / (ms * 1e-3) / 1e12
+    if nbytes / (HBM_PEAK_GBS * 1e9) >= nflops / (MFMA_BF16_PEAK_TFS * 1e12):
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
+
+
+def measure(name: str, steps: int, warmup: int, flush: bool):
+    """Time one workload: the whole mla_decode call (planner, decode kernel,
+    combine), the call on a reused plan (decode kernel + combine), and the
+    decode kernel alone, warm; with `flush`, also each of them with the 256 MB
+    Infinity Cache evicted (a 512 MB read sweep) before every call."""
+    import ctypes
     import torch
     import mla_paged_decode_04_amd as mla
 
@@ -152,112 +202,140 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, flush: bool):
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     lib = mla.library()
     stream = torch.cuda.current_stream()
-    import ctypes
     args = (q.data_ptr(), kv.data_ptr(), bt.data_ptr(), sl.data_ptr(), s_q,
             float(wl.softmax_scale), float(inp.kv_scale), out.data_ptr(), lse.data_ptr(),
             ctypes.byref(desc), ws.data_ptr(), ws_bytes, stream.cuda_stream)
-    scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=q.device) if flush else None
 
-    def step():
-        st = lib.mla_decode(*args)
+    def call(fn):
+        st = fn(*args)
         if st != 0:
-            raise RuntimeError(f"mla_decode status {st}")
+            raise RuntimeError(f"{fn.__name__} status {st}")
 
-    def fwd():
-        st = lib.mla_decode_fwd_only(*args)
-        if st != 0:
-            raise RuntimeError(f"mla_decode_fwd_only status {st}")
+    full = lambda: call(lib.mla_decode)                 # noqa: E731
+    reuse = lambda: call(lib.mla_decode_with_plan)      # noqa: E731
+    kernel = lambda: call(lib.mla_decode_fwd_only)      # noqa: E731
 
     for _ in range(warmup):
-        step()
+        full()
     torch.cuda.synchronize()
-
-    # whole steps: K back-to-back calls bracketed by events and synchronisation
-    if flush:
-        per = []
-        for _ in range(steps):
-            scratch.fill_(1.0)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            step()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            per.append(e0.elapsed_time(e1))
-        ms_step = float(np.median(per))
-        wall_ms = float(np.sum(per))
-    else:
+    # the first calls of a process run slower while the clocks ramp up: a
+    # fixed half second of untimed calls before anything is timed
+    t_end = time.perf_counter() + 0.5
+    while time.perf_counter() < t_end:
+        full()
         torch.cuda.synchronize()
+
+    def back_to_back(fn):
+        """K calls between one event pair (the kernel-trace durations agree
+        with this average within about 1 %)."""
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         e0.record(stream)
         for _ in range(steps):
-            step()
+            fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        wall_ms = (time.perf_counter() - t0) * 1e3
-        ms_step = e0.elapsed_time(e1) / steps
+        return e0.elapsed_time(e1) / steps, (time.perf_counter() - t0) * 1e3
 
-    # the decode kernel alone, on the same stream (plan left in the workspace)
-    fwd_ms = []
-    for _ in range(steps):
-        if flush:
-            scratch.fill_(1.0)
-        f0 = torch.cuda.Event(enable_timing=True)
-        f1 = torch.cuda.Event(enable_timing=True)
-        f0.record(stream)
-        fwd()
-        f1.record(stream)
-        if flush:
-            torch.cuda.synchronize()
-        fwd_ms.append((f0, f1))
-    torch.cuda.synchronize()
-    fwd_t = [a.elapsed_time(b) for a, b in fwd_ms]
-    fwd_pairs_avg = float(np.mean(fwd_t))
-    # The kernel's average launch time: K back-to-back launches between one
-    # event pair (a pair around every launch reads 5-11 % above the kernel
-    # durations rocprofv3 traces; the back-to-back average matches them).
-    # With the MALL flush between launches only the per-launch pairs apply.
-    if flush:
-        fwd_ms_avg = fwd_pairs_avg
-    else:
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
+    def per_call(fn, scratch=None):
+        """An event pair around every call (reads a few us above the trace),
+        after a 512 MB read sweep when `scratch` is given; median. The sweep
+        reads (the sum is discarded) rather than writes, so that it leaves
+        clean lines: a write sweep leaves the Infinity Cache full of dirty
+        lines whose write-back is then charged to the timed call."""
+        ts = []
         for _ in range(steps):
-            fwd()
-        g1.record(stream)
+            if scratch is not None:
+                scratch.sum()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    plan = lambda: call_plan()   # noqa: E731
+
+    def call_plan():
+        st = lib.mla_decode_plan(sl.data_ptr(), s_q, ctypes.byref(desc), ws.data_ptr(), ws_bytes,
+                                 stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"mla_decode_plan status {st}")
+
+    r = {"workload": name}
+    r["call_ms"], r["wall_ms_timed"] = back_to_back(full)
+    r["reuse_ms"], _ = back_to_back(reuse)
+    r["kernel_ms"], _ = back_to_back(kernel)
+    r["plan_ms"], _ = back_to_back(plan)
+    r["kernel_ms_event_pairs"] = per_call(kernel)
+    r["call_ms_event_pairs"] = per_call(full)
+    if flush:
+        scratch = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=q.device)
+        scratch.sum()
         torch.cuda.synchronize()
-        fwd_ms_avg = g0.elapsed_time(g1) / steps
-    # leave a correct result behind (fwd-only overwrote split partials only)
-    step()
+        r["kernel_ms_flushed"] = per_call(kernel, scratch)
+        r["call_ms_flushed"] = per_call(full, scratch)
+        r["reuse_ms_flushed"] = per_call(reuse, scratch)
+        del scratch
+    # leave a correct result behind (the kernel-only launches rewrite partials)
+    full()
     torch.cuda.synchronize()
+    r["nbytes"] = algorithmic_bytes(inp)
+    r["nflops"] = algorithmic_flops(inp)
+    r["kernel"] = decode_kernel_name(s_q * H)
+    r["inp"] = inp
+    return r
 
-    nbytes = algorithmic_bytes(inp)
-    nflops = algorithmic_flops(inp)
-    gbs = nbytes / (ms_step * 1e-3) / 1e9
-    tfs = nflops / (ms_step * 1e-3) / 1e12
-    fwd_gbs = nbytes / (fwd_ms_avg * 1e-3) / 1e9
-    fwd_tfs = nflops / (fwd_ms_avg * 1e-3) / 1e12
-    hbm_bound = nbytes / (HBM_PEAK_GBS * 1e9) >= nflops / (MFMA_BF16_PEAK_TFS * 1e12)
-    if hbm_bound:
-        roof = {"bound": "hbm", "achieved": round(fwd_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(fwd_gbs / HBM_PEAK_GBS, 4)}
-    else:
-        roof = {"bound": "mfma", "achieved": round(fwd_tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(fwd_tfs / MFMA_BF16_PEAK_TFS, 4)}
-    kernel = decode_kernel_name(s_q * H)
-    roof["traffic"] = traffic_from_profile(kernel, name)
-    roof["kernel"] = kernel
-    roof["kernel_ms"] = round(fwd_ms_avg, 5)
-    roof["kernel_ms_event_pairs"] = round(fwd_pairs_avg, 5)
-    roof["hbm_frac"] = round(fwd_gbs / HBM_PEAK_GBS, 4)
-    roof["mfma_frac"] = round(fwd_tfs / MFMA_BF16_PEAK_TFS, 4)
 
+def workload_summary(r: dict) -> dict:
+    """The per-workload figures of the JSON line: times in microseconds and the
+    fraction of the roofline for the kernel, the call and the reused-plan call."""
+    nb, nf = r["nbytes"], r["nflops"]
+    us = lambda ms: round(ms * 1e3, 2)   # noqa: E731
+    out = {"kernel": r["kernel"], "algorithmic_bytes": nb, "algorithmic_flops": nf,
+           "bound": roofline_of(nb, nf, 1.0)["bound"],
+           "kernel_us": us(r["kernel_ms"]), "call_us": us(r["call_ms"]),
+           "reuse_plan_call_us": us(r["reuse_ms"]), "plan_us": us(r["plan_ms"]),
+           "frac_kernel": roofline_of(nb, nf, r["kernel_ms"])["frac"],
+           "frac_call": roofline_of(nb, nf, r["call_ms"])["frac"],
+           "frac_reuse_plan_call": roofline_of(nb, nf, r["reuse_ms"])["frac"],
+           "kernel_us_event_pairs": us(r["kernel_ms_event_pairs"]),
+           "call_us_event_pairs": us(r["call_ms_event_pairs"])}
+    if "kernel_ms_flushed" in r:
+        out.update({"mall_flushed": {
+            "kernel_us": us(r["kernel_ms_flushed"]), "call_us": us(r["call_ms_flushed"]),
+            "reuse_plan_call_us": us(r["reuse_ms_flushed"]),
+            "frac_kernel": roofline_of(nb, nf, r["kernel_ms_flushed"])["frac"],
+            "frac_call": roofline_of(nb, nf, r["call_ms_flushed"])["frac"],
+            "timing": "event pair around each call, after a 512 MB read sweep; median"}})
+    out["hbm_frac_kernel"] = round(nb / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    out["mfma_frac_kernel"] = round(nf / (r["kernel_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
+    return out
+
+
+def bench_line(r: dict, steps: int, warmup: int, flush: bool, others=None, cpu=None):
+    """The JSON line for one measured workload."""
+    wl = r["inp"].wl
+    nbytes, nflops, ms_step = r["nbytes"], r["nflops"], r["call_ms"]
+    roof = roofline_of(nbytes, nflops, r["kernel_ms"])
+    roof["traffic"] = traffic_from_profile(r["kernel"], wl.name)
+    roof["kernel"] = r["kernel"]
+    roof["kernel_ms"] = round(r["kernel_ms"], 5)
+    roof["kernel_ms_event_pairs"] = round(r["kernel_ms_event_pairs"], 5)
+    roof["hbm_frac"] = round(nbytes / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    roof["mfma_frac"] = round(nflops / (r["kernel_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
+    roof["call_frac"] = roofline_of(nbytes, nflops, ms_step)["frac"]
+    roof["reuse_plan_call_frac"] = roofline_of(nbytes, nflops, r["reuse_ms"])["frac"]
+    if "kernel_ms_flushed" in r:
+        roof["frac_mall_flushed"] = roofline_of(nbytes, nflops, r["kernel_ms_flushed"])["frac"]
+        roof["kernel_ms_mall_flushed"] = round(r["kernel_ms_flushed"], 5)
     res = {
         "metric": METRIC,
-        "value": round(gbs, 2),
+        "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": steps,
@@ -268,21 +346,27 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, flush: bool):
         "vs_baseline": None,
         "dtype": wl.kv_dtype,
         "data": "synthetic",
-        "config": {"workload": name, "batch": B, "s_q": s_q, "heads": H,
+        "config": {"workload": wl.name, "batch": wl.batch, "s_q": wl.s_q, "heads": wl.heads,
                    "seq_lens": wl.lens if wl.lens != "fixed" else list(set(wl.lens_arg)),
                    "seq_len_range": list(wl.lens_arg), "block_size": wl.block_size,
                    "kv_dtype": wl.kv_dtype, "d_qk": 576, "d_v": 512, "causal": wl.causal,
                    "parallelism": "single_gpu"},
-        "tflops": round(tfs, 3),
-        "seqs_per_s": round(B / (ms_step * 1e-3), 1),
+        "tflops": round(nflops / (ms_step * 1e-3) / 1e12, 3),
+        "seqs_per_s": round(wl.batch / (ms_step * 1e-3), 1),
         "algorithmic_bytes": nbytes,
         "algorithmic_flops": nflops,
-        "wall_ms_timed": round(wall_ms, 3),
+        "wall_ms_timed": round(r["wall_ms_timed"], 3),
         "mall_flush": flush,
+        "timing": ("value / ms_per_step: K back-to-back mla_decode calls (planner, decode kernel, "
+                   "combine) between one event pair on the launch stream, warm; roofline: the decode "
+                   "kernel alone, timed the same way; *_mall_flushed: an event pair around each call "
+                   "after a 512 MB read sweep"),
         "roofline": roof,
     }
-    if with_cpu:
-        res["cpu_baseline"] = cpu_baseline(inp)
+    if others is not None:
+        res["workloads"] = others
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     return res
 
 
@@ -397,8 +481,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(mi.WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one line per workload")
-    ap.add_argument("--flush", action="store_true",
-                    help="evict the 256 MB Infinity Cache before every timed call")
+    ap.add_argument("--only", action="store_true",
+                    help="time only --workload (no per-workload summary of the others)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the timings with the 256 MB Infinity Cache evicted before each call")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration)")
@@ -407,6 +493,10 @@ def main():
     ap.add_argument("--append", action="store_true",
                     help="only time the cache append (128 and 65536 new rows, bf16 and fp8)")
     a = ap.parse_args()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
     if a.copy_calibration:
         copy_calibration()
         return
@@ -419,15 +509,29 @@ def main():
             for dt in ("bf16", "fp8"):
                 print(json.dumps(bench_append(n, dt, a.steps, a.warmup)), flush=True)
         return
-    if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
-                          "n_gpus": a.gpus}))
-        sys.exit(2)
-    names = list(mi.WORKLOADS) if a.all else [a.workload]
-    for n in names:
-        res = bench_one(n, a.steps, a.warmup, with_cpu=not a.no_cpu and n == names[0],
-                        flush=a.flush)
-        print(json.dumps(res), flush=True)
+    flush = not a.no_flush
+    if a.all:
+        for n in BENCH_WORKLOADS:
+            r = measure(n, a.steps, a.warmup, flush)
+            print(json.dumps(bench_line(r, a.steps, a.warmup, flush, others={n: workload_summary(r)})),
+                  flush=True)
+        return
+    head = measure(a.workload, a.steps, a.warmup, flush)
+    others = {a.workload: workload_summary(head)}
+    if not a.only:
+        for n in BENCH_WORKLOADS:
+            if n != a.workload:
+                r = measure(n, a.steps, a.warmup, flush)
+                others[n] = workload_summary(r)
+                del r
+                print(f"# timed {n}", file=sys.stderr, flush=True)
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline(head["inp"])
+        one = cpu_baseline_one_thread()
+        if one is not None:
+            cpu["one_thread"] = one
+    print(json.dumps(bench_line(head, a.steps, a.warmup, flush, others=others, cpu=cpu)), flush=True)
 
 
 if __name__ == "__main__":

@@ -20,6 +20,13 @@
  *   lse[b][i][h]         = ln(sum_t exp(s_t))                  (natural log)
  * A row that sees no key gets out = 0 and lse = -inf.
  *
+ * Input range: the kernels keep each row's softmax reference max from the
+ * first key tile it sees and move it only when a later score exceeds it by
+ * more than 64 (base 2), so un-normalised weights stay below 2^64 and the fp32
+ * output accumulators below 2^64 * max|v| * L. Caches whose latent values
+ * reach about 2^60 / L would overflow where the textbook algorithm would not;
+ * real latent caches are many orders of magnitude below that.
+ *
  * Every entry point is safe to call without a GPU as long as it returns an
  * error before launching (argument checks never touch the device).
  */
@@ -63,8 +70,9 @@ typedef struct mla_decode_desc {
     int32_t max_blocks_per_seq;  /* columns of block_table, >= 1 */
     int32_t kv_dtype;            /* mla_dtype_t */
     int32_t causal;              /* 0 or 1 */
-    int32_t split_keys;          /* 0: automatic split-KV; else every sequence is cut into
-                                    chunks of this many keys (multiple of 64) */
+    int32_t split_keys;          /* tuning/test override, 0 in production: 0 = automatic
+                                    split-KV; else every sequence is cut into chunks of this
+                                    many keys (multiple of 64) */
 } mla_decode_desc_t;
 
 /* Bytes of device workspace mla_decode needs for this problem (host-only
@@ -94,11 +102,17 @@ size_t mla_decode_workspace_size(int32_t s_q, const mla_decode_desc_t* desc);
  * Errors: on any MLA_ERR_* other than MLA_ERR_HIP nothing is launched and
  * nothing is written.
  *
+ * Block-table entries inside a sequence's range [0, ceil(L / bs)) must name a
+ * page in [0, num_blocks). An entry outside that range is not read: its
+ * tokens are left out of the softmax (as if they were not cached) and flag
+ * bit 2 below is set. Entries past ceil(L / bs) are never read.
+ *
  * Workspace layout after a call (for inspection by tests): int32 header
  * [0] work items, [1] chunk keys, [2] partial slots, [3] flags (bit 0: a
  * seq_len was clamped; bit 1: the plan did not fit the workspace bounds, which
- * the bounds exclude, and nothing was computed); at byte 256 the work items,
- * 8 x int32 each:
+ * the bounds exclude, and nothing was computed; bit 2: a block-table entry in
+ * range was outside [0, num_blocks)); at byte 256 the work items, 8 x int32
+ * each:
  * {b, row_group, key_begin, key_end, partial_slot (-1 = written directly), 0, 0, 0}.
  */
 mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
@@ -106,9 +120,30 @@ mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* bloc
                         float kv_scale, void* out, float* lse, const mla_decode_desc_t* desc,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Launches only the decode kernel (no planner, no combine), for timing that
- * kernel on its own: `workspace` must already hold the plan of a preceding
- * mla_decode or mla_decode_plan call with the same seq_lens and description.
+/*
+ * Decode on a plan made earlier: launches the decode kernel and the LSE
+ * combine but not the split planner. A decode step runs the same batch
+ * (same seq_lens values, s_q and description) through every layer of a model,
+ * so the plan can be made once per step ("[NVIDIA] Add Cutlass MLA backend",
+ * review thread on the ahead-of-time scheduler metadata: planning once per
+ * batch rather than once per call) and reused for each layer's q and cache.
+ *
+ * `workspace` must hold the plan that mla_decode or mla_decode_plan left
+ * there for the same seq_lens values, s_q and description, and nothing else
+ * may have used it since. q, kv_cache, block_table (same lengths), out and
+ * lse may differ from the planning call. Flag bit 2 accumulates over the calls
+ * that reuse one plan. Arguments, ownership and errors as for mla_decode.
+ */
+mla_status_t mla_decode_with_plan(const void* q, const void* kv_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t s_q, float softmax_scale,
+                                  float kv_scale, void* out, float* lse,
+                                  const mla_decode_desc_t* desc, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* TIMING / TEST HOOK, not for production use: launches only the decode
+ * kernel (no planner, no combine), for timing that kernel on its own:
+ * `workspace` must already hold the plan of a preceding mla_decode or
+ * mla_decode_plan call with the same seq_lens and description.
  * Rows of work items that were split get their partials in the workspace
  * instead of out/lse (fp16 rows scaled by a per-row power of two, with a
  * base-2 lse per row). Same arguments, checks and errors as mla_decode. */
@@ -119,13 +154,15 @@ mla_status_t mla_decode_fwd_only(const void* q, const void* kv_cache, const int3
                                  size_t workspace_bytes, void* stream);
 
 /* Runs only the split planner (the first kernel mla_decode launches) and
- * leaves the header and work items in the workspace as described above. */
+ * leaves the header and work items in the workspace as described above, ready
+ * for mla_decode_with_plan (also used by tests to inspect the plan). */
 mla_status_t mla_decode_plan(const int32_t* seq_lens, int32_t s_q, const mla_decode_desc_t* desc,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Host mirror of the planner: fills items[8 * n] for host seq_lens; returns the
- * number of items, or -1 if the description is invalid or max_items is short.
- * Also reports rows per work item and the chunk length chosen. */
+/* TEST HOOK, not for production use: host mirror of the planner; fills
+ * items[8 * n] for host seq_lens; returns the number of items, or -1 if the
+ * description is invalid or max_items is short. Also reports rows per work
+ * item and the chunk length chosen. */
 int32_t mla_plan_host(const int32_t* seq_lens_host, int32_t s_q, const mla_decode_desc_t* desc,
                       int32_t* items, int32_t max_items, int32_t* rows_per_item,
                       int32_t* chunk_keys);

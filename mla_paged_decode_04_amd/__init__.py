@@ -13,8 +13,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["mla_decode", "mla_decode_plan", "mla_plan_host", "mla_kv_append", "mla_absorb_q",
-           "mla_absorb_out", "workspace_size",
+__all__ = ["mla_decode", "mla_decode_plan", "mla_decode_with_plan",
+           "mla_plan_host", "mla_kv_append", "mla_absorb_q", "mla_absorb_out", "workspace_size",
            "library", "MlaError", "D_QK", "D_V", "LIB_PATH"]
 
 D_QK = 576
@@ -66,6 +66,8 @@ def library() -> ctypes.CDLL:
     lib.mla_decode.restype = ctypes.c_int
     lib.mla_decode_fwd_only.argtypes = [vp, vp, vp, vp, i32, f32, f32, vp, vp, pdesc, vp, sz, vp]
     lib.mla_decode_fwd_only.restype = ctypes.c_int
+    lib.mla_decode_with_plan.argtypes = [vp, vp, vp, vp, i32, f32, f32, vp, vp, pdesc, vp, sz, vp]
+    lib.mla_decode_with_plan.restype = ctypes.c_int
     lib.mla_decode_plan.argtypes = [vp, i32, pdesc, vp, sz, vp]
     lib.mla_decode_plan.restype = ctypes.c_int
     lib.mla_plan_host.argtypes = [vp, i32, pdesc, vp, i32, vp, vp]
@@ -122,19 +124,8 @@ def _check(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
-               seq_lens: torch.Tensor, softmax_scale: float, kv_scale: float = 1.0,
-               causal: bool = True, out: Optional[torch.Tensor] = None,
-               lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-               split_keys: int = 0, want_lse: bool = True
-               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Paged MLA decode (weight-absorbed MQA form).
-
-    q [B, s_q, H, 576] bf16; kv_cache [num_blocks, bs, 576] (or [num_blocks,
-    bs, 1, 576]) bf16 or float8_e4m3fn; block_table [B, max_blocks] int32;
-    seq_lens [B] int32. Returns out [B, s_q, H, 512] bf16 and lse [B, s_q, H]
-    fp32 (natural log), computed on the current torch stream.
-    """
+def _prepare(q, kv_cache, block_table, seq_lens, causal, out, lse, split_keys, want_lse):
+    """Checks and output allocation shared by the decode entry points."""
     if kv_cache.dim() == 4 and kv_cache.shape[2] == 1:
         kv_cache = kv_cache.view(kv_cache.shape[0], kv_cache.shape[1], kv_cache.shape[3])
     _check(q, "q", torch.bfloat16, 4)
@@ -165,20 +156,64 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
         _check(lse, "lse", torch.float32, 3)
         if tuple(lse.shape) != (B, s_q, H):
             raise ValueError(f"lse must be {(B, s_q, H)}")
+    return kv_cache, desc, out, lse
+
+
+def _decode_call(fn_name, q, kv_cache, block_table, seq_lens, softmax_scale, kv_scale, causal,
+                 out, lse, workspace, split_keys, want_lse):
+    kv_cache, desc, out, lse = _prepare(q, kv_cache, block_table, seq_lens, causal, out, lse,
+                                        split_keys, want_lse)
+    B, s_q, H, _ = q.shape
     lib = library()
     need = int(lib.mla_decode_workspace_size(s_q, ctypes.byref(desc)))
     if need == 0 and B > 0:
-        raise MlaError(2, f"mla_decode (B={B}, s_q={s_q}, H={H}, bs={bs})")
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    st = lib.mla_decode(q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
-                        seq_lens.data_ptr(), s_q, float(softmax_scale), float(kv_scale),
-                        out.data_ptr(), lse.data_ptr() if lse is not None else None,
-                        ctypes.byref(desc), workspace.data_ptr(), workspace.numel(), stream)
+        raise MlaError(2, f"{fn_name} (B={B}, s_q={s_q}, H={H}, bs={kv_cache.shape[1]})")
+    if workspace is None:
+        if fn_name == "mla_decode_with_plan":
+            raise ValueError("mla_decode_with_plan needs the workspace that holds the plan")
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = getattr(lib, fn_name)(q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
+                               seq_lens.data_ptr(), s_q, float(softmax_scale), float(kv_scale),
+                               out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                               ctypes.byref(desc), workspace.data_ptr(), workspace.numel(), stream)
     if st != 0:
-        raise MlaError(st, "mla_decode")
+        raise MlaError(st, fn_name)
     return out, lse
+
+
+def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+               seq_lens: torch.Tensor, softmax_scale: float, kv_scale: float = 1.0,
+               causal: bool = True, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               split_keys: int = 0, want_lse: bool = True
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Paged MLA decode (weight-absorbed MQA form).
+
+    q [B, s_q, H, 576] bf16; kv_cache [num_blocks, bs, 576] (or [num_blocks,
+    bs, 1, 576]) bf16 or float8_e4m3fn; block_table [B, max_blocks] int32;
+    seq_lens [B] int32. Returns out [B, s_q, H, 512] bf16 and lse [B, s_q, H]
+    fp32 (natural log), computed on the current torch stream. A workspace
+    passed in (uint8, at least ``workspace_size`` bytes) keeps the plan for
+    ``mla_decode_with_plan``.
+    """
+    return _decode_call("mla_decode", q, kv_cache, block_table, seq_lens, softmax_scale,
+                        kv_scale, causal, out, lse, workspace, split_keys, want_lse)
+
+
+def mla_decode_with_plan(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens: torch.Tensor, softmax_scale: float, workspace: torch.Tensor,
+                         kv_scale: float = 1.0, causal: bool = True,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         split_keys: int = 0, want_lse: bool = True
+                         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``mla_decode`` on the plan an earlier ``mla_decode`` / ``mla_decode_plan``
+    left in ``workspace`` for the same seq_lens values, s_q and description
+    (no planner launch)."""
+    return _decode_call("mla_decode_with_plan", q, kv_cache, block_table, seq_lens, softmax_scale,
+                        kv_scale, causal, out, lse, workspace, split_keys, want_lse)
 
 
 def mla_decode_plan(seq_lens: torch.Tensor, s_q: int, num_heads: int, block_size: int,

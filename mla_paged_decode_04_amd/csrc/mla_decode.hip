@@ -123,14 +123,32 @@ struct ChunkRange {
   bool search;
 };
 
+// Partial slots: a sequence split n >= 2 ways takes n <= 2 (n - 1) slots per
+// row group, and n - 1 < (its keys rounded to 64) / chunk, so a plan uses
+// fewer than 2 * work / chunk slots. An automatic chunk of at least
+// 2 * work / slot_cap therefore keeps every plan within slot_cap slots. With
+// the default cap of 8 * SLOTS this is the search's own lower end,
+// work / (4 * SLOTS).
+constexpr int DEFAULT_SLOT_CAP = 8 * SLOTS;
+
+__host__ __device__ inline int chunk_floor(long long work, int slot_cap) {
+  if (slot_cap <= 0) return 1 << 30;   // no slots at all: no splits
+  long long c = (2 * work + slot_cap - 1) / slot_cap;
+  c = (c + NT - 1) / NT * NT;
+  return c > (1LL << 30) ? (1 << 30) : static_cast<int>(c);
+}
+
 __host__ __device__ inline ChunkRange chunk_range(long long work, int pairs, bool uniform, int forced,
-                                                  int target) {
+                                                  int target, int slot_cap) {
   ChunkRange r;
-  const int c0 = chunk_from_work(work, forced, target);
+  int c0 = chunk_from_work(work, forced, target);
+  const int floor_c = forced == 0 ? chunk_floor(work, slot_cap) : 0;
+  if (c0 < floor_c) c0 = floor_c;
   r.search = forced == 0 && pairs < SEARCH_MAX_PAIRS && !uniform;
   r.lo = r.hi = c0;
   if (r.search) {
     r.lo = chunk_from_work(work, 0, 4 * SLOTS);
+    if (r.lo < floor_c) r.lo = floor_c;
     r.hi = c0 >= (1 << 29) ? c0 : 2 * c0;
   }
   return r;
@@ -181,15 +199,16 @@ struct WsLayout {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline WsLayout ws_layout(int batch, int s_q, int heads, int max_keys, int forced) {
+inline WsLayout ws_layout(int batch, int s_q, int heads, int max_keys, int forced,
+                          int slot_cap = DEFAULT_SLOT_CAP) {
   int rows = s_q * heads;
   RowCfg rc = row_config(rows);
   WsLayout w;
   w.max_items = max_items_bound(batch, rows, max_keys, forced);
-  // Partial slots: a pair split n >= 2 ways uses n <= 2(n - 1) slots, and the
-  // automatic chunk is at least work / (4 * SLOTS), so sum(n - 1) <= 4 * SLOTS.
+  // Partial slots: bounded by the items, and for automatic splits by the
+  // planner's slot cap (chunk_floor).
   w.max_slots = w.max_items;
-  if (forced == 0 && w.max_slots > 8LL * SLOTS) w.max_slots = 8LL * SLOTS;
+  if (forced == 0 && w.max_slots > slot_cap) w.max_slots = slot_cap;
   size_t off = HEADER_BYTES;
   w.items = off;   off = align256(off + (size_t)w.max_items * ITEM_INTS * 4);
   w.pairs = off;   off = align256(off + (size_t)batch * rc.nrg * 2 * 4);
@@ -209,7 +228,7 @@ struct PlanParams {
   int32_t* header;       // [0] items [1] chunk [2] slots [3] clamp flag
   int32_t* items;        // ITEM_INTS per item
   int32_t* pairs;        // per (b, row group): first slot, number of splits
-  int batch, nrg, max_keys, forced_chunk, target, overhead;
+  int batch, nrg, max_keys, forced_chunk, target, overhead, slot_cap;
   long long max_items, max_slots;
 };
 
@@ -231,13 +250,17 @@ __device__ __forceinline__ T wave_inclusive_scan(T v) {
 // seq_lens are read once into LDS. Block-wide steps: the total work (sum of
 // row groups x keys rounded to 64) bounds the chunk length, the candidate
 // chunks are costed (few pairs only), then an exclusive scan of per-thread
-// item / partial-slot counts places every item.
+// item / partial-slot counts places every item. With one sequence per thread
+// the items are then written item-parallel (each thread finds an item's
+// sequence by a binary search over the scan), otherwise by their owners.
 __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
   extern __shared__ int32_t s_len[];          // batch entries
   __shared__ long long s_work[PLAN_WAVES], s_keys[PLAN_WAVES];
   __shared__ int s_min[PLAN_WAVES], s_max[PLAN_WAVES];
   __shared__ int s_cnt[CHUNK_CANDIDATES], s_mx[CHUNK_CANDIDATES];
   __shared__ int s_long[PLAN_WAVES], s_tail[PLAN_WAVES], s_slots[PLAN_WAVES], s_flag[PLAN_WAVES];
+  // one sequence per thread: inclusive scan of long items and first slot per sequence
+  __shared__ int s_inc_long[PLAN_THREADS], s_slot0[PLAN_THREADS];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
 
   int clamped = 0;
@@ -287,7 +310,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     lmax = max(lmax, s_max[i]);
     flag |= s_flag[i];
   }
-  const ChunkRange cr = chunk_range(total, p.batch * p.nrg, lmin == lmax, p.forced_chunk, p.target);
+  const ChunkRange cr = chunk_range(total, p.batch * p.nrg, lmin == lmax, p.forced_chunk, p.target,
+                                    p.slot_cap);
   int chunk = cr.lo;
   if (cr.search) {
     // items and longest item for every candidate chunk (8 threads per
@@ -368,37 +392,76 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
   // Cannot happen within the workspace bounds; if it did, no item runs and
   // the header says so (bit 1 of the flag word).
   const bool overflow = tot_items > p.max_items || tot_slots > p.max_slots;
-  for (int b = b0; b < b1; ++b) {
-    const int L = s_len[b];
-    int n, len;
-    seq_split(L, chunk, &n, &len);
-    if (overflow) n = 1;
-    // pair (b, rg) owns the partial slots slot + rg * n .. + n - 1. Items go
-    // longest first: every chunk but a sequence's last (all of full length)
-    // before the last chunks, chunk-major within each class, so the row
-    // groups of one chunk stay consecutive (side by side on one XCD, sharing
-    // its L2 for the cache rows).
-    for (int rg = 0; rg < p.nrg; ++rg) {
-      p.pairs[2 * (b * p.nrg + rg)] = n > 1 ? slot + rg * n : -1;
-      p.pairs[2 * (b * p.nrg + rg) + 1] = n;
+  // Pair (b, rg) owns the partial slots slot_b + rg * n .. + n - 1. Items go
+  // longest first: every chunk but a sequence's last (all of full length)
+  // before the last chunks, chunk-major within each class, so the row groups
+  // of one chunk stay consecutive (side by side on one XCD, sharing its L2
+  // for the cache rows).
+  auto write_item = [&](int item, int b, int rg, int s, int n, int len, int L, int slot_b) {
+    if (item < p.max_items) {
+      int4* it = reinterpret_cast<int4*>(p.items + (size_t)item * ITEM_INTS);
+      it[0] = make_int4(b, rg, s * len, min(L, (s + 1) * len));
+      it[1] = make_int4(n > 1 ? slot_b + rg * n + s : -1, 0, 0, 0);
     }
-    for (int s = 0; s < n; ++s)
-      for (int rg = 0; rg < p.nrg; ++rg) {
-        int& item = s < n - 1 ? litem : titem;
-        if (item < p.max_items) {
-          int4* it = reinterpret_cast<int4*>(p.items + (size_t)item * ITEM_INTS);
-          it[0] = make_int4(b, rg, s * len, min(L, (s + 1) * len));
-          it[1] = make_int4(n > 1 ? slot + rg * n + s : -1, 0, 0, 0);
-        }
-        ++item;
+  };
+  if (per == 1) {
+    // thread b owns sequence b: publish its long-item scan and first slot,
+    // then write items and pairs spread over all threads
+    const int me_long = overflow ? 0 : my_long;
+    const int inc = litem + me_long;   // exclusive start + own count
+    s_inc_long[tid] = tid < p.batch ? inc : INT32_MAX;
+    s_slot0[tid] = slot;
+    __syncthreads();
+    const int n_long = overflow ? 0 : tot_long;
+    for (int i = tid; i < n_long; i += PLAN_THREADS) {
+      // the sequence of long item i: the first b with inclusive scan > i
+      int lo = 0, hi = p.batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_inc_long[mid] > i) hi = mid; else lo = mid + 1;
       }
-    if (n > 1) slot += p.nrg * n;
+      const int b = lo, L = s_len[b];
+      int n, len;
+      seq_split(L, chunk, &n, &len);
+      const int local = i - (s_inc_long[b] - p.nrg * (n - 1));
+      const int s = local / p.nrg;
+      write_item(i, b, local - s * p.nrg, s, n, len, L, s_slot0[b]);
+    }
+    const int n_tail = p.batch * p.nrg;
+    for (int i = tid; i < n_tail; i += PLAN_THREADS) {
+      // last chunks: nrg per sequence, in sequence order; also the pair entry
+      const int b = i / p.nrg, rg = i - b * p.nrg, L = s_len[b];
+      int n, len;
+      seq_split(L, chunk, &n, &len);
+      if (overflow) n = 1;
+      write_item(n_long + i, b, rg, n - 1, n, len, L, s_slot0[b]);
+      p.pairs[2 * i] = n > 1 ? s_slot0[b] + rg * n : -1;
+      p.pairs[2 * i + 1] = n;
+    }
+  } else {
+    for (int b = b0; b < b1; ++b) {
+      const int L = s_len[b];
+      int n, len;
+      seq_split(L, chunk, &n, &len);
+      if (overflow) n = 1;
+      for (int rg = 0; rg < p.nrg; ++rg) {
+        p.pairs[2 * (b * p.nrg + rg)] = n > 1 ? slot + rg * n : -1;
+        p.pairs[2 * (b * p.nrg + rg) + 1] = n;
+      }
+      for (int s = 0; s < n; ++s)
+        for (int rg = 0; rg < p.nrg; ++rg) {
+          int& item = s < n - 1 ? litem : titem;
+          write_item(item, b, rg, s, n, len, L, slot);
+          ++item;
+        }
+      if (n > 1) slot += p.nrg * n;
+    }
   }
   if (tid == 0) {
     p.header[0] = overflow ? 0 : tot_items;
     p.header[1] = chunk;
     p.header[2] = tot_slots;
-    p.header[3] = flag | (overflow ? 2 : 0);
+    p.header[3] = (flag ? FLAG_SEQ_LEN_CLAMPED : 0) | (overflow ? FLAG_PLAN_OVERFLOW : 0);
   }
 }
 
@@ -522,7 +585,8 @@ void launch_decode(int kv_dtype, int kind, dim3 grid, hipStream_t st, const FwdP
 }
 
 mla_status_t launch_plan(const int32_t* seq_lens, int32_t s_q, const mla_decode_desc_t* desc,
-                         void* workspace, const WsLayout& ws, hipStream_t st) {
+                         void* workspace, const WsLayout& ws, hipStream_t st,
+                         int slot_cap = DEFAULT_SLOT_CAP) {
   RowCfg rc = row_config(s_q * desc->num_heads);
   char* base = static_cast<char*>(workspace);
   PlanParams pp;
@@ -538,6 +602,7 @@ mla_status_t launch_plan(const int32_t* seq_lens, int32_t s_q, const mla_decode_
   pp.forced_chunk = desc->split_keys;
   pp.max_items = ws.max_items;
   pp.max_slots = ws.max_slots;
+  pp.slot_cap = slot_cap;
   hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(PLAN_THREADS),
                      static_cast<unsigned>(desc->batch) * sizeof(int32_t), st, pp);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
@@ -569,23 +634,34 @@ mla_status_t mla_decode_plan(const int32_t* seq_lens, int32_t s_q, const mla_dec
 
 namespace {
 
-mla_status_t check_call(const void* q, const void* kv_cache, const int32_t* block_table,
+// Host-only checks of the decode arguments other than the workspace.
+mla_status_t check_args(const void* q, const void* kv_cache, const int32_t* block_table,
                         const int32_t* seq_lens, int32_t s_q, float softmax_scale,
                         float kv_scale, const void* out, const float* lse,
-                        const mla_decode_desc_t* desc, const void* workspace,
-                        size_t workspace_bytes, WsLayout* ws) {
+                        const mla_decode_desc_t* desc) {
   mla_status_t st = check_desc(s_q, desc);
   if (st != MLA_OK) return st;
   if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f) ||
       !(std::isfinite(kv_scale) && kv_scale > 0.f))
     return MLA_ERR_INVALID_ARGUMENT;
   if (q == nullptr || kv_cache == nullptr || block_table == nullptr || seq_lens == nullptr ||
-      out == nullptr || workspace == nullptr)
+      out == nullptr)
     return MLA_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) ||
-      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(workspace, 256) ||
-      (lse != nullptr && !aligned(lse, 4)))
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse != nullptr && !aligned(lse, 4)))
     return MLA_ERR_INVALID_ARGUMENT;
+  return MLA_OK;
+}
+
+mla_status_t check_call(const void* q, const void* kv_cache, const int32_t* block_table,
+                        const int32_t* seq_lens, int32_t s_q, float softmax_scale,
+                        float kv_scale, const void* out, const float* lse,
+                        const mla_decode_desc_t* desc, const void* workspace,
+                        size_t workspace_bytes, WsLayout* ws) {
+  mla_status_t st = check_args(q, kv_cache, block_table, seq_lens, s_q, softmax_scale, kv_scale,
+                               out, lse, desc);
+  if (st != MLA_OK) return st;
+  if (workspace == nullptr || !aligned(workspace, 256)) return MLA_ERR_INVALID_ARGUMENT;
   *ws = ws_layout(desc->batch, s_q, desc->num_heads, max_keys_of(desc), desc->split_keys);
   if (workspace_bytes < ws->total) return MLA_ERR_WORKSPACE_TOO_SMALL;
   return MLA_OK;
@@ -607,6 +683,7 @@ mla_status_t launch_decode_kernel(const void* q, const void* kv_cache,
   fp.out = static_cast<uint16_t*>(out);
   fp.lse = lse;
   fp.header = reinterpret_cast<const int32_t*>(base);
+  fp.flags = reinterpret_cast<int32_t*>(base) + 3;
   fp.items = reinterpret_cast<const int32_t*>(base + ws.items);
   fp.part_o = reinterpret_cast<_Float16*>(base + ws.part_o);
   fp.part_lse = reinterpret_cast<float*>(base + ws.part_lse);
@@ -679,6 +756,21 @@ mla_status_t mla_decode_fwd_only(const void* q, const void* kv_cache, const int3
                                 false);
 }
 
+mla_status_t mla_decode_with_plan(const void* q, const void* kv_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t s_q, float softmax_scale,
+                                  float kv_scale, void* out, float* lse,
+                                  const mla_decode_desc_t* desc, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  WsLayout ws;
+  mla_status_t st = check_call(q, kv_cache, block_table, seq_lens, s_q, softmax_scale, kv_scale,
+                               out, lse, desc, workspace, workspace_bytes, &ws);
+  if (st != MLA_OK) return st;
+  if (desc->batch == 0) return MLA_OK;
+  return launch_decode_kernel(q, kv_cache, block_table, seq_lens, s_q, softmax_scale, kv_scale,
+                                out, lse, desc, workspace, ws, static_cast<hipStream_t>(stream),
+                                true);
+}
+
 int32_t mla_plan_host(const int32_t* seq_lens_host, int32_t s_q, const mla_decode_desc_t* desc,
                       int32_t* items, int32_t max_items, int32_t* rows_per_item,
                       int32_t* chunk_keys) {
@@ -695,7 +787,8 @@ int32_t mla_plan_host(const int32_t* seq_lens_host, int32_t s_q, const mla_decod
     lmin = std::min(lmin, L);
     lmax = std::max(lmax, L);
   }
-  const ChunkRange cr = chunk_range(work, desc->batch * rc.nrg, lmin == lmax, desc->split_keys, rc.target);
+  const ChunkRange cr = chunk_range(work, desc->batch * rc.nrg, lmin == lmax, desc->split_keys, rc.target,
+                                    DEFAULT_SLOT_CAP);
   int chunk = cr.lo;
   if (cr.search) {
     const int step = chunk_step(cr);

@@ -136,6 +136,19 @@ __device__ __forceinline__ int partial_exponent(float amax) {
   return amax > 0.f && amax < INFINITY ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
 }
 
+// Bits of the workspace header's flag word ([3]).
+constexpr int FLAG_SEQ_LEN_CLAMPED = 1;   // a seq_len was outside [0, max_blocks * bs]
+constexpr int FLAG_PLAN_OVERFLOW = 2;     // the plan did not fit the workspace bounds
+constexpr int FLAG_BAD_PAGE = 4;          // a block-table entry in range was outside [0, num_blocks)
+
+// Record (once per wave) that a tile's page id was outside [0, num_blocks):
+// the tile was read from page 0, zeroed, and its keys masked out. Called after
+// the last tile wait, so the atomic does not disturb the DMA vmcnt counting.
+__device__ __forceinline__ void flag_bad_page(int32_t* flags, bool bad) {
+  if (bad && (threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_or(flags, FLAG_BAD_PAGE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 struct FwdParams {
   const uint16_t* q;
   const uint8_t* kv;
@@ -144,6 +157,7 @@ struct FwdParams {
   uint16_t* out;
   float* lse;
   const int32_t* header;
+  int32_t* flags;     // header word 3: decode kernels OR in FLAG_BAD_PAGE
   const int32_t* items;
   _Float16* part_o;   // split partials: fp16 rows of o * 2^part_scale
   float* part_lse;     // base-2 lse per partial row

@@ -260,12 +260,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
         lds_dma16(src + (n & 1) * 16 * ROWB + (n >> 1) * 64, dma_lane[n & 1], l0 + n * 1024);
     }
   };
+  // keys of tile j that hold data; -1 when its page id is out of range (the
+  // tile is then zeroed and every key masked)
   auto valid_keys = [&](int j) {
     const int ts = t0 + KT * j;
     int page = bt[ts >> bsh];
-    if (page < 0 || page >= p.num_blocks) return 0;
+    if (page < 0 || page >= p.num_blocks) return -1;
     return min(KT, t1 - ts);
   };
+  bool bad_page = false;
+  bool tile_ok = true;
   auto fix_tail = [&](int nv, char* buf) {
     if (nv >= KT) return;
 #pragma unroll
@@ -288,7 +292,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
       wait_vmcnt<0>();
     }
     mem_fence_compiler();
-    fix_tail(valid_keys(j), cur);
+    const int nv = valid_keys(j);
+    tile_ok = nv >= 0;
+    bad_page |= !tile_ok;
+    fix_tail(nv, cur);
     return cur;
   };
 
@@ -322,7 +329,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
       for (int jj = 0; jj < 4; ++jj) {
         const int key = ts + 16 * mi + 4 * g + jj;
         float v = sacc[mi][jj] * p.scale_log2;
-        v = key < limit ? v : -INFINITY;
+        v = key < limit && tile_ok ? v : -INFINITY;
         x[mi][jj] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -408,6 +415,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
     for (j += 4, ++itn; j < ntiles; j += 4, ++itn)
       compute(prepare(j, itn), t0 + KT * j, std::true_type{});
   }
+  flag_bad_page(p.flags, bad_page);
   __syncthreads();
   merge_and_store<4>(p, smem, o, m_run, l_run, b, 0, slot);
 }

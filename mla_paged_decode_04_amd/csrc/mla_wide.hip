@@ -162,12 +162,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
       }
     }
   };
+  // keys of tile j that hold data; -1 when its page id is out of range (the
+  // tile is then zeroed and every key masked)
   auto valid_keys = [&](int j) {
     const int ts = t0 + W_NTK * j;
     int page = bt[ts >> bsh];
-    if (page < 0 || page >= p.num_blocks) return 0;
+    if (page < 0 || page >= p.num_blocks) return -1;
     return min(W_NTK, t1 - ts);
   };
+  bool bad_page = false, tile_bad = false;
   // wait until this wave's transfers of tile j landed, given that tiles up to
   // j + ahead were issued after it
   auto wait_tile = [&](int ahead) {
@@ -193,6 +196,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
     wait_tile(min(2, ntiles - 1 - j));
     mem_fence_compiler();
     const int nv = valid_keys(j);
+    tile_bad = nv < 0;
+    bad_page |= tile_bad;
     const char* cur;
     if constexpr (!F8) {
       cur = smem + (j & 3) * W_TILE;
@@ -269,13 +274,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) x[h][jj] = sacc[h][jj];
-    if (__builtin_amdgcn_ballot_w64(ts + W_NTK > limit)) {   // a tile that reaches a row's limit
+    // a tile that reaches a row's limit, or whose page id was out of range
+    if (tile_bad || __builtin_amdgcn_ballot_w64(ts + W_NTK > limit)) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int key = ts + 16 * h + 4 * g + jj;
-          x[h][jj] = key < limit ? x[h][jj] : -INFINITY;
+          x[h][jj] = key < limit && !tile_bad ? x[h][jj] : -INFINITY;
         }
     }
     float tmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
@@ -336,6 +342,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
     compute(cur, t0 + W_NTK * j, std::true_type{});
     for (++j; j < ntiles; ++j) compute(prepare(j), t0 + W_NTK * j, std::true_type{});
   }
+
+  flag_bad_page(p.flags, bad_page);
 
   // ---- write this wave's rows: final (slot < 0) or split partial ----
   const float l_row = wave_sum_across_groups(l_run);

@@ -225,12 +225,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
       for (int i = 0; i < X_NDMA; ++i) one(i, std::false_type{});
     }
   };
+  // keys of slot-tile j that hold data; -1 when its page id is out of range
+  // (the tile is then zeroed and every key masked)
   auto valid_keys = [&](int j) {
     const int ts = t0 + KT * j;
     int page = bt[ts >> bsh];
-    if (page < 0 || page >= p.num_blocks) return 0;
+    if (page < 0 || page >= p.num_blocks) return -1;
     return min(KT, t1 - ts);
   };
+  bool bad_page = false, tile_bad = false;
 
   // Tile 0 is requested before q is loaded, so its latency overlaps the q
   // loads (the compiler's own wait for q below also covers it: it was issued
@@ -310,6 +313,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
     mem_fence_compiler();
     char* cur = smem + (j & 3) * X_TILE;
     const int nv = valid_keys(j);
+    tile_bad = nv < 0;
+    bad_page |= tile_bad;
     if (nv < KT) {
       const int lk = F8 ? (lane >> 2) : (lane >> 3);   // key within the transfer
 #pragma unroll
@@ -348,11 +353,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
       for (int t = 0; t < D / 16; ++t) {
         const bf16x8_t a = kr[t % QK_AHEAD];
         if (t + QK_AHEAD < D / 16) kr[t % QK_AHEAD] = lds_b128(kaddr(t + QK_AHEAD));
-        const bf16x8_t qv = SLOW ? q_operand_mem(t) : q_operand(t);
-        if (t == 0)
-          qk_first(sacc, a, qv);
-        else
-          qk_next(sacc, a, qv);
+        // the rescaling loop's q operand comes through a VALU select
+        // (masked rows), so it takes the forms with the wait states
+        if constexpr (SLOW) {
+          const bf16x8_t qv = q_operand_mem(t);
+          if (t == 0)
+            qk_first_v(sacc, a, qv);
+          else
+            qk_next_v(sacc, a, qv);
+        } else {
+          const bf16x8_t qv = q_operand(t);
+          if (t == 0)
+            qk_first(sacc, a, qv);
+          else
+            qk_next(sacc, a, qv);
+        }
       }
     } else {
       auto kaddr = [&](int u) { return (kbase ^ ((u & 1) << 5)) + (u >> 1) * X_GSTRIDE + 2048 * half; };
@@ -381,8 +396,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
     float x[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = sacc[e];
-    if (__builtin_amdgcn_ballot_w64(ts + X_STEP > limit)) {   // a step that reaches a row's limit
-      const int rel = limit - ts - 4 * hi;   // element e is visible iff 8(e >> 2) + (e & 3) < rel
+    // a step that reaches a row's limit, or whose page id was out of range
+    if (tile_bad || __builtin_amdgcn_ballot_w64(ts + X_STEP > limit)) {
+      // element e is visible iff 8(e >> 2) + (e & 3) < rel
+      const int rel = tile_bad ? -64 : limit - ts - 4 * hi;
 #pragma unroll
       for (int e = 0; e < 16; ++e) x[e] = 8 * (e >> 2) + (e & 3) < rel ? x[e] : -INFINITY;
     }
@@ -478,6 +495,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
       compute(cur, k, std::true_type{});
     }
   }
+
+  flag_bad_page(p.flags, bad_page);
 
   // ---- write this wave's rows: final (slot < 0) or split partial ----
   // The rows leave through LDS (the ring is free once every wave is past its

@@ -18,7 +18,9 @@ What it computes (plain reading of the pages):
     scores = softmax_scale * (q . k); lse is the natural log of the softmax
     denominator including both scales; with s_q > 1 query tokens the causal
     mask is bottom-right aligned (query token i sees keys [0, L - s_q + 1 + i));
-    a row that sees no key gets out = 0, lse = -inf.
+    a row that sees no key gets out = 0, lse = -inf; a block-table entry
+    outside [0, num_blocks) inside a sequence's range holds no keys (its
+    tokens are left out of the softmax).
 
 Everything is float64 and unblocked: one numpy matmul per (sequence, query
 token) for the scores and one for the weighted sum of values.
@@ -86,20 +88,39 @@ def decode_rows(raw: np.ndarray, kv_dtype: str) -> np.ndarray:
 # paging
 # ---------------------------------------------------------------------------
 
+def page_is_valid(page: int, num_blocks: int) -> bool:
+    """A block-table entry names a page of the cache only if it lies in
+    [0, num_blocks). (Reading: the pages never show an invalid entry inside a
+    sequence's range; such a page is taken to hold no keys.)"""
+    return 0 <= page < num_blocks
+
+
 def gather_keys(kv: np.ndarray, block_table_row: np.ndarray, seq_len: int,
                 kv_dtype: str, kv_scale: float) -> np.ndarray:
     """Rows 0..seq_len-1 of one sequence, in token order, as float64.
 
     Token t lives at page ``block_table_row[t // bs]``, slot ``t % bs``
     (paged cache of the kernel test in the CUTLASS_MLA fp8 review thread).
+    Rows of an invalid page (``page_is_valid``) are left as zeros here and
+    excluded by ``valid_key_mask``.
     """
     bs = kv.shape[1]
-    out = np.empty((seq_len, D_QK), dtype=np.float64)
+    out = np.zeros((seq_len, D_QK), dtype=np.float64)
     for t in range(0, seq_len, bs):
         page = int(block_table_row[t // bs])
+        if not page_is_valid(page, kv.shape[0]):
+            continue
         n = min(bs, seq_len - t)
         out[t:t + n] = decode_rows(kv[page, :n], kv_dtype)
     return out * np.float64(kv_scale)
+
+
+def valid_key_mask(block_table_row: np.ndarray, seq_len: int, block_size: int,
+                   num_blocks: int) -> np.ndarray:
+    """True for the tokens 0..seq_len-1 whose page is valid."""
+    pages = np.asarray(block_table_row[:(seq_len + block_size - 1) // block_size], dtype=np.int64)
+    ok = (pages >= 0) & (pages < num_blocks)
+    return np.repeat(ok, block_size)[:seq_len]
 
 
 # ---------------------------------------------------------------------------
@@ -123,6 +144,20 @@ def attend(qrows: np.ndarray, keys: np.ndarray, softmax_scale: float
     return out, lse
 
 
+def attend_abs(qrows: np.ndarray, keys: np.ndarray, softmax_scale: float) -> np.ndarray:
+    """The softmax-weighted mean of |v| per output element: sum_t w_t |v_t| /
+    sum_t w_t with the same weights as ``attend`` ([n, 512]; zeros when there
+    is no key). It bounds |out| elementwise (convexity) and is the scale of
+    the error that rounding the weights makes in out, which is what the
+    elementwise parity bound of the GPU tests is stated against."""
+    n = qrows.shape[0]
+    if keys.shape[0] == 0:
+        return np.zeros((n, D_V))
+    s = np.float64(softmax_scale) * (qrows @ keys.T)
+    w = np.exp(s - s.max(axis=1, keepdims=True))
+    return (w @ np.abs(keys[:, :D_V])) / w.sum(axis=1, keepdims=True)
+
+
 def visible_keys(seq_len: int, s_q: int, i: int, causal: bool) -> int:
     """Number of keys query token i (0-based among the s_q new tokens) sees.
     The new tokens are the last s_q of the sequence (they are already in the
@@ -134,27 +169,37 @@ def visible_keys(seq_len: int, s_q: int, i: int, causal: bool) -> int:
 
 def mla_decode(q_bits: np.ndarray, kv: np.ndarray, block_table: np.ndarray,
                seq_lens: np.ndarray, s_q: int, softmax_scale: float,
-               kv_scale: float, kv_dtype: str, causal: bool = True
-               ) -> Tuple[np.ndarray, np.ndarray]:
+               kv_scale: float, kv_dtype: str, causal: bool = True,
+               with_abs: bool = False):
     """Paged MLA decode in its weight-absorbed MQA form.
 
     q_bits: uint16 bf16 bits [B, s_q, H, 576]; kv: uint16 bf16 bits or uint8
     e4m3fn codes [num_blocks, bs, 576]; block_table int32 [B, max_blocks];
-    seq_lens int32 [B]. Returns float64 out [B, s_q, H, 512], lse [B, s_q, H].
+    seq_lens int32 [B]. Returns float64 out [B, s_q, H, 512], lse [B, s_q, H]
+    (and, with ``with_abs``, ``attend_abs`` of every row as a third array).
+    Keys on invalid pages are not attended (``valid_key_mask``).
     """
     B, sq, H, d = q_bits.shape
     assert sq == s_q and d == D_QK and kv.shape[2] == D_QK
+    nb, bs = kv.shape[0], kv.shape[1]
     out = np.zeros((B, s_q, H, D_V), dtype=np.float64)
     lse = np.full((B, s_q, H), -np.inf, dtype=np.float64)
+    vabs = np.zeros((B, s_q, H, D_V), dtype=np.float64) if with_abs else None
     for b in range(B):
         L = int(seq_lens[b])
         keys = gather_keys(kv, block_table[b], L, kv_dtype, kv_scale)
+        ok = valid_key_mask(block_table[b], L, bs, nb)
         for i in range(s_q):
             n_vis = visible_keys(L, s_q, i, causal)
             qrows = bf16_bits_to_f64(q_bits[b, i])
-            o, l = attend(qrows, keys[:n_vis], softmax_scale)
+            vis = keys[:n_vis][ok[:n_vis]]
+            o, l = attend(qrows, vis, softmax_scale)
             out[b, i] = o
             lse[b, i] = l
+            if with_abs:
+                vabs[b, i] = attend_abs(qrows, vis, softmax_scale)
+    if with_abs:
+        return out, lse, vabs
     return out, lse
 
 
@@ -183,18 +228,42 @@ def combine_partials(o_parts: np.ndarray, lse_parts: np.ndarray
 # ---------------------------------------------------------------------------
 
 def cos_diff(x: np.ndarray, y: np.ndarray) -> float:
-    """The parity metric of the kernel test in the CUTLASS_MLA fp8 review
-    thread: 1 - 2*sum(x*y) / max(sum(x*x + y*y), 1e-12)."""
-    x = np.asarray(x, dtype=np.float64)
-    y = np.asarray(y, dtype=np.float64)
-    return float(1.0 - 2.0 * (x * y).sum() / max(float((x * x + y * y).sum()), 1e-12))
+    """The similarity measure the kernel test of the CUTLASS_MLA fp8 review
+    thread asserts on, from its definition: the squared distance of x and y
+    relative to their summed squared norms, ||x - y||^2 / (||x||^2 + ||y||^2).
+    It is 0 for x = y, 1 when one of them is zero (or the two are
+    orthogonal) and 2 for y = -x. Two all-zero arrays count as equal (0)."""
+    x = np.asarray(x, dtype=np.float64).ravel()
+    y = np.asarray(y, dtype=np.float64).ravel()
+    den = float(np.dot(x, x) + np.dot(y, y))
+    if den == 0.0:
+        return 0.0
+    d = x - y
+    return float(np.dot(d, d) / den)
 
 
 def rel_fro(x: np.ndarray, ref: np.ndarray) -> float:
-    """Relative Frobenius error ||x - ref|| / ||ref||."""
+    """Relative Frobenius error ||x - ref||_F / ||ref||_F over all elements
+    (0 when both are zero, inf when only ref is)."""
+    x = np.asarray(x, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    num = math.sqrt(float(np.dot(x - ref, x - ref)))
+    den = math.sqrt(float(np.dot(ref, ref)))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else math.inf
+    return num / den
+
+
+def rel_fro_rows(x: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """``rel_fro`` of every row (last axis) on its own; rows where ref is zero
+    give 0 if x is zero there too, else inf."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
+    num = np.sqrt(((x - ref) ** 2).sum(axis=-1))
+    den = np.sqrt((ref ** 2).sum(axis=-1))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = num / den
+    return np.where(den > 0, r, np.where(num > 0, np.inf, 0.0))
 
 
 # ---------------------------------------------------------------------------

@@ -305,6 +305,154 @@ def test_cos_diff_metric_and_failure_signature():
     # a relative error e gives cos_diff ~ e^2/2, far under the page's fp8 bar at 1e-2
     y = x + 1e-2 * np.linalg.norm(x) / math.sqrt(x.size) * np.random.default_rng(1).standard_normal(x.shape)
     assert orc.cos_diff(x, y) < g["fp8_cos_diff_threshold"]
+    # orthogonal vectors are as far apart as a zero output; two zero arrays are equal
+    assert orc.cos_diff(np.array([1.0, 0.0]), np.array([0.0, 3.0])) == 1.0
+    assert orc.cos_diff(np.zeros(3), np.zeros(3)) == 0.0
+
+
+# ---------------------------------------------------------------------------
+# the comparison metrics against hand-computed values
+# ---------------------------------------------------------------------------
+
+def test_cos_diff_hand_computed():
+    # x = (3, 4), y = (3, 5): |x - y|^2 = 1, |x|^2 + |y|^2 = 25 + 34 = 59
+    assert orc.cos_diff(np.array([3.0, 4.0]), np.array([3.0, 5.0])) == pytest.approx(1.0 / 59.0, rel=1e-15)
+    # 2-D inputs are taken over all elements: |d|^2 = 2, norms 4 + 6
+    x = np.array([[1.0, 1.0], [1.0, 1.0]])
+    y = np.array([[1.0, 2.0], [0.0, 1.0]])
+    assert orc.cos_diff(x, y) == pytest.approx(2.0 / 10.0, rel=1e-15)
+
+
+def test_rel_fro_hand_computed():
+    # ref = (3, 4) has norm 5; x - ref = (0, 1): error 1/5 exactly
+    assert orc.rel_fro(np.array([3.0, 5.0]), np.array([3.0, 4.0])) == pytest.approx(0.2, rel=1e-15)
+    # matrices: Frobenius over all elements, not a spectral norm:
+    # diff = I (Frobenius sqrt 2, spectral 1); ref = diag(2, 0) (2 either way)
+    ref = np.array([[2.0, 0.0], [0.0, 0.0]])
+    assert orc.rel_fro(ref + np.eye(2), ref) == pytest.approx(math.sqrt(2.0) / 2.0, rel=1e-15)
+    assert orc.rel_fro(np.zeros(2), np.zeros(2)) == 0.0
+    assert orc.rel_fro(np.ones(2), np.zeros(2)) == math.inf
+    # per row: rows (3,4)->(3,5) and (1,0)->(0,0)
+    rows = orc.rel_fro_rows(np.array([[3.0, 5.0], [0.0, 0.0], [0.0, 0.0]]),
+                            np.array([[3.0, 4.0], [1.0, 0.0], [0.0, 0.0]]))
+    np.testing.assert_allclose(rows, [0.2, 1.0, 0.0], rtol=1e-15)
+
+
+def _rel_fro_squared(x, ref):
+    return float(np.linalg.norm((x - ref).ravel()) ** 2 / np.linalg.norm(ref.ravel()) ** 2)
+
+
+def _rel_fro_x_norm(x, ref):
+    return float(np.linalg.norm((x - ref).ravel()) / np.linalg.norm(np.asarray(x).ravel()))
+
+
+def _rel_fro_spectral(x, ref):
+    return float(np.linalg.norm(x - ref, 2) / np.linalg.norm(ref, 2))
+
+
+def _cos_diff_unsquared(x, y):
+    return float(np.linalg.norm(np.ravel(x - y)) / math.sqrt(float((x * x + y * y).sum())))
+
+
+@pytest.mark.parametrize("mutant", ["squared_ratio", "x_norm_denominator", "spectral_norm"])
+def test_rel_fro_mutants_fail_the_hand_computed_pins(monkeypatch, mutant):
+    fn = {"squared_ratio": _rel_fro_squared, "x_norm_denominator": _rel_fro_x_norm,
+          "spectral_norm": _rel_fro_spectral}[mutant]
+    monkeypatch.setattr(orc, "rel_fro", fn)
+    with pytest.raises(AssertionError):
+        test_rel_fro_hand_computed()
+
+
+def test_cos_diff_mutant_fails_the_hand_computed_pin(monkeypatch):
+    monkeypatch.setattr(orc, "cos_diff", _cos_diff_unsquared)
+    with pytest.raises(AssertionError):
+        test_cos_diff_hand_computed()
+
+
+# ---------------------------------------------------------------------------
+# the weighted mean of |v| (scale of the elementwise parity bound)
+# ---------------------------------------------------------------------------
+
+def test_attend_abs_closed_forms():
+    rng = np.random.default_rng(3)
+    keys = rng.standard_normal((9, 576))
+    q = rng.standard_normal((2, 576))
+    # one key: |v_0|
+    np.testing.assert_allclose(orc.attend_abs(q, keys[:1], 0.3), np.abs(keys[:1, :512]).repeat(2, 0),
+                               rtol=1e-15)
+    # uniform weights (scale 0): the plain mean of |v|
+    np.testing.assert_allclose(orc.attend_abs(q, keys, 0.0)[0], np.abs(keys[:, :512]).mean(0), rtol=1e-13)
+    # no key: zeros
+    assert (orc.attend_abs(q, keys[:0], 0.3) == 0).all()
+    # it bounds |out| elementwise and equals |out| when every v has one sign
+    o, _ = orc.attend(q, keys, 0.3)
+    a = orc.attend_abs(q, keys, 0.3)
+    assert (np.abs(o) <= a + 1e-12).all()
+    kp = np.abs(keys)
+    np.testing.assert_allclose(orc.attend(q, kp, 0.3)[0], orc.attend_abs(q, kp, 0.3), rtol=1e-13)
+
+
+def test_attend_abs_matches_loops():
+    inp = tiny(lens=(4, 7), seed=19)
+    wl = inp.wl
+    _, _, vabs = orc.mla_decode(inp.q_bits, inp.kv, inp.block_table, inp.seq_lens, wl.s_q,
+                                wl.softmax_scale, inp.kv_scale, wl.kv_dtype, wl.causal, with_abs=True)
+    for b in range(wl.batch):
+        L = int(inp.seq_lens[b])
+        keys = [[_bf16_scalar(x) for x in inp.kv[int(inp.block_table[b][t // wl.block_size])][t % wl.block_size]]
+                for t in range(L)]
+        for h in range(wl.heads):
+            q = [_bf16_scalar(x) for x in inp.q_bits[b][0][h]]
+            ex = [math.exp(wl.softmax_scale * sum(q[j] * keys[t][j] for j in range(576))) for t in range(L)]
+            for d in (0, 7, 300, 511):
+                want = sum(ex[t] * abs(keys[t][d]) for t in range(L)) / sum(ex)
+                assert vabs[b, 0, h, d] == pytest.approx(want, rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# block-table entries outside [0, num_blocks): those tokens hold no keys
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bad", [-1, 10 ** 6])
+@pytest.mark.parametrize("s_q,causal", [(1, True), (3, True), (2, False)])
+def test_invalid_page_keys_are_dropped(bad, s_q, causal):
+    inp = tiny(s_q=s_q, bs=8, lens=(13, 30), seed=31, causal=causal)
+    wl = inp.wl
+    bt = inp.block_table.copy()
+    bt[1, 1] = bad                       # tokens 8..15 of sequence 1
+    o, l = orc.mla_decode(inp.q_bits, inp.kv, bt, inp.seq_lens, s_q, wl.softmax_scale,
+                          inp.kv_scale, wl.kv_dtype, causal)
+    # brute force over the tokens whose page is valid, by loops
+    for b in range(wl.batch):
+        L = int(inp.seq_lens[b])
+        toks = [t for t in range(L) if 0 <= bt[b][t // 8] < inp.kv.shape[0]]
+        assert len(toks) == (L - 8 if b == 1 else L)
+        for i in range(s_q):
+            n = (L - s_q + 1 + i) if causal else L
+            vis = [t for t in toks if t < n]
+            for h in range(wl.heads):
+                q = [_bf16_scalar(x) for x in inp.q_bits[b][i][h]]
+                ks = [[_bf16_scalar(x) for x in inp.kv[int(bt[b][t // 8])][t % 8]] for t in vis]
+                ex = [math.exp(wl.softmax_scale * sum(q[j] * k[j] for j in range(576))) for k in ks]
+                assert l[b, i, h] == pytest.approx(math.log(sum(ex)), abs=1e-12)
+                for d in (0, 100, 511):
+                    want = sum(e * k[d] for e, k in zip(ex, ks)) / sum(ex)
+                    assert o[b, i, h, d] == pytest.approx(want, abs=1e-12)
+    # the other sequence is untouched
+    o0, l0 = orc.mla_decode(inp.q_bits, inp.kv, inp.block_table, inp.seq_lens, s_q, wl.softmax_scale,
+                            inp.kv_scale, wl.kv_dtype, causal)
+    np.testing.assert_array_equal(o[0], o0[0])
+    np.testing.assert_array_equal(l[0], l0[0])
+
+
+def test_sequence_with_only_invalid_pages_is_empty():
+    inp = tiny(bs=8, lens=(5, 12), seed=4)
+    wl = inp.wl
+    bt = inp.block_table.copy()
+    bt[0, :] = -7
+    o, l = orc.mla_decode(inp.q_bits, inp.kv, bt, inp.seq_lens, 1, wl.softmax_scale, inp.kv_scale,
+                          wl.kv_dtype, True)
+    assert (o[0] == 0).all() and np.isneginf(l[0]).all()
 
 
 def test_workload_matches_printed_kernel_test_case():
