@@ -46,6 +46,8 @@ extern "C" {
 #define MLA_MAX_SQ 512        /* query tokens per sequence, up to the decode threshold */
 #define MLA_MAX_BATCH 16384
 #define MLA_ABI_VERSION 1
+/* Size of the device array mla_decode_noalloc uses instead of a workspace. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
 
 typedef enum mla_status {
     MLA_OK = 0,
@@ -209,6 +211,33 @@ mla_status_t mla_absorb_q(const void* q_nope, const void* q_pe, const void* w_uk
                           int32_t tokens, int32_t heads, int32_t d_nope, void* stream);
 mla_status_t mla_absorb_out(const void* o, const void* w_uv, void* out, int32_t tokens,
                             int32_t heads, int32_t d_v, void* stream);
+
+/*
+ * mla_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same decode, with the workspace replaced by a fixed device array of
+ * MLA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on every GPU it
+ * runs on until the process ends. Nothing is allocated per call.
+ *
+ * When mla_decode_workspace_size() fits the array, the plan and the results
+ * are those of mla_decode; otherwise (long 128-head batches) the automatic
+ * split uses fewer partial slots (longer key chunks) so that it fits.
+ * Descriptions that do not fit even unsplit, or a split_keys override that
+ * does not fit, return MLA_ERR_WORKSPACE_TOO_SMALL and launch nothing.
+ *
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or host threads without ordering) race and must
+ * be serialised by the caller; calls on one stream are ordered. Every value
+ * the kernels read from the array is written earlier in the same call.
+ * Arguments (no workspace), ownership and errors as for mla_decode;
+ * MLA_ERR_HIP also when the array's device address cannot be obtained.
+ */
+mla_status_t mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                                const int32_t* seq_lens, int32_t s_q, float softmax_scale,
+                                float kv_scale, void* out, float* lse,
+                                const mla_decode_desc_t* desc, void* stream);
+/* MLA_NOALLOC_SCRATCH_BYTES, as compiled into the library. */
+size_t mla_decode_noalloc_scratch_bytes(void);
 
 const char* mla_status_string(mla_status_t status);
 int32_t mla_abi_version(void);

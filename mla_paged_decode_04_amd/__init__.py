@@ -13,7 +13,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["mla_decode", "mla_decode_plan", "mla_decode_with_plan",
+__all__ = ["mla_decode", "mla_decode_plan", "mla_decode_with_plan", "mla_decode_noalloc",
            "mla_plan_host", "mla_kv_append", "mla_absorb_q", "mla_absorb_out", "workspace_size",
            "library", "MlaError", "D_QK", "D_V", "LIB_PATH"]
 
@@ -68,6 +68,10 @@ def library() -> ctypes.CDLL:
     lib.mla_decode_fwd_only.restype = ctypes.c_int
     lib.mla_decode_with_plan.argtypes = [vp, vp, vp, vp, i32, f32, f32, vp, vp, pdesc, vp, sz, vp]
     lib.mla_decode_with_plan.restype = ctypes.c_int
+    lib.mla_decode_noalloc.argtypes = [vp, vp, vp, vp, i32, f32, f32, vp, vp, pdesc, vp]
+    lib.mla_decode_noalloc.restype = ctypes.c_int
+    lib.mla_decode_noalloc_scratch_bytes.argtypes = []
+    lib.mla_decode_noalloc_scratch_bytes.restype = sz
     lib.mla_decode_plan.argtypes = [vp, i32, pdesc, vp, sz, vp]
     lib.mla_decode_plan.restype = ctypes.c_int
     lib.mla_plan_host.argtypes = [vp, i32, pdesc, vp, i32, vp, vp]
@@ -214,6 +218,24 @@ def mla_decode_with_plan(q: torch.Tensor, kv_cache: torch.Tensor, block_table: t
     (no planner launch)."""
     return _decode_call("mla_decode_with_plan", q, kv_cache, block_table, seq_lens, softmax_scale,
                         kv_scale, causal, out, lse, workspace, split_keys, want_lse)
+
+
+def mla_decode_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                       seq_lens: torch.Tensor, softmax_scale: float, out: torch.Tensor,
+                       lse: Optional[torch.Tensor], kv_scale: float = 1.0, causal: bool = True,
+                       split_keys: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``mla_decode`` into caller-provided out / lse with the library's fixed
+    device scratch array instead of a workspace: the call allocates nothing."""
+    kv_cache, desc, out, lse = _prepare(q, kv_cache, block_table, seq_lens, causal, out, lse,
+                                        split_keys, False)
+    st = library().mla_decode_noalloc(
+        q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), q.shape[1],
+        float(softmax_scale), float(kv_scale), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, ctypes.byref(desc),
+        torch.cuda.current_stream(q.device).cuda_stream)
+    if st != 0:
+        raise MlaError(st, "mla_decode_noalloc")
+    return out, lse
 
 
 def mla_decode_plan(seq_lens: torch.Tensor, s_q: int, num_heads: int, block_size: int,

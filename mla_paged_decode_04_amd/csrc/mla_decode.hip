@@ -23,6 +23,7 @@
 //                          pairs with log-sum-exp weights
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 
 #include "mla_internal.h"
 
@@ -850,5 +851,84 @@ const char* mla_status_string(mla_status_t s) {
 }
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// decode without a caller workspace: plan, work items and split partials live
+// in a fixed device array of this library
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// One copy per GPU, held from the library's load until the process ends. In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// kernels get the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The device address of `scratch` on the current device (looked up once per
+// device), or nullptr if the lookup fails.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// A workspace layout that fits the scratch array: the regular one when it
+// fits (the plan is then the same as mla_decode's), else automatic splits
+// with as many partial slots as fit. Returns false if nothing fits.
+bool scratch_layout(int32_t s_q, const mla_decode_desc_t* desc, WsLayout* ws, int* slot_cap) {
+  const int mk = max_keys_of(desc);
+  *slot_cap = DEFAULT_SLOT_CAP;
+  *ws = ws_layout(desc->batch, s_q, desc->num_heads, mk, desc->split_keys);
+  if (ws->total <= MLA_NOALLOC_SCRATCH_BYTES) return true;
+  if (desc->split_keys != 0) return false;
+  const WsLayout none = ws_layout(desc->batch, s_q, desc->num_heads, mk, 0, 0);
+  if (none.total > MLA_NOALLOC_SCRATCH_BYTES) return false;
+  const size_t per_slot = (size_t)row_config(s_q * desc->num_heads).rgs * (4 + 4 + DV * 2);
+  int cap = static_cast<int>((MLA_NOALLOC_SCRATCH_BYTES - none.total) / per_slot);
+  // the three partial regions are each rounded up to 256 bytes
+  while (cap > 0 && ws_layout(desc->batch, s_q, desc->num_heads, mk, 0, cap).total > MLA_NOALLOC_SCRATCH_BYTES)
+    --cap;
+  *slot_cap = cap;
+  *ws = ws_layout(desc->batch, s_q, desc->num_heads, mk, 0, cap);
+  return ws->total <= MLA_NOALLOC_SCRATCH_BYTES;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_decode_noalloc_scratch_bytes(void) { return MLA_NOALLOC_SCRATCH_BYTES; }
+
+mla_status_t mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                                const int32_t* seq_lens, int32_t s_q, float softmax_scale,
+                                float kv_scale, void* out, float* lse,
+                                const mla_decode_desc_t* desc, void* stream) {
+  mla_status_t st = check_args(q, kv_cache, block_table, seq_lens, s_q, softmax_scale, kv_scale,
+                               out, lse, desc);
+  if (st != MLA_OK) return st;
+  WsLayout ws;
+  int slot_cap = DEFAULT_SLOT_CAP;
+  if (!scratch_layout(s_q, desc, &ws, &slot_cap)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (desc->batch == 0) return MLA_OK;
+  void* base = scratch_on_current_device();
+  if (base == nullptr) return MLA_ERR_HIP;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = launch_plan(seq_lens, s_q, desc, base, ws, hs, slot_cap);
+  if (st != MLA_OK) return st;
+  return launch_decode_kernel(q, kv_cache, block_table, seq_lens, s_q, softmax_scale, kv_scale, out,
+                              lse, desc, base, ws, hs, true);
+}
 
 }  // extern "C"

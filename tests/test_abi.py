@@ -290,3 +290,26 @@ def test_automatic_chunk_is_near_the_best_list_schedule(name):
                                                         split_keys=c)[0], 320)
                for c in range(256, 8192, 64))
     assert auto <= 1.03 * best, (auto, best)
+
+
+def test_noalloc_entry_checks_arguments_on_the_host():
+    """mla_decode_noalloc: argument errors come back before any device call
+    (no GPU here), an empty batch is a no-op, and a description whose plan
+    cannot fit the fixed 64 MiB array even unsplit is refused."""
+    lib = mla.library()
+    assert lib.mla_decode_noalloc_scratch_bytes() == 64 * 1024 * 1024
+
+    def call_na(d, s_q=1, ptrs=None, softmax_scale=0.07):
+        p = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, out=FAKE)
+        p.update(ptrs or {})
+        return lib.mla_decode_noalloc(p["q"], p["kv"], p["bt"], p["sl"], s_q, softmax_scale, 1.0,
+                                      p["out"], None, ctypes.byref(d), None)
+
+    assert call_na(desc(), ptrs={"q": 0}) == INVALID
+    assert call_na(desc(), ptrs={"out": FAKE + 2}) == INVALID
+    assert call_na(desc(), softmax_scale=float("nan")) == INVALID
+    assert call_na(desc(num_heads=129)) == UNSUPPORTED
+    assert call_na(desc(batch=0)) == OK
+    # a forced 64-key split of 128-row items over long contexts needs far more
+    # than 64 MiB of partials: refused
+    assert call_na(desc(batch=64, num_heads=128, max_blocks_per_seq=256, split_keys=64), s_q=4) == WS_SMALL
