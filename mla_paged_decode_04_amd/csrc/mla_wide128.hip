@@ -3,9 +3,10 @@
 // description) with 128 query rows per work item, 32 per wave, on gfx950's
 // 32x32x16 bf16 MFMA. A 32-row MFMA tile feeds each LDS byte of K or V to 32
 // rows (twice the 16-row tiles), and issues at full rate with one wave per
-// SIMD. fp8 e4m3fn caches ("[Attention] Blackwell FP8 MLA support with
-// CUTLASS_MLA backend", Test Plan) are widened to bf16 in registers, right
-// before each MFMA.
+// SIMD. With fp8 e4m3fn caches ("[Attention] Blackwell FP8 MLA support with
+// CUTLASS_MLA backend", Test Plan) the scores run on the 32x32x64 fp8 MFMA
+// against an exact two-term fp8 split of q, and V is widened to bf16 in
+// registers right before each PV MFMA.
 #include <type_traits>
 
 #include "mla_internal.h"
@@ -79,6 +80,59 @@ __device__ __forceinline__ void qk_next_v(f32x16_t& s, const bf16x8_t& a, const 
 }
 __device__ __forceinline__ void qk_done(f32x16_t& s) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
+}
+
+// fp8 caches: S^T on gfx950's 32x32x64 MFMA with both operands e4m3fn, the
+// keys' codes as stored and q split per row into q * 2^e = hi + lo (below).
+// Same chain rules as the bf16 forms; VALU reads of the result wait for the
+// 16 passes of the last MFMA (qk8_done).
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void qk8_first(f32x16_t& s, const i32x8_t& a, const i32x8_t& b) {
+  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk8_next(f32x16_t& s, const i32x8_t& a, const i32x8_t& b) {
+  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk8_first_v(f32x16_t& s, const i32x8_t& a, const i32x8_t& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk8_next_v(f32x16_t& s, const i32x8_t& a, const i32x8_t& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk8_done(f32x16_t& s) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
+}
+
+// Four float32 values x (|x| < 256) -> e4m3fn codes of hi = nearest(x) and
+// lo = nearest(x - hi), packed four to a dword. For x = q * 2^e with q a bf16
+// value (8 significant bits) the residual x - hi is a multiple of q's last
+// place with at most 4 significant bits, so lo is exact and hi + lo = x
+// whenever that place is at least e4m3fn's smallest step 2^-9 (elements down
+// to 2^-10 of a row maximum scaled to [128, 256); smaller ones lose bits
+// below 2^-18 of the row maximum).
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_fp8x4(float x0, float x1, float x2, float x3, uint32_t& hi,
+                                            uint32_t& lo) {
+  s16x2_t h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2_t{0, 0}, x0, x1, 1.0f, false);
+  h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x2, x3, 1.0f, true);
+  hi = __builtin_bit_cast(uint32_t, h);
+  const uint32_t d01 = fp8x2_to_bf16x2(hi, false), d23 = fp8x2_to_bf16x2(hi, true);   // exact
+  const float r0 = x0 - __builtin_bit_cast(float, d01 << 16);
+  const float r1 = x1 - __builtin_bit_cast(float, d01 & 0xFFFF0000u);
+  const float r2 = x2 - __builtin_bit_cast(float, d23 << 16);
+  const float r3 = x3 - __builtin_bit_cast(float, d23 & 0xFFFF0000u);
+  s16x2_t l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2_t{0, 0}, r0, r1, 1.0f, false);
+  l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, r2, r3, 1.0f, true);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// 8 bf16 (one uint4) times 2^e -> hi and lo codes, two dwords each.
+__device__ __forceinline__ void split_fp8x8(uint4 v, float mul, uint32_t* hi, uint32_t* lo) {
+  auto f = [](uint32_t w, bool upper) {
+    return __builtin_bit_cast(float, upper ? (w & 0xFFFF0000u) : (w << 16));
+  };
+  split_fp8x4(f(v.x, false) * mul, f(v.x, true) * mul, f(v.y, false) * mul, f(v.y, true) * mul, hi[0], lo[0]);
+  split_fp8x4(f(v.z, false) * mul, f(v.z, true) * mul, f(v.w, false) * mul, f(v.w, true) * mul, hi[1], lo[1]);
 }
 
 // LDS reads by 32-bit LDS byte address. The per-lane operand offsets are
@@ -184,7 +238,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
       vt0 = (4 * hi + j) * 128 + (((2 * g16 + (r >> 1)) ^ swz16(4 * hi + j)) << 4) + 8 * (r & 1);
     } else {
       dma_lane[0] = dma_lane[1] = (lane >> 2) * ROWB + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-      kb0 = n32 * 64 + ((hi ^ swz8(n32)) << 4);
+      kb0 = n32 * 64 + (((2 * hi) ^ swz8(n32)) << 4);
       const int jj = ig >> 1, q = ig & 1;
       const int key = 4 * hi + (jj & 3) + 8 * (jj >> 2);
       vt0 = key * 64 + ((g16 ^ swz8(key)) << 4) + 8 * q;
@@ -247,27 +301,89 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   // k-steps 32..35 (dims 512..575 either way) go to qrope: chunk 2(t - 32) + h
   // of row r at position (2(t - 32) + h) ^ swz16(r) of its 128 bytes. Each
   // wave writes and reads only its own rows.
-  constexpr int QREG = D / 16 - 4;
+  // bf16 caches: k-steps 0..31 in registers (qb), 32..35 in qrope.
+  // fp8 caches: the 64-dim blocks 0..7 as hi/lo e4m3fn operands in registers
+  // (q8h, q8l: lane (row n, half h) byte j is dim 64 blk + 32 h + j, the same
+  // bijection as the K operand read below; A and B of the 32x32x64 MFMA pair
+  // their bytes by lane half and byte), block 8 (the rope dims) in qrope as
+  // chunks 4 part + 2 h + (j >> 4), part 0 = hi, 1 = lo.
+  constexpr int QREG = F8 ? 1 : D / 16 - 4;
   bf16x8_t qb[QREG];
+  constexpr int Q8 = F8 ? 8 : 1;
+  i32x8_t q8h[Q8], q8l[Q8];
   const int qr_off = row_local * 128;
   const int qr_swz = swz16(row_local);
-  {
-    const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
+  const uint16_t* qrow_g = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
+  // fp8: row scale 2^qe puts the row's largest |q| in [128, 256); scores are
+  // then sums of products of exact e4m3fn values, and 2^-qe is folded into
+  // this row's score scale
+  float qmul = 1.f, scale_row = p.scale_log2;
+  if constexpr (!F8) {
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-      const int d = F8 ? 32 * (t >> 1) + 16 * hi + 8 * (t & 1) : 16 * t + 8 * hi;
-      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + d) : make_uint4(0, 0, 0, 0);
+      const int d = 16 * t + 8 * hi;
+      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow_g + d) : make_uint4(0, 0, 0, 0);
       if (t < QREG)
         qb[t] = __builtin_bit_cast(bf16x8_t, v);
       else
         *reinterpret_cast<uint4*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4)) = v;
     }
+  } else {
+    float qmax = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow_g + 64 * (c >> 2) + 32 * hi + 8 * (c & 3))
+                             : make_uint4(0, 0, 0, 0);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        qmax = fmaxf(qmax, fmaxf(fabsf(__builtin_bit_cast(float, w[i] << 16)),
+                                 fabsf(__builtin_bit_cast(float, w[i] & 0xFFFF0000u))));
+    }
+    qmax = halves_max(qmax);
+    const int qe = qmax > 0.f && qmax < INFINITY ? 8 - __builtin_amdgcn_frexp_expf(qmax) : 0;
+    qmul = __builtin_ldexpf(1.f, qe);
+    scale_row = p.scale_log2 * __builtin_ldexpf(1.f, -qe);
+#pragma unroll
+    for (int blk = 0; blk < 9; ++blk) {
+      uint32_t h8[8], l8[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow_g + 64 * blk + 32 * hi + 8 * c)
+                               : make_uint4(0, 0, 0, 0);
+        split_fp8x8(v, qmul, h8 + 2 * c, l8 + 2 * c);
+      }
+      if (blk < 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          q8h[blk < Q8 ? blk : 0][i] = static_cast<int>(h8[i]);
+          q8l[blk < Q8 ? blk : 0][i] = static_cast<int>(l8[i]);
+        }
+      } else {
+#pragma unroll
+        for (int part = 0; part < 2; ++part)
+#pragma unroll
+          for (int half16 = 0; half16 < 2; ++half16) {
+            const uint32_t* src = (part ? l8 : h8) + 4 * half16;
+            *reinterpret_cast<uint4*>(qrope + qr_off + (((4 * part + 2 * hi + half16) ^ qr_swz) << 4)) =
+                make_uint4(src[0], src[1], src[2], src[3]);
+          }
+      }
+    }
   }
   // q loads (and with them tile 0, issued before) complete here, so the
   // compiler places no wait for them inside the tile loop (it cannot see the
   // DMAs)
+  if constexpr (!F8) {
 #pragma unroll
-  for (int t = 0; t < QREG; ++t) asm volatile("" ::"v"(qb[t]));
+    for (int t = 0; t < QREG; ++t) asm volatile("" ::"v"(qb[t]));
+  } else {
+#pragma unroll
+    for (int t = 0; t < Q8; ++t)
+#pragma unroll
+      // per dword: a 256-bit operand would be an x86 register class in the host pass
+      for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(q8h[t][i]), "v"(q8l[t][i]));
+  }
   // tiles 1 and 2 go out once q and tile 0 are resident
 #pragma unroll
   for (int k = 1; k < 3; ++k)
@@ -279,14 +395,34 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   // The slow loop reads the register part of q from memory at every use, so
   // the q registers die at the fast loop's exit instead of being saved to
   // scratch there for a loop that rarely runs.
-  const uint16_t* qrow_g = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
   auto q_operand_mem = [&](int t) -> bf16x8_t {
     if (t < QREG) {
-      const int d = F8 ? 32 * (t >> 1) + 16 * hi + 8 * (t & 1) : 16 * t + 8 * hi;
+      const int d = 16 * t + 8 * hi;
       const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow_g + d) : make_uint4(0, 0, 0, 0);
       return __builtin_bit_cast(bf16x8_t, v);
     }
     return q_operand(t);
+  };
+  // fp8 operands of block blk: registers (blocks 0..7 in the fast loop),
+  // recomputed from memory (blocks 0..7 in the rescaling loop), or qrope
+  auto q8_rope = [&](int part) -> i32x8_t {
+    const uint4 a = *reinterpret_cast<const uint4*>(qrope + qr_off + (((4 * part + 2 * hi) ^ qr_swz) << 4));
+    const uint4 c = *reinterpret_cast<const uint4*>(qrope + qr_off + (((4 * part + 2 * hi + 1) ^ qr_swz) << 4));
+    return i32x8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z, (int)c.w};
+  };
+  auto q8_mem = [&](int blk, i32x8_t& h, i32x8_t& l) {
+    uint32_t h8[8], l8[8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow_g + 64 * blk + 32 * hi + 8 * c)
+                             : make_uint4(0, 0, 0, 0);
+      split_fp8x8(v, qmul, h8 + 2 * c, l8 + 2 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      h[i] = static_cast<int>(h8[i]);
+      l[i] = static_cast<int>(l8[i]);
+    }
   };
 
   f32x16_t o[DV / 32];
@@ -370,27 +506,44 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
         }
       }
     } else {
-      auto kaddr = [&](int u) { return (kbase ^ ((u & 1) << 5)) + (u >> 1) * X_GSTRIDE + 2048 * half; };
-      constexpr int AH = (QK_AHEAD + 1) / 2;   // reads cover two k-steps each
-      u32x4_t kr[AH];
+      // K operand of 64-dim block blk: key 32 half + n32, chunks 2h and
+      // 2h + 1 (dims 64 blk + 32 h .. + 31), no conversion
+      auto kaddr = [&](int blk) { return kbase + blk * X_GSTRIDE + 2048 * half; };
+      auto kread = [&](int blk) -> i32x8_t {
+        const u32x4_t a = lds_u128(kaddr(blk)), c = lds_u128(kaddr(blk) ^ 16);
+        return i32x8_t{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+      };
+      i32x8_t kr = kread(0);
 #pragma unroll
-      for (int u = 0; u < AH; ++u) kr[u] = lds_u128(kaddr(u));
-#pragma unroll
-      for (int u = 0; u < D / 32; ++u) {
-        const u32x4_t v = kr[u % AH];
-        if (u + AH < D / 32) kr[u % AH] = lds_u128(kaddr(u + AH));
-        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(v[0], v[1]));
-        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(v[2], v[3]));
-        const bf16x8_t qv0 = SLOW ? q_operand_mem(2 * u) : q_operand(2 * u);
-        const bf16x8_t qv1 = SLOW ? q_operand_mem(2 * u + 1) : q_operand(2 * u + 1);
-        if (u == 0)
-          qk_first_v(sacc, a0, qv0);
-        else
-          qk_next_v(sacc, a0, qv0);
-        qk_next_v(sacc, a1, qv1);
+      for (int blk = 0; blk < 9; ++blk) {
+        const i32x8_t a = kr;
+        if (blk + 1 < 9) kr = kread(blk + 1);
+        if (blk == 8) {
+          const i32x8_t h = q8_rope(0), l = q8_rope(1);
+          qk8_next(sacc, a, h);
+          qk8_next(sacc, a, l);
+        } else if constexpr (SLOW) {
+          // operands recomputed with VALU code: the forms with wait states
+          i32x8_t h, l;
+          q8_mem(blk, h, l);
+          if (blk == 0)
+            qk8_first_v(sacc, a, h);
+          else
+            qk8_next_v(sacc, a, h);
+          qk8_next_v(sacc, a, l);
+        } else {
+          if (blk == 0)
+            qk8_first(sacc, a, q8h[blk]);
+          else
+            qk8_next(sacc, a, q8h[blk]);
+          qk8_next(sacc, a, q8l[blk]);
+        }
       }
     }
-    qk_done(sacc);
+    if constexpr (F8)
+      qk8_done(sacc);
+    else
+      qk_done(sacc);
 
     // ---- online softmax on the raw scores (scale folded into max and FMA) ----
     float x[16];
@@ -406,7 +559,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
     float tmax = x[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, x[e]);
-    tmax = halves_max(tmax) * p.scale_log2;
+    tmax = halves_max(tmax) * scale_row;
     if constexpr (!SLOW) {
       if (m_run == -INFINITY) m_run = tmax;   // o and l of this row are still zero
       if (__builtin_amdgcn_ballot_w64(tmax > m_run + BIG_SLACK)) return false;
@@ -430,7 +583,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
     float pe[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], p.scale_log2, neg_m));
+      pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], scale_row, neg_m));
       l_run += pe[e];
     }
     bf16x8_t pb[2];
