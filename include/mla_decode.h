@@ -113,8 +113,9 @@ size_t mla_decode_workspace_size(int32_t s_q, const mla_decode_desc_t* desc);
  * [0] work items, [1] chunk keys, [2] partial slots, [3] flags (bit 0: a
  * seq_len was clamped; bit 1: the plan did not fit the workspace bounds, which
  * the bounds exclude, and nothing was computed; bit 2: a block-table entry in
- * range was outside [0, num_blocks)); at byte 256 the work items, 8 x int32
- * each:
+ * range was outside [0, num_blocks); bit 3: a work item or split of the plan
+ * in the workspace did not fit this call's description, and was skipped (see
+ * mla_decode_with_plan)); at byte 256 the work items, 8 x int32 each:
  * {b, row_group, key_begin, key_end, partial_slot (-1 = written directly), 0, 0, 0}.
  */
 mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
@@ -135,6 +136,12 @@ mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* bloc
  * may have used it since. q, kv_cache, block_table (same lengths), out and
  * lse may differ from the planning call. Flag bit 2 accumulates over the calls
  * that reuse one plan. Arguments, ownership and errors as for mla_decode.
+ * A plan that does not match (a stale or foreign workspace) is not trusted:
+ * every work item and split is checked against this call's description
+ * before any address is formed from it, and one that does not fit is skipped
+ * and sets flag bit 3; the rows it would have written are then left as they
+ * were (so out and lse are incomplete: a set bit 3 means the call's results
+ * must not be used).
  */
 mla_status_t mla_decode_with_plan(const void* q, const void* kv_cache, const int32_t* block_table,
                                   const int32_t* seq_lens, int32_t s_q, float softmax_scale,

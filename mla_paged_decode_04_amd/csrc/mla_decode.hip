@@ -477,7 +477,8 @@ struct CombineParams {
   const int32_t* part_scale;
   uint16_t* out;
   float* lse;
-  int rows, rgs, nrg, n_pairs;
+  int32_t* flags;   // header word 3: FLAG_BAD_ITEM for a pair whose slots do not fit
+  int rows, rgs, nrg, n_pairs, max_slots;
 };
 
 // Grid (pair, chunk): thread (row, 8-dim slice) of one (sequence, row group)
@@ -491,6 +492,10 @@ __global__ __launch_bounds__(NTHREADS) void mla_combine_kernel(CombineParams p) 
   const int first = p.pairs[2 * pair];
   const int n = p.pairs[2 * pair + 1];
   if (first < 0 || n <= 1) return;
+  if ((long long)first + n > p.max_slots) {   // a stale plan (see item_in_range)
+    flag_bad_item(p.flags);
+    return;
+  }
   const int idx = blockIdx.y * NTHREADS + threadIdx.x;
   const int rr = idx / COMBINE_SLICES;
   const int d0 = (idx % COMBINE_SLICES) * 8;
@@ -571,6 +576,9 @@ mla_status_t check_desc(int32_t s_q, const mla_decode_desc_t* d) {
   if (d->split_keys % NT != 0) return MLA_ERR_INVALID_ARGUMENT;
   long long max_keys = (long long)d->max_blocks_per_seq * d->block_size;
   if (max_keys > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
+  // the plan's item and slot counts are int32 and size the decode grid
+  if (max_items_bound(d->batch, s_q * d->num_heads, static_cast<int>(max_keys), d->split_keys) > (1LL << 30))
+    return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 
@@ -697,6 +705,9 @@ mla_status_t launch_decode_kernel(const void* q, const void* kv_cache,
   fp.max_keys = max_keys_of(desc);
   fp.causal = desc->causal;
   fp.num_blocks = desc->num_blocks;
+  fp.batch = desc->batch;
+  fp.max_items = static_cast<int>(ws.max_items);
+  fp.max_slots = static_cast<int>(ws.max_slots);
   fp.scale_log2 = softmax_scale * kv_scale * LOG2E;
   fp.out_scale = kv_scale;
   // a multiple of 8 workgroups: the wide kernel deals items out per XCD
@@ -716,6 +727,8 @@ mla_status_t launch_decode_kernel(const void* q, const void* kv_cache,
   cp.rgs = rc.rgs;
   cp.nrg = rc.nrg;
   cp.n_pairs = desc->batch * rc.nrg;
+  cp.flags = fp.flags;
+  cp.max_slots = fp.max_slots;
   const unsigned chunks = (unsigned)((rc.rgs * COMBINE_SLICES + NTHREADS - 1) / NTHREADS);
   hipLaunchKernelGGL(mla_combine_kernel, dim3(cp.n_pairs, chunks), dim3(NTHREADS), 0, hs, cp);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;

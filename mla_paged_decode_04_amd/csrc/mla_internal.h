@@ -140,6 +140,7 @@ __device__ __forceinline__ int partial_exponent(float amax) {
 constexpr int FLAG_SEQ_LEN_CLAMPED = 1;   // a seq_len was outside [0, max_blocks * bs]
 constexpr int FLAG_PLAN_OVERFLOW = 2;     // the plan did not fit the workspace bounds
 constexpr int FLAG_BAD_PAGE = 4;          // a block-table entry in range was outside [0, num_blocks)
+constexpr int FLAG_BAD_ITEM = 8;          // the workspace plan did not fit this call: items skipped
 
 // Record (once per wave) that a tile's page id was outside [0, num_blocks):
 // the tile was read from page 0, zeroed, and its keys masked out. Called after
@@ -147,6 +148,12 @@ constexpr int FLAG_BAD_PAGE = 4;          // a block-table entry in range was ou
 __device__ __forceinline__ void flag_bad_page(int32_t* flags, bool bad) {
   if (bad && (threadIdx.x & 63) == 0)
     __hip_atomic_fetch_or(flags, FLAG_BAD_PAGE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct FwdParams;
+__device__ __forceinline__ void flag_bad_item(int32_t* flags) {
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_or(flags, FLAG_BAD_ITEM, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 struct FwdParams {
@@ -163,9 +170,21 @@ struct FwdParams {
   float* part_lse;     // base-2 lse per partial row
   int32_t* part_scale; // per partial row
   int heads, s_q, rows, bs, max_blocks, max_keys, causal, num_blocks;
+  int batch, max_items, max_slots;   // bounds of the plan this call can run
   float scale_log2;   // softmax_scale * kv_scale * log2(e)
   float out_scale;    // kv_scale
 };
+
+// A work item is checked before any index is formed from it: the plan in the
+// workspace comes from an earlier call when it is reused (mla_decode_with_plan,
+// mla_decode_fwd_only), and a stale or foreign plan must not send the kernels
+// outside their buffers. An item that fails is skipped and FLAG_BAD_ITEM set.
+// (Items start on 64-key boundaries, which the tile addressing relies on.)
+__device__ __forceinline__ bool item_in_range(const FwdParams& p, int rgs, int b, int rg, int t0, int t1,
+                                              int slot) {
+  return b >= 0 && b < p.batch && rg >= 0 && rg * rgs < p.rows && t0 >= 0 && (t0 & (NT - 1)) == 0 &&
+         t0 <= t1 && t1 <= p.max_keys && slot < p.max_slots;
+}
 
 // Decode-kernel launchers (one per translation unit); the grid is one
 // workgroup per potential work item.

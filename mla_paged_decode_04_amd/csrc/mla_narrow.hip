@@ -161,7 +161,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
   // even for a workgroup that then finds it has no item.
   const int item_id = blockIdx.x;
   const int32_t* it = p.items + (size_t)item_id * ITEM_INTS;
-  const int n_items = p.header[0];
+  const int n_items = min(p.header[0], p.max_items);
   // work-item fields are uniform: keep them (and all tile addressing derived
   // from them) in SGPRs, so no vector load ever enters the DMA vmcnt queue
   const int b = __builtin_amdgcn_readfirstlane(it[0]);
@@ -173,6 +173,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
   asm volatile("" ::"s"(n_items), "s"(b), "s"(t0), "s"(t1), "s"(slot), "s"(p.bs), "s"(p.max_blocks),
                "s"(p.block_table), "s"(p.seq_lens));
   if (item_id >= n_items) return;
+  if (!item_in_range(p, 16, b, 0, t0, t1, slot)) {
+    flag_bad_item(p.flags);
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
   // XCD-aware item order: consecutive workgroups go to different XCDs, so
   // hand each XCD a contiguous run of items (the row groups and chunks of one
   // sequence then share that XCD's L2). The grid is a multiple of 8.
-  const int n_items = p.header[0];
+  const int n_items = min(p.header[0], p.max_items);
   const int per_xcd = (n_items + 7) >> 3;
   const int xw = blockIdx.x;
   if ((xw >> 3) >= per_xcd) return;
@@ -77,6 +77,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
   const int t0 = __builtin_amdgcn_readfirstlane(it[2]);
   const int t1 = __builtin_amdgcn_readfirstlane(it[3]);
   const int slot = __builtin_amdgcn_readfirstlane(it[4]);
+  if (!item_in_range(p, RGS, b, rg, t0, t1, slot)) {
+    flag_bad_item(p.flags);
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);

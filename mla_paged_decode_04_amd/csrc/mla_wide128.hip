@@ -30,7 +30,7 @@ constexpr int X_STEP = 32;        // keys per compute step (one 32x32 S block)
 #define QK_AHEAD 4                // k-steps whose K reads are issued ahead
 #endif
 #ifndef PV_AHEAD
-#define PV_AHEAD 4                // PV MFMAs whose V^T reads are issued ahead
+#define PV_AHEAD 8                // PV MFMAs whose V^T reads are issued ahead
 #endif
 
 // bf16 slot layout: [9 column groups][32 keys][8 x 16-byte chunks], chunk c of
@@ -56,6 +56,18 @@ __device__ __forceinline__ float halves_sum(float v) {
   float y = v;
   asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(v), "+v"(y));
   return v + y;
+}
+
+// The lane id, read afresh where it is used: an opaque asm the compiler can
+// neither merge with other reads nor hoist out of the loop. Lane constants
+// derived from it are recomputed at each use (a few VALU instructions that
+// run under the MFMAs) rather than kept live across the tile loop, where the
+// register pressure would send them to scratch, and the wait for a scratch
+// reload would also wait for every tile transfer in flight.
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
 }
 
 // The S^T accumulation chain is issued from inline asm so that S lives in
@@ -176,7 +188,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
 
   // XCD-aware item order (consecutive workgroups go to different XCDs): each
   // XCD takes a contiguous run of items. The grid is a multiple of 8.
-  const int n_items = p.header[0];
+  const int n_items = min(p.header[0], p.max_items);
   const int per_xcd = (n_items + 7) >> 3;
   const int xw = blockIdx.x;
   if ((xw >> 3) >= per_xcd) return;
@@ -188,6 +200,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   const int t0 = __builtin_amdgcn_readfirstlane(it[2]);
   const int t1 = __builtin_amdgcn_readfirstlane(it[3]);
   const int slot = __builtin_amdgcn_readfirstlane(it[4]);
+  if (!item_in_range(p, X_RGS, b, rg, t0, t1, slot)) {
+    flag_bad_item(p.flags);
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -211,39 +227,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   }
 
   // ---- lane constants (byte offsets) ----
-  // DMA: lane l of transfer n lands at slot byte n * 1024 + 16 l. bf16:
-  // column group n >> 2, key 8(n & 3) + (l >> 3), position l & 7; fp8: column
-  // group n >> 2, key 16(n & 3) + (l >> 2), position l & 3. The lane fetches
-  // the global chunk that belongs at that position.
-  uint32_t dma_lane[2];
   // K operand (key n32), bf16 k-step t: (slot + kb0) ^ ((t & 3) << 5), plus
   // (t >> 2) * X_GSTRIDE; fp8 k-step pair u: (slot + kb0) ^ ((u & 1) << 5),
   // plus (u >> 1) * X_GSTRIDE + 2048 * (32-key half of the slot)
-  uint32_t kb0;
+  // (kb0, computed at each use from a fresh lane id)
+  auto kb0_of = [](int ln) -> uint32_t {
+    const int n = ln & 31, h = (ln >> 5) & 1;
+    if constexpr (!F8)
+      return n * 128 + ((h ^ swz16(n)) << 4);
+    else
+      return n * 64 + (((2 * h) ^ swz8(n)) << 4);
+  };
   // V^T operand, bf16 dim block db, 16-key step s, 4-key read x:
   // (slot + vt0) ^ (64 (db & 1) + 32 x), plus (db >> 1) * X_GSTRIDE + 2048 s
   // + 1024 x; fp8: (slot + vt0) ^ (32 (db & 1)), plus (db >> 1) * X_GSTRIDE
-  // + 2048 * half + 1024 s
-  uint32_t vt0;
-  {
-    const int g16 = (lane >> 4) & 1, ig = lane & 15;
+  // + 2048 * half + 1024 s (computed at each use from a fresh lane id)
+  auto vt0_of = [](int ln) -> uint32_t {
+    const int g16 = (ln >> 4) & 1, ig = ln & 15, h = (ln >> 5) & 1;
     if constexpr (!F8) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int key = 8 * h + (lane >> 3);   // key bits 1..3 as in transfer parity h
-        dma_lane[h] = (lane >> 3) * ROWB + (((lane & 7) ^ swz16(key)) << 4);
-      }
-      kb0 = n32 * 128 + ((hi ^ swz16(n32)) << 4);
       const int j = ig >> 2, r = ig & 3;
-      vt0 = (4 * hi + j) * 128 + (((2 * g16 + (r >> 1)) ^ swz16(4 * hi + j)) << 4) + 8 * (r & 1);
+      return (4 * h + j) * 128 + (((2 * g16 + (r >> 1)) ^ swz16(4 * h + j)) << 4) + 8 * (r & 1);
     } else {
-      dma_lane[0] = dma_lane[1] = (lane >> 2) * ROWB + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-      kb0 = n32 * 64 + (((2 * hi) ^ swz8(n32)) << 4);
       const int jj = ig >> 1, q = ig & 1;
-      const int key = 4 * hi + (jj & 3) + 8 * (jj >> 2);
-      vt0 = key * 64 + ((g16 ^ swz8(key)) << 4) + 8 * q;
+      const int key = 4 * h + (jj & 3) + 8 * (jj >> 2);
+      return key * 64 + ((g16 ^ swz8(key)) << 4) + 8 * q;
     }
-  }
+  };
 
   typedef const __attribute__((address_space(4))) int32_t const_i32;
   const_i32* bt = (const_i32*)(p.block_table + (size_t)b * p.max_blocks);
@@ -256,12 +265,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   // Issue this wave's X_NDMA transfers of slot-tile j (exactly X_NDMA VMEM
   // instructions; the vmcnt arithmetic relies on it). A tile never crosses a
   // page: items start on 64-key boundaries and pages hold 64 or 128 keys.
+  // Lane l of transfer n lands at slot byte n * 1024 + 16 l. bf16: column
+  // group n >> 2, key 8(n & 3) + (l >> 3), position l & 7; fp8: column group
+  // n >> 2, key 16(n & 3) + (l >> 2), position l & 3. The lane fetches the
+  // global chunk that belongs at that position.
   auto issue = [&](int j) {
     const int ts = t0 + KT * j;
     int page = bt[ts >> bsh];
     if (page < 0 || page >= p.num_blocks) page = 0;
     const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts & (p.bs - 1))) * ROWB;
     const uint32_t l0 = lds_addr(smem + (j & 3) * X_TILE);
+    const int ln = fresh_lane();
+    uint32_t dma_lane[2];
+    if constexpr (!F8) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int key = 8 * h + (ln >> 3);   // key bits 1..3 as in transfer parity h
+        dma_lane[h] = (ln >> 3) * ROWB + (((ln & 7) ^ swz16(key)) << 4);
+      }
+    } else {
+      dma_lane[0] = dma_lane[1] = (ln >> 2) * ROWB + (((ln & 3) ^ ((ln >> 4) & 3)) << 4);
+    }
     auto one = [&](int i, auto nt_tag) {
       const int n = w * X_NDMA + i;
       const char* g = F8 ? src + (n & 3) * 16 * ROWB + (n >> 2) * 64 : src + (n & 3) * 8 * ROWB + (n >> 2) * 128;
@@ -287,12 +311,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
     if (page < 0 || page >= p.num_blocks) return -1;
     return min(KT, t1 - ts);
   };
-  bool bad_page = false, tile_bad = false;
+  bool bad_page = false;
 
   // Tile 0 is requested before q is loaded, so its latency overlaps the q
   // loads (the compiler's own wait for q below also covers it: it was issued
-  // first); tiles 1 and 2 go out once q is resident, so that wait does not
-  // include them while every workgroup starts at once.
+  // first); tile 1 goes out once q is resident, so that wait does not include
+  // it while every workgroup starts at once.
   if (ntiles > 0) issue(0);
 
   // Q^T operand: k-step t holds dims 16t + 8h .. +7 (bf16), or for fp8 (whose
@@ -384,10 +408,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
       // per dword: a 256-bit operand would be an x86 register class in the host pass
       for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(q8h[t][i]), "v"(q8l[t][i]));
   }
-  // tiles 1 and 2 go out once q and tile 0 are resident
-#pragma unroll
-  for (int k = 1; k < 3; ++k)
-    if (k < ntiles) issue(k);
+  // tile 1 goes out once q and tile 0 are resident
+  if (ntiles > 1) issue(1);
   auto q_operand = [&](int t) -> bf16x8_t {
     if (t < QREG) return qb[t];
     return *reinterpret_cast<const bf16x8_t*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4));
@@ -433,53 +455,58 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   float m_run = -INFINITY, l_run = 0.f;
 
 
-  // Make slot-tile j resident for every wave: wait for this wave's transfers,
-  // zero its slots of keys past the end, barrier (tile j complete everywhere;
-  // tile j - 1 consumed by every wave), then issue tile j + 3 into the slot
-  // of tile j - 1.
-  auto prepare = [&](int j) -> const char* {
+  // The ring runs two tiles ahead. prepare(j) makes tile j resident for
+  // every wave (wait for this wave's transfers, zero its slots of keys past
+  // the end, barrier), then issues tile j + 2 into the slot of tile j - 2,
+  // which every wave has finished with once it is past the barrier: while
+  // step k's PV reads tile(k) and step k + 1's QK reads tile(k + 1), the two
+  // tiles after them are in flight. Bit (j & 3) of bad_slots records whether
+  // tile j's page id was out of range.
+  int bad_slots = 0;
+  auto prepare = [&](int j) {
     mem_fence_compiler();
-    const int ahead = min(2, ntiles - 1 - j);
-    if (ahead >= 2)
-      wait_vmcnt<2 * X_NDMA>();
-    else if (ahead == 1)
+    if (j + 1 < ntiles)
       wait_vmcnt<X_NDMA>();
     else
       wait_vmcnt<0>();
     mem_fence_compiler();
-    char* cur = smem + (j & 3) * X_TILE;
+    char* t = smem + (j & 3) * X_TILE;
     const int nv = valid_keys(j);
-    tile_bad = nv < 0;
-    bad_page |= tile_bad;
+    const bool bad = nv < 0;
+    bad_page |= bad;
+    bad_slots = (bad_slots & ~(1 << (j & 3))) | (bad ? 1 << (j & 3) : 0);
     if (nv < KT) {
-      const int lk = F8 ? (lane >> 2) : (lane >> 3);   // key within the transfer
+      const int ln = fresh_lane();
+      const int lk = F8 ? (ln >> 2) : (ln >> 3);   // key within the transfer
 #pragma unroll
       for (int i = 0; i < X_NDMA; ++i) {
         const int n = w * X_NDMA + i;
         if (lk >= nv - (F8 ? 16 : 8) * (n & 3))
-          *reinterpret_cast<uint4*>(cur + n * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+          *reinterpret_cast<uint4*>(t + n * 1024 + ln * 16) = make_uint4(0, 0, 0, 0);
       }
     }
     __syncthreads();
-    if (j + 3 < ntiles) issue(j + 3);
-    return cur;
+    if (j + 2 < ntiles) issue(j + 2);
+  };
+  auto tile_of = [&](int k) -> const char* { return smem + ((F8 ? k >> 1 : k) & 3) * X_TILE; };
+  // Element e of step k's scores (C layout) is a visible key iff
+  // 8(e >> 2) + (e & 3) < rel_of(k); a tile whose page id was out of range
+  // has none.
+  auto rel_of = [&](int k) -> int {
+    const int j = F8 ? k >> 1 : k;
+    return (bad_slots >> (j & 3)) & 1 ? -64 : limit - (t0 + X_STEP * k) - 4 * hi;
   };
 
-  // One 32-key step k (slot-tile cur). The fast variant never touches the
-  // accumulators with VALU code and returns false (before consuming the
-  // step) if a row's max jumped more than BIG_SLACK above its reference.
-  auto compute = [&](const char* cur, int k, auto slow_tag) -> bool {
-    constexpr bool SLOW = decltype(slow_tag)::value;
-    if (!wave_active) return true;
-    const int ts = t0 + X_STEP * k;
-    const int half = F8 ? (k & 1) : 0;   // fp8: which 32 keys of the 64-key slot
-
-    // ---- S^T: 32 keys x this wave's 32 rows ----
-    // The K reads are software-pipelined QK_AHEAD k-steps ahead by hand: the
-    // asm MFMAs look cheap to the scheduler, which would otherwise issue each
-    // read just before its use and expose the LDS latency on every k-step.
-    f32x16_t sacc;
-    const uint32_t kbase = lds_addr(cur) + kb0;
+  // S^T of step k (32 keys x this wave's 32 rows) from tile `tile`, with the
+  // operands that need no wait states (q from registers or qrope, K from
+  // LDS). between(g) runs after the MFMAs of each of the 9 groups of 64 dims:
+  // a wave issues in order and an MFMA occupies the matrix core for 32
+  // (bf16) or 64 (fp8) cycles, so VALU work placed there executes meanwhile.
+  // The K reads are software-pipelined by hand: the asm MFMAs look cheap to
+  // the scheduler, which would otherwise issue each read just before its use
+  // and expose the LDS latency every time.
+  auto qk = [&](const char* tile, int k, f32x16_t& sacc, auto&& between) {
+    const uint32_t kbase = lds_addr(tile) + kb0_of(fresh_lane());
     if constexpr (!F8) {
       auto kaddr = [&](int t) { return (kbase ^ ((t & 3) << 5)) + (t >> 2) * X_GSTRIDE; };
       bf16x8_t kr[QK_AHEAD];
@@ -489,26 +516,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
       for (int t = 0; t < D / 16; ++t) {
         const bf16x8_t a = kr[t % QK_AHEAD];
         if (t + QK_AHEAD < D / 16) kr[t % QK_AHEAD] = lds_b128(kaddr(t + QK_AHEAD));
-        // the rescaling loop's q operand comes through a VALU select
-        // (masked rows), so it takes the forms with the wait states
-        if constexpr (SLOW) {
-          const bf16x8_t qv = q_operand_mem(t);
-          if (t == 0)
-            qk_first_v(sacc, a, qv);
-          else
-            qk_next_v(sacc, a, qv);
-        } else {
-          const bf16x8_t qv = q_operand(t);
-          if (t == 0)
-            qk_first(sacc, a, qv);
-          else
-            qk_next(sacc, a, qv);
+        if (t == 0)
+          qk_first(sacc, a, q_operand(t));
+        else
+          qk_next(sacc, a, q_operand(t));
+        if ((t & 3) == 3) {
+          between(t >> 2);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
       // K operand of 64-dim block blk: key 32 half + n32, chunks 2h and
-      // 2h + 1 (dims 64 blk + 32 h .. + 31), no conversion
-      auto kaddr = [&](int blk) { return kbase + blk * X_GSTRIDE + 2048 * half; };
+      // 2h + 1 (dims 64 blk + 32 h .. + 31), as stored
+      auto kaddr = [&](int blk) { return kbase + blk * X_GSTRIDE + 2048 * (k & 1); };
       auto kread = [&](int blk) -> i32x8_t {
         const u32x4_t a = lds_u128(kaddr(blk)), c = lds_u128(kaddr(blk) ^ 16);
         return i32x8_t{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
@@ -519,18 +539,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
         const i32x8_t a = kr;
         if (blk + 1 < 9) kr = kread(blk + 1);
         if (blk == 8) {
-          const i32x8_t h = q8_rope(0), l = q8_rope(1);
-          qk8_next(sacc, a, h);
-          qk8_next(sacc, a, l);
-        } else if constexpr (SLOW) {
-          // operands recomputed with VALU code: the forms with wait states
-          i32x8_t h, l;
-          q8_mem(blk, h, l);
-          if (blk == 0)
-            qk8_first_v(sacc, a, h);
-          else
-            qk8_next_v(sacc, a, h);
-          qk8_next_v(sacc, a, l);
+          qk8_next(sacc, a, q8_rope(0));
+          qk8_next(sacc, a, q8_rope(1));
         } else {
           if (blk == 0)
             qk8_first(sacc, a, q8h[blk]);
@@ -538,114 +548,243 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
             qk8_next(sacc, a, q8h[blk]);
           qk8_next(sacc, a, q8l[blk]);
         }
+        between(blk);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  auto qk_wait = [&](f32x16_t& sacc) {
     if constexpr (F8)
       qk8_done(sacc);
     else
       qk_done(sacc);
-
-    // ---- online softmax on the raw scores (scale folded into max and FMA) ----
-    float x[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) x[e] = sacc[e];
-    // a step that reaches a row's limit, or whose page id was out of range
-    if (tile_bad || __builtin_amdgcn_ballot_w64(ts + X_STEP > limit)) {
-      // element e is visible iff 8(e >> 2) + (e & 3) < rel
-      const int rel = tile_bad ? -64 : limit - ts - 4 * hi;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = 8 * (e >> 2) + (e & 3) < rel ? x[e] : -INFINITY;
-    }
-    float tmax = x[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, x[e]);
-    tmax = halves_max(tmax) * scale_row;
-    if constexpr (!SLOW) {
-      if (m_run == -INFINITY) m_run = tmax;   // o and l of this row are still zero
-      if (__builtin_amdgcn_ballot_w64(tmax > m_run + BIG_SLACK)) return false;
-    } else {
-      // unconditional (alpha = 1 for rows whose max did not move): a
-      // conditional rescale merges two versions of O and makes the compiler
-      // hold all of O in VGPRs; one block at a time needs 16 temporaries
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);   // m_run = -inf gives 0
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < DV / 32; ++d) {
-        o[d] *= alpha;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // rows without any key so far keep m = -inf: a finite stand-in makes
-    // their masked scores give exp2(-inf) = 0, never NaN
-    const float neg_m = -fmaxf(m_run, -1e30f);
-    float pe[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], scale_row, neg_m));
-      l_run += pe[e];
-    }
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      pb[s] = __builtin_bit_cast(
-          bf16x8_t, make_uint4(pack_bf16x2(pe[8 * s], pe[8 * s + 1]), pack_bf16x2(pe[8 * s + 2], pe[8 * s + 3]),
-                               pack_bf16x2(pe[8 * s + 4], pe[8 * s + 5]), pack_bf16x2(pe[8 * s + 6], pe[8 * s + 7])));
-
-    // keep the V^T reads of the PV loop out of the softmax code above (their
-    // registers would stay live across it)
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- O^T += V^T P^T over the two 16-key steps ----
-    const uint32_t vbase = lds_addr(cur) + vt0;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int db = 0; db < DV / 32; ++db) {
-        bf16x8_t a;
-        if constexpr (!F8) {
-          const uint32_t off = (db >> 1) * X_GSTRIDE + 2048 * s;
-          const s16x4_t a0 = lds_tr16((vbase ^ (64 * (db & 1))) + off);
-          const s16x4_t a1 = lds_tr16((vbase ^ (64 * (db & 1) + 32)) + off + 1024);
-          a = __builtin_bit_cast(
-              bf16x8_t, make_uint4(__builtin_bit_cast(uint2, a0).x, __builtin_bit_cast(uint2, a0).y,
-                                   __builtin_bit_cast(uint2, a1).x, __builtin_bit_cast(uint2, a1).y));
-        } else {
-          const uint2 v = lds_tr8((vbase ^ (32 * (db & 1))) + (db >> 1) * X_GSTRIDE + 2048 * half + 1024 * s);
-          a = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(v.x, v.y));
-        }
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], o[db], 0, 0, 0);
-      }
-    }
-    // Interleave the PV reads and MFMAs with a bounded read-ahead: left to
-    // itself the scheduler issues nearly all 64 reads first, and the
-    // registers they hold push the loop's lane constants out to scratch.
-    {
-      constexpr int RPM = F8 ? 1 : 2;   // LDS reads per MFMA
-#pragma unroll
-      for (int i = 0; i < PV_AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * (DV / 32) - PV_AHEAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < PV_AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    return true;
   };
 
+  // O^T += V^T P^T over step k's two 16-key halves (tile `tile`): 32 MFMAs,
+  // MFMA i on dim block i & 15 of half i >> 4. The V^T reads run PV_AHEAD
+  // MFMAs ahead through a ring of raw operands, and the operand of MFMA i + 1
+  // is assembled (widened, for fp8) right after MFMA i issues, in its shadow.
+  // The order is fixed per MFMA: left to the scheduler, the reads sink to
+  // their uses under the loop's register pressure and each MFMA waits for a
+  // full LDS round trip.
+  auto pv = [&](const char* tile, int k, const bf16x8_t* pb) {
+    const int half = F8 ? (k & 1) : 0;   // fp8: which 32 keys of the 64-key slot
+    const uint32_t vbase = lds_addr(tile) + vt0_of(fresh_lane());
+    constexpr int NPV = 2 * (DV / 32);
+    typedef std::conditional_t<F8, uint2, uint4> raw_t;
+    auto vread = [&](int i) -> raw_t {
+      const int s = i >> 4, db = i & 15;
+      if constexpr (!F8) {
+        const uint32_t off = (db >> 1) * X_GSTRIDE + 2048 * s;
+        const uint2 a0 = __builtin_bit_cast(uint2, lds_tr16((vbase ^ (64 * (db & 1))) + off));
+        const uint2 a1 = __builtin_bit_cast(uint2, lds_tr16((vbase ^ (64 * (db & 1) + 32)) + off + 1024));
+        return make_uint4(a0.x, a0.y, a1.x, a1.y);
+      } else {
+        return lds_tr8((vbase ^ (32 * (db & 1))) + (db >> 1) * X_GSTRIDE + 2048 * half + 1024 * s);
+      }
+    };
+    auto operand = [&](const raw_t& r) -> bf16x8_t {
+      if constexpr (!F8)
+        return __builtin_bit_cast(bf16x8_t, r);
+      else
+        return __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(r.x, r.y));
+    };
+    raw_t vr[PV_AHEAD];
+#pragma unroll
+    for (int i = 0; i < PV_AHEAD; ++i) vr[i] = vread(i);
+    bf16x8_t a = operand(vr[0]);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      o[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[i >> 4], o[i & 15], 0, 0, 0);
+      if (i + PV_AHEAD < NPV) vr[i % PV_AHEAD] = vread(i + PV_AHEAD);
+      if (i + 1 < NPV) a = operand(vr[(i + 1) % PV_AHEAD]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Online softmax of one step's raw scores (the scale is folded into the
+  // max and the FMA), in 8 stages so that the fast loop can spread it over
+  // the next step's QK MFMAs; each stage pins its results (an empty asm that
+  // takes them as operands), which keeps the compiler from sinking the work
+  // past the QK chain to where it is used. Stage 2 decides whether the step
+  // stays on the fast path: no row's max more than BIG_SLACK above its
+  // reference (which a row's first keys set). The stages leave m_run, l_run
+  // and O alone otherwise; the caller adds lsum to l_run once the step is
+  // accepted.
+  float sx[16], tmax = 0.f, neg_m = 0.f, lsum = 0.f;
+  bool jump = false;
+  bf16x8_t pb[2];
+  auto pin = [](float& v) { asm volatile("" : "+v"(v)); };
+  auto smx = [&](int st, const f32x16_t& sc, int rel) {
+    if (st == 0) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sx[e] = sc[e];
+      // keys past a row's limit or on a bad page (rare: a uniform branch)
+      if (__builtin_amdgcn_ballot_w64(rel < 28)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sx[e] = 8 * (e >> 2) + (e & 3) < rel ? sx[e] : -INFINITY;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pin(sx[e]);
+    } else if (st == 1) {
+      tmax = fmaxf(fmaxf(fmaxf(sx[0], sx[1]), fmaxf(sx[2], sx[3])), fmaxf(fmaxf(sx[4], sx[5]), fmaxf(sx[6], sx[7])));
+      tmax = fmaxf(tmax, fmaxf(fmaxf(fmaxf(sx[8], sx[9]), fmaxf(sx[10], sx[11])),
+                               fmaxf(fmaxf(sx[12], sx[13]), fmaxf(sx[14], sx[15]))));
+      pin(tmax);
+    } else if (st == 2) {
+      tmax = halves_max(tmax) * scale_row;
+      if (m_run == -INFINITY) m_run = tmax;   // o and l of this row are still zero
+      jump = __builtin_amdgcn_ballot_w64(tmax > m_run + BIG_SLACK) != 0;
+      // rows without any key so far keep m = -inf: a finite stand-in makes
+      // their masked scores give exp2(-inf) = 0, never NaN
+      neg_m = -fmaxf(m_run, -1e30f);
+      lsum = 0.f;
+      pin(m_run);
+      pin(neg_m);
+    } else if (st <= 6) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * (st - 3) + i;
+        sx[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[e], scale_row, neg_m));
+        lsum += sx[e];
+        pin(sx[e]);
+      }
+      pin(lsum);
+    } else if (st == 7) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        pb[s] = __builtin_bit_cast(
+            bf16x8_t, make_uint4(pack_bf16x2(sx[8 * s], sx[8 * s + 1]), pack_bf16x2(sx[8 * s + 2], sx[8 * s + 3]),
+                                 pack_bf16x2(sx[8 * s + 4], sx[8 * s + 5]),
+                                 pack_bf16x2(sx[8 * s + 6], sx[8 * s + 7])));
+        asm volatile("" : "+v"(pb[s]));
+      }
+    }
+  };
+
+  // One step with rescaling (the rare path after a row's max jumped): the q
+  // operands are re-read from memory (so q's registers die at the fast
+  // loop's exit instead of being saved to scratch for a loop that rarely
+  // runs) and reach the MFMAs through VALU code, hence the forms with wait
+  // states; every row is rescaled by alpha = 2^(m_old - m_new) (1 for rows
+  // whose max did not move: a conditional rescale merges two versions of O
+  // and makes the compiler hold all of O in VGPRs).
+  auto compute_slow = [&](const char* tile, int k, int rel) {
+    f32x16_t sacc;
+    const uint32_t kbase = lds_addr(tile) + kb0_of(fresh_lane());
+    if constexpr (!F8) {
+      auto kaddr = [&](int t) { return (kbase ^ ((t & 3) << 5)) + (t >> 2) * X_GSTRIDE; };
+      bf16x8_t kr[QK_AHEAD];
+#pragma unroll
+      for (int t = 0; t < QK_AHEAD; ++t) kr[t] = lds_b128(kaddr(t));
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const bf16x8_t a = kr[t % QK_AHEAD];
+        if (t + QK_AHEAD < D / 16) kr[t % QK_AHEAD] = lds_b128(kaddr(t + QK_AHEAD));
+        const bf16x8_t qv = q_operand_mem(t);
+        if (t == 0)
+          qk_first_v(sacc, a, qv);
+        else
+          qk_next_v(sacc, a, qv);
+      }
+    } else {
+      auto kaddr = [&](int blk) { return kbase + blk * X_GSTRIDE + 2048 * (k & 1); };
+      auto kread = [&](int blk) -> i32x8_t {
+        const u32x4_t a = lds_u128(kaddr(blk)), c = lds_u128(kaddr(blk) ^ 16);
+        return i32x8_t{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+      };
+#pragma unroll
+      for (int blk = 0; blk < 9; ++blk) {
+        const i32x8_t a = kread(blk);
+        i32x8_t h, l;
+        if (blk == 8) {
+          h = q8_rope(0);
+          l = q8_rope(1);
+        } else {
+          q8_mem(blk, h, l);
+        }
+        if (blk == 0)
+          qk8_first_v(sacc, a, h);
+        else
+          qk8_next_v(sacc, a, h);
+        qk8_next_v(sacc, a, l);
+      }
+    }
+    qk_wait(sacc);
+    smx(0, sacc, rel);
+    smx(1, sacc, rel);
+    tmax = halves_max(tmax) * scale_row;
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);   // m_run = -inf gives 0
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d) {
+      o[d] *= alpha;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    neg_m = -fmaxf(m_run, -1e30f);
+    lsum = 0.f;
+#pragma unroll
+    for (int st = 3; st < 8; ++st) smx(st, sacc, rel);
+    l_run += lsum;
+    __builtin_amdgcn_sched_barrier(0);
+    pv(tile, k, pb);
+  };
+
+  // Fast loop, software-pipelined across steps: step k + 1's QK MFMAs are
+  // interleaved with step k's softmax, then step k's PV follows.
+  if (ntiles > 0) prepare(0);
   int k = 0;
-  const char* cur = nullptr;
-  for (; k < nsteps; ++k) {
-    if (!F8 || (k & 1) == 0) cur = prepare(F8 ? (k >> 1) : k);
-    if (!compute(cur, k, std::false_type{})) break;
-  }
-  if (k < nsteps) {   // rare: finish with rescaling, starting at the resident step k
-    compute(cur, k, std::true_type{});
-    for (++k; k < nsteps; ++k) {
-      if (!F8 || (k & 1) == 0) cur = prepare(F8 ? (k >> 1) : k);
-      compute(cur, k, std::true_type{});
+  if (!wave_active) {
+    // rows past the end: no compute, but the same barriers and transfers
+    for (int j = 1; j < ntiles; ++j) prepare(j);
+    k = nsteps;
+  } else if (nsteps > 0) {
+    f32x16_t s_cur;
+    int rel_cur = rel_of(0);
+    qk(tile_of(0), 0, s_cur, [](int) {});
+    qk_wait(s_cur);
+    bool jumped = false;
+    for (; k + 1 < nsteps; ++k) {
+      if (!F8 || (k & 1)) prepare(F8 ? (k + 1) >> 1 : k + 1);
+      const int rel_nxt = rel_of(k + 1);
+      f32x16_t s_nxt;
+      qk(tile_of(k + 1), k + 1, s_nxt, [&](int g) { smx(g, s_cur, rel_cur); });
+      // the compiler may move or copy s_nxt (or reuse its registers when the
+      // step is dropped) right after the chain: wait for the last MFMA first
+      // (its wait states overlap that MFMA's own passes)
+      qk_wait(s_nxt);
+      if (jump) {
+        jumped = true;
+        break;
+      }
+      l_run += lsum;
+      pv(tile_of(k), k, pb);
+      s_cur = s_nxt;
+      rel_cur = rel_nxt;
+    }
+    if (!jumped) {
+#pragma unroll
+      for (int g = 0; g < 8; ++g) smx(g, s_cur, rel_cur);
+      if (!jump) {
+        l_run += lsum;
+        pv(tile_of(k), k, pb);
+        ++k;
+      }
+    }
+    // rare: finish with rescaling, from step k, whose tile is resident (as
+    // is the next step's)
+    if (k < nsteps) {
+      int prepared = F8 ? min(k + 1, nsteps - 1) >> 1 : min(k + 1, nsteps - 1);
+      for (; k < nsteps; ++k) {
+        const int j = F8 ? k >> 1 : k;
+        if (j > prepared) {
+          prepare(j);
+          prepared = j;
+        }
+        compute_slow(tile_of(k), k, rel_of(k));
+      }
     }
   }
 

@@ -472,3 +472,55 @@ def test_plan_reuse_across_layers(mla, case):
         r = run_oracle(inp)
         assert_parity(out.float().cpu().double().numpy(), lse.cpu().double().numpy(), r[0], r[1],
                       dtype, f"plan reuse {tag} layer {li}", vabs=r.vabs)
+
+
+# ---------------------------------------------------------------------------
+# a plan that does not fit the call: items skipped and flagged, never run
+# ---------------------------------------------------------------------------
+
+STALE = [
+    ("narrow_bf16", 1, 16, 64, "bf16", (900, 2500, 60, 3000, 1200, 700, 2000, 64)),
+    ("wide_fp8", 1, 64, 64, "fp8", (1300, 200, 2600, 64, 900, 1800, 3000, 500)),
+    ("wide128_fp8_sq2", 2, 64, 64, "fp8", (1000, 2200, 130, 1700, 600, 2900, 64, 1500)),
+    ("wide128_bf16", 1, 128, 128, "bf16", (700, 1900, 2400, 256, 1300, 128, 2048, 999)),
+]
+
+
+@pytest.mark.parametrize("case", STALE, ids=[c[0] for c in STALE])
+def test_stale_plan_items_are_skipped_and_flagged(mla, case):
+    """A plan made for 8 sequences, then reused by mla_decode_with_plan for a
+    call on the first 4 (views of the same buffers, the same workspace). The
+    plan's items for sequences 4..7 are out of range for that call: the
+    kernels skip them, set flag bit 3 and leave rows 4..7 of out and lse as
+    they were. Every address such an item could form lies inside the 8-row
+    buffers and the workspace, so this holds with or without the check."""
+    tag, s_q, H, bs, dtype, lens = case
+    inp = mi.make_inputs(mi.Workload(tag, 8, s_q, H, bs, dtype, "fixed", lens, seed=81))
+    q, kv, bt, sl = to_device(inp)
+    dev = q.device
+    wl = inp.wl
+    desc8 = mla.make_desc(8, H, bs, kv.shape[0], bt.shape[1], 0 if dtype == "bf16" else 1, True)
+    ws = torch.empty(mla.workspace_size(s_q, desc8), dtype=torch.uint8, device=dev)
+    out = torch.empty((8, s_q, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((8, s_q, H), dtype=torch.float32, device=dev)
+    mla.mla_decode(q, kv, bt, sl, wl.softmax_scale, inp.kv_scale, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    hdr = ws[:16].view(torch.int32).cpu()
+    items = ws[256:256 + 32 * int(hdr[0])].view(torch.int32).view(-1, 8).cpu()
+    assert (items[:, 0] >= 4).any(), "the 8-sequence plan has items for sequences 4..7"
+    assert int(hdr[3]) & 8 == 0
+    out.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    mla.mla_decode_with_plan(q[:4], kv, bt[:4], sl[:4], wl.softmax_scale, ws, kv_scale=inp.kv_scale,
+                             out=out[:4], lse=lse[:4])
+    torch.cuda.synchronize()
+    flags = int(ws[:16].view(torch.int32)[3].item())
+    assert flags & 8, f"{tag}: flag bit 3 not set ({flags})"
+    assert torch.isnan(out[4:].float()).all(), "a skipped item wrote rows 4..7 of out"
+    assert torch.isnan(lse[4:]).all(), "a skipped item wrote rows 4..7 of lse"
+    # a fresh plan on the same views is exact again
+    mla.mla_decode(q[:4], kv, bt[:4], sl[:4], wl.softmax_scale, inp.kv_scale, out=out[:4], lse=lse[:4])
+    torch.cuda.synchronize()
+    r = run_oracle(inp)
+    assert_parity(out[:4].float().cpu().double().numpy(), lse[:4].cpu().double().numpy(), r[0][:4], r[1][:4],
+                  dtype, f"after stale plan {tag}", vabs=r.vabs[:4])
