@@ -17,6 +17,37 @@ constexpr int G_TM = 64;                        // tokens per tile (16 per wave)
 constexpr int G_TK = 32;                        // k per step
 constexpr int G_TN_MAX = 512;                   // output columns per tile (at most)
 
+// Weight-stationary shapes (column slice, A read-ahead in k-steps, token
+// tiles per workgroup) of the two projections; tuning knobs.
+#ifndef ABSQ_TN
+#define ABSQ_TN 128
+#endif
+#ifndef ABSQ_AHEAD
+#define ABSQ_AHEAD 4
+#endif
+#ifndef ABSQ_TPW
+#define ABSQ_TPW 16
+#endif
+#ifndef ABSO_TN
+#define ABSO_TN 64
+#endif
+#ifndef ABSO_AHEAD
+#define ABSO_AHEAD 16
+#endif
+#ifndef ABSO_TPW
+#define ABSO_TPW 32
+#endif
+
+#ifndef RSQ_TPW
+#define RSQ_TPW 32
+#endif
+#ifndef RSQ_AHT
+#define RSQ_AHT 4
+#endif
+#ifndef RSQ_NW
+#define RSQ_NW 8
+#endif
+
 struct GemmParams {
   const uint16_t* a;       // A(t, h, k) = a[(t * H + h) * lda + k]
   const uint16_t* b;       // B(h, k, n) = b[(h * K + k) * N + n]
@@ -142,14 +173,25 @@ __global__ __launch_bounds__(G_THREADS) void mla_bgemm_kernel(GemmParams p) {
 // whose slot for flat k-step f is f % AH; AH divides the k-steps per tile),
 // which keeps enough reads in flight with one workgroup per CU. No barrier is
 // needed inside a tile: B does not change.
+//
+// The grid is one-dimensional and XCD-aware: workgroups are dealt to the 8
+// XCDs in turn, so the column slices of one (token group, head) get ids 8
+// apart. They then run side by side on one XCD, and the A rows they all read
+// come from HBM once, into that XCD's L2, instead of once per slice.
 template <int TN, int KMAX, int WS_AHEAD, int WS_TPW>   // WS_TPW: token tiles per workgroup
 __global__ __launch_bounds__(G_THREADS) void mla_bgemm_ws_kernel(GemmParams p) {
   constexpr int BROW = TN * 2 + 8;
   constexpr int CROW = TN * 2 + 16;
   __shared__ __attribute__((aligned(16))) char bsm[KMAX * BROW];
   __shared__ __attribute__((aligned(16))) char csm[G_TM * CROW];
-  const int h = blockIdx.z;
-  const int n0 = blockIdx.x * TN;
+  const int ns = p.N / TN;                                   // column slices
+  const int groups = ((p.T + G_TM - 1) / G_TM + WS_TPW - 1) / WS_TPW;
+  const int j = blockIdx.x >> 3;
+  const int pair = (j / ns) * 8 + (blockIdx.x & 7);         // (token group, head)
+  if (pair >= groups * p.H) return;
+  const int h = pair % p.H;
+  const int gy = pair / p.H;
+  const int n0 = (j % ns) * TN;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int jj = (lane >> 2) & 3, qq = lane & 3;
@@ -167,7 +209,7 @@ __global__ __launch_bounds__(G_THREADS) void mla_bgemm_ws_kernel(GemmParams p) {
   }
   __syncthreads();
 
-  const int tile0 = blockIdx.y * WS_TPW;
+  const int tile0 = gy * WS_TPW;
   const int ntile = min(WS_TPW, (p.T + G_TM - 1) / G_TM - tile0);
   // the flat k-step sequence of this workgroup: tile u, step s -> u * steps + s
   const int total = ntile * steps;
@@ -183,7 +225,7 @@ __global__ __launch_bounds__(G_THREADS) void mla_bgemm_ws_kernel(GemmParams p) {
 
   for (int u = 0; u < ntile; ++u) {
     const int t0 = (tile0 + u) * G_TM;
-    if (p.pe != nullptr && blockIdx.x == 0) {   // the rotary part of q
+    if (p.pe != nullptr && n0 == 0) {   // the rotary part of q
       for (int i = tid; i < G_TM * 8; i += G_THREADS) {
         const int t = t0 + (i >> 3), c = i & 7;
         if (t < p.T)
@@ -236,6 +278,139 @@ __global__ __launch_bounds__(G_THREADS) void mla_bgemm_ws_kernel(GemmParams p) {
   }
 }
 
+// Register-stationary variant that writes whole rows: each of the NW waves
+// keeps its 16 * NTW-column slice of the head's B (all K rows) in VGPRs as
+// MFMA operands (NTW x K/32 fragments), so
+// the main loop reads only A and has no LDS traffic for B. A workgroup runs
+// RS_TPW tiles of 16 tokens; every tile is staged in LDS as complete output
+// rows (absorb_q: the 512 latent columns and the copied q_pe), which leave as
+// contiguous runs (1152 bytes per q row) instead of per-slice pieces.
+// B enters the registers through a per-wave LDS staging area, 32 rows at a
+// time, read back with the transposed reads (no workgroup barrier: each wave
+// stages and reads only its own area). One workgroup per (token group, head),
+// head fastest: workgroups that run together read neighbouring A rows and
+// write neighbouring output rows.
+constexpr int RS_TM = 16;        // tokens per tile
+template <int K, int NW, int NTW, int AHT, int TPW, bool PE>   // NW waves; AHT: tiles of A read ahead
+__global__ __launch_bounds__(NW * 64) void mla_bgemm_rs_kernel(GemmParams p) {
+  constexpr int NTH = NW * 64;
+  constexpr int WCOL = 16 * NTW;                 // columns per wave
+  constexpr int N = NW * WCOL;                   // columns per workgroup (= p.N)
+  constexpr int SROW = WCOL * 2 + 8;             // staging row (bytes)
+  constexpr int OUTC = N + (PE ? 64 : 0);        // staged output columns
+  constexpr int CROW = OUTC * 2 + 16;            // LDS row of the staged tile
+  constexpr int KS = K / G_TK;                   // k-steps
+  constexpr int STG = NW * G_TK * SROW;
+  constexpr int CST = RS_TM * CROW;
+  constexpr int AH = AHT * KS;                   // ring slots: flat k-steps ahead
+  static_assert(TPW % AHT == 0, "the tile loop is unrolled by AHT");
+  __shared__ __attribute__((aligned(16))) char lds[STG > CST ? STG : CST];
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int jj = (lane >> 2) & 3, qq = lane & 3;
+  const int tiles = (p.T + RS_TM - 1) / RS_TM;
+  const int groups = (tiles + TPW - 1) / TPW;
+  const int pair = blockIdx.x;   // (token group, head), head fastest
+  if (pair >= groups * p.H) return;
+  const int h = pair % p.H;
+  const int tile0 = (pair / p.H) * TPW;
+  const int ntile = min(TPW, tiles - tile0);
+
+  // ---- B slice of this wave into registers: frag[nt][s] ----
+  bf16x8_t frag[NTW][KS];
+  {
+    char* st = lds + w * G_TK * SROW;
+    const uint16_t* bw = p.b + (size_t)h * K * N + w * WCOL;
+    constexpr int CPR = WCOL / 8;                  // 16-byte chunks per staged row
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int i = lane; i < G_TK * CPR; i += 64) {
+        const int r = i / CPR, c = i % CPR;
+        *reinterpret_cast<uint4*>(st + r * SROW + c * 16) =
+            *reinterpret_cast<const uint4*>(bw + (size_t)(s * G_TK + r) * N + 8 * c);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const char* src = st + (8 * g + jj) * SROW + (16 * nt + 4 * qq) * 2;
+        const s16x4_t b0 = gemm_read_tr(src);
+        const s16x4_t b1 = gemm_read_tr(src + 4 * SROW);
+        frag[nt][s] = __builtin_bit_cast(
+            bf16x8_t, make_uint4(__builtin_bit_cast(uint2, b0).x, __builtin_bit_cast(uint2, b0).y,
+                                 __builtin_bit_cast(uint2, b1).x, __builtin_bit_cast(uint2, b1).y));
+      }
+    }
+  }
+  __syncthreads();   // the staging areas become the output tile
+
+  // A fragments, flat k-step f = u * KS + s, AH ahead in a register ring
+  const int total = ntile * KS;
+  auto load_a = [&](int f) {
+    const int u = f / KS, s = f - u * KS;
+    const int t = (tile0 + u) * RS_TM + c16;
+    if (t >= p.T) return make_uint4(0, 0, 0, 0);
+    return *reinterpret_cast<const uint4*>(p.a + ((size_t)t * p.H + h) * p.lda + s * G_TK + 8 * g);
+  };
+  uint4 ring[AH];
+#pragma unroll
+  for (int i = 0; i < AH; ++i) ring[i] = i < total ? load_a(i) : make_uint4(0, 0, 0, 0);
+  // absorb_q: q_pe chunk (row tid >> 3, 16 bytes tid & 7) of tile u, AHT tiles
+  // ahead as well (threads 0..127): a load issued within its own tile would
+  // hold every tile's barrier for a memory round trip
+  auto load_pe = [&](int u) {
+    const int t = (tile0 + u) * RS_TM + (tid >> 3);
+    if (!PE || tid >= RS_TM * 8 || u >= ntile || t >= p.T) return make_uint4(0, 0, 0, 0);
+    return *reinterpret_cast<const uint4*>(p.pe + ((size_t)t * p.H + h) * 64 + 8 * (tid & 7));
+  };
+  uint4 pe_ring[AHT];
+#pragma unroll
+  for (int i = 0; i < AHT; ++i) pe_ring[i] = load_pe(i);
+
+  // the tile loop is unrolled by AHT so that every ring slot is a constant:
+  // flat k-step (u0 + uu) * KS + s sits in slot uu * KS + s
+  for (int u0 = 0; u0 < ntile; u0 += AHT)
+#pragma unroll
+  for (int uu = 0; uu < AHT; ++uu) {
+    const int u = u0 + uu;
+    if (u >= ntile) break;
+    const int t0 = (tile0 + u) * RS_TM;
+    f32x4_t acc[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int f = u * KS + s;
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ring[uu * KS + s]);
+      if (f + AH < total) ring[uu * KS + s] = load_a(f + AH);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag[nt][s], a, acc[nt], 0, 0, 0);
+    }
+    // acc[nt] lane (c16 = token, g) holds C[t0 + c16][w * WCOL + 16nt + 4g + j]
+    {
+      char* crow = lds + c16 * CROW + (w * WCOL) * 2;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+        *reinterpret_cast<uint2*>(crow + (16 * nt + 4 * g) * 2) =
+            make_uint2(pack_bf16x2(acc[nt][0], acc[nt][1]), pack_bf16x2(acc[nt][2], acc[nt][3]));
+    }
+    if constexpr (PE) {   // q_pe (t, h, 0:64) -> columns N .. N + 63
+      if (tid < RS_TM * 8)
+        *reinterpret_cast<uint4*>(lds + (tid >> 3) * CROW + N * 2 + (tid & 7) * 16) = pe_ring[uu];
+      pe_ring[uu] = load_pe(u + AHT);
+    }
+    __syncthreads();
+    constexpr int CCH = OUTC / 8;                  // 16-byte chunks per output row
+    for (int i = tid; i < RS_TM * CCH; i += NTH) {
+      const int r = i / CCH, c = i % CCH;
+      const int tt = t0 + r;
+      if (tt < p.T)
+        *reinterpret_cast<uint4*>(p.c + ((size_t)tt * p.H + h) * p.ldc + 8 * c) =
+            *reinterpret_cast<const uint4*>(lds + r * CROW + c * 16);
+    }
+    __syncthreads();   // the tile buffer is rewritten by the next tile
+  }
+}
+
 bool al(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
 mla_status_t launch_bgemm(const GemmParams& gp, void* stream) {
@@ -245,14 +420,27 @@ mla_status_t launch_bgemm(const GemmParams& gp, void* stream) {
   // many tokens: weight-stationary. Narrow column slices keep the LDS per
   // workgroup small enough for two or more workgroups per CU (measured faster
   // than wider slices, which read A fewer times).
-  if (gp.N == 512 && gp.K == 128 && tiles >= 32) {   // absorb_q, d_nope = 128: 128-column slices
-    const unsigned ty = (unsigned)((tiles + 15) / 16);
-    hipLaunchKernelGGL((mla_bgemm_ws_kernel<128, 128, 4, 16>), dim3(4, ty, gp.H), dim3(G_THREADS), 0, st0, gp);
+  // absorb_q, d_nope = 128, at least 256 tokens: whole rows, B in registers
+  const int tiles16 = (gp.T + RS_TM - 1) / RS_TM;
+  if (tiles16 >= 16 && gp.K == 128 && gp.N == 512 && gp.pe != nullptr) {   // absorb_q
+    const unsigned n = (unsigned)(((tiles16 + RSQ_TPW - 1) / RSQ_TPW) * gp.H);
+    hipLaunchKernelGGL((mla_bgemm_rs_kernel<128, RSQ_NW, 512 / 16 / RSQ_NW, RSQ_AHT, RSQ_TPW, true>), dim3(n),
+                       dim3(64 * RSQ_NW), 0, st0, gp);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
   }
-  if (gp.K == 512 && gp.N % 64 == 0 && tiles >= 64) {   // absorb_out: 64-column slices
-    const unsigned ty = (unsigned)((tiles + 31) / 32);
-    hipLaunchKernelGGL((mla_bgemm_ws_kernel<64, 512, 8, 32>), dim3(gp.N / 64, ty, gp.H), dim3(G_THREADS), 0, st0, gp);
+  // one-dimensional XCD-aware grid: 8 x slices x ceil(pairs / 8) workgroups
+  auto ws_grid = [&](int tn, int tpw) {
+    const long long pairs = (long long)((tiles + tpw - 1) / tpw) * gp.H;
+    return dim3(static_cast<unsigned>(8LL * (gp.N / tn) * ((pairs + 7) / 8)));
+  };
+  if (gp.N == 512 && gp.K == 128 && tiles >= 32) {   // absorb_q, d_nope = 128
+    hipLaunchKernelGGL((mla_bgemm_ws_kernel<ABSQ_TN, 128, ABSQ_AHEAD, ABSQ_TPW>), ws_grid(ABSQ_TN, ABSQ_TPW),
+                       dim3(G_THREADS), 0, st0, gp);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
+  if (gp.K == 512 && gp.N % ABSO_TN == 0 && tiles >= 64) {   // absorb_out
+    hipLaunchKernelGGL((mla_bgemm_ws_kernel<ABSO_TN, 512, ABSO_AHEAD, ABSO_TPW>), ws_grid(ABSO_TN, ABSO_TPW),
+                       dim3(G_THREADS), 0, st0, gp);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
   }
   // absorb_q (N = 512, K = d_nope): whole 512-column rows per tile; otherwise
