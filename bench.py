@@ -482,7 +482,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(mi.WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--only", action="store_true",
-                    help="time only --workload (no per-workload summary of the others)")
+                    help="time only --workload (no per-workload summary of the others); with "
+                         "--absorb / --append, only the largest size")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the timings with the 256 MB Infinity Cache evicted before each call")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -501,11 +502,11 @@ def main():
         copy_calibration()
         return
     if a.absorb:
-        for T, H in ((128, 16), (64, 128), (4096, 128)):
+        for T, H in ((4096, 128),) if a.only else ((128, 16), (64, 128), (4096, 128)):
             print(json.dumps(bench_absorb(T, H, 128, a.steps, a.warmup)), flush=True)
         return
     if a.append:
-        for n in (128, 65536):
+        for n in (65536,) if a.only else (128, 65536):
             for dt in ("bf16", "fp8"):
                 print(json.dumps(bench_append(n, dt, a.steps, a.warmup)), flush=True)
         return
