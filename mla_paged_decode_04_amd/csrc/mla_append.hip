@@ -37,7 +37,6 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
 // so the inputs are clamped to +-448 first; clamped, it gives the same code as
 // f32_to_e4m3fn above for every non-NaN float32 (all 2^32 inputs compared on
 // MI355X). NaN inputs take f32_to_e4m3fn.
-typedef short s16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32x4_to_e4m3fn(float y0, float y1, float y2, float y3) {
   if (__builtin_expect((y0 != y0) | (y1 != y1) | (y2 != y2) | (y3 != y3), 0))
     return f32_to_e4m3fn(y0) | (f32_to_e4m3fn(y1) << 8) | (f32_to_e4m3fn(y2) << 16) | (f32_to_e4m3fn(y3) << 24);

@@ -80,14 +80,50 @@ __host__ __device__ inline int ceil_div_small(int a, int b) {
 // Split of one sequence's key range [0, keys) into n chunks of `len` keys
 // (len a multiple of the tile); keys == 0 still yields one (empty) chunk.
 // Computed in 64-key units (chunk is a multiple of 64, keys <= 2^30), where
-// ceil(keys / x) = ceil(ceil(keys / 64) / (x / 64)).
+// ceil(keys / x) = ceil(ceil(keys / 64) / (x / 64)). With k = ceil(keys / 64)
+// and c = chunk / 64: n = ceil(k / c) and len / 64 = l = ceil(k / n), and
+// these n chunks of l cover k exactly once more than n - 1 would: l <= c
+// (k / n <= c, c an integer), so (n - 1) l <= (n - 1) c < k.
 __host__ __device__ inline void seq_split(int keys, int chunk, int* n, int* len) {
   if (keys <= 0) { *n = 1; *len = 0; return; }
   const int k64 = (keys + NT - 1) / NT;
   const int n0 = ceil_div_small(k64, chunk / NT);
-  const int l64 = ceil_div_small(k64, n0);
-  *len = l64 * NT;
-  *n = ceil_div_small(k64, l64);
+  *len = ceil_div_small(k64, n0) * NT;
+  *n = n0;
+}
+
+// The same arithmetic on the device, in float64: a reciprocal estimate
+// refined by one Newton step (relative error far below 2^-40) gives a
+// truncated quotient within one of floor(a / b) for a <= 2^25; the remainder
+// a - q b is exact in float64 (integers below 2^52) and corrects it. The
+// divisor's refined reciprocal is computed once where the divisor repeats.
+__device__ __forceinline__ double rcp_refined(double d) {
+  const double r = __builtin_amdgcn_rcp(d);
+  return __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+}
+// floor(a / b) and the remainder, for 0 <= a < 2^31 and 1 <= b <= 2^25
+__device__ __forceinline__ int floor_div_dev(int a, double db, double rb, double* rem_out) {
+  const double da = a;
+  const double q = __builtin_trunc(da * rb);
+  const double rem = __builtin_fma(-q, db, da);
+  // branch-free correction by -1, 0 or +1
+  const double adj = (rem < 0.0 ? -1.0 : 0.0) + (rem >= db ? 1.0 : 0.0);
+  *rem_out = __builtin_fma(-adj, db, rem);
+  return static_cast<int>(q + adj);
+}
+__device__ __forceinline__ int ceil_div_dev(int a, double db, double rb) {
+  double rem;
+  const int q = floor_div_dev(a, db, rb, &rem);
+  return rem > 0.0 ? q + 1 : q;
+}
+// seq_split with the chunk's 64-key count c64 and its refined reciprocal
+__device__ __forceinline__ void seq_split_dev(int keys, double c64, double rc, int* n, int* len) {
+  if (keys <= 0) { *n = 1; *len = 0; return; }
+  const int k64 = (keys + NT - 1) / NT;
+  const int n0 = ceil_div_dev(k64, c64, rc);
+  const double dn = n0;
+  *len = ceil_div_dev(k64, dn, rcp_refined(dn)) * NT;
+  *n = n0;
 }
 
 __host__ __device__ inline int chunk_from_work(long long work, int forced, int target) {
@@ -236,15 +272,60 @@ struct PlanParams {
 constexpr int PLAN_THREADS = 256;
 constexpr int PLAN_WAVES = PLAN_THREADS / 64;
 
-template <typename T>
-__device__ __forceinline__ T wave_inclusive_scan(T v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    T u = __shfl_up(v, off);
-    if (lane >= off) v += u;
-  }
+// Cross-lane steps on DPP (operands moved between lanes by the VALU, with no
+// LDS round trip; the planner is a chain of such steps, so their latency is
+// its run time). Controls: quad_perm [1,0,3,2] = 0xB1 and [2,3,0,1] = 0x4E
+// (lane ^ 1, lane ^ 2), row_half_mirror 0x141 (lane i <- 7 - i within 8),
+// row_mirror 0x140 (i <- 15 - i within 16), row_shr:n 0x110 + n, row_bcast:15
+// 0x142 (row r <- lane 15 of row r - 1) and row_bcast:31 0x143 (rows 2, 3 <-
+// lane 31). A lane with no source, or in a row the mask leaves out, gets
+// `fill`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_move(int fill, int v) {
+  return __builtin_amdgcn_update_dpp(fill, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ long long dpp_move64(long long fill, long long v) {
+  const uint64_t f = static_cast<uint64_t>(fill), u = static_cast<uint64_t>(v);
+  const uint32_t lo = static_cast<uint32_t>(dpp_move<CTRL, ROWS>(static_cast<int>(f), static_cast<int>(u)));
+  const uint32_t hi =
+      static_cast<uint32_t>(dpp_move<CTRL, ROWS>(static_cast<int>(f >> 32), static_cast<int>(u >> 32)));
+  return static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Inclusive scan over the 64 lanes of a wave: shifts by 1, 2, 4, 8 inside
+// each 16-lane row, then the totals of rows 0 and 2 carried into rows 1 and 3,
+// then lane 31's into rows 2 and 3. `ident` is op's identity.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_scan(T v, T ident, Op op) {
+  auto mv = [&](auto ctrl, auto rows, T x) -> T {
+    constexpr int C = decltype(ctrl)::value, R = decltype(rows)::value;
+    if constexpr (sizeof(T) == 8)
+      return dpp_move64<C, R>(ident, x);
+    else
+      return dpp_move<C, R>(ident, x);
+  };
+  using std::integral_constant;
+  v = op(v, mv(integral_constant<int, 0x111>{}, integral_constant<int, 0xF>{}, v));
+  v = op(v, mv(integral_constant<int, 0x112>{}, integral_constant<int, 0xF>{}, v));
+  v = op(v, mv(integral_constant<int, 0x114>{}, integral_constant<int, 0xF>{}, v));
+  v = op(v, mv(integral_constant<int, 0x118>{}, integral_constant<int, 0xF>{}, v));
+  v = op(v, mv(integral_constant<int, 0x142>{}, integral_constant<int, 0xA>{}, v));
+  v = op(v, mv(integral_constant<int, 0x143>{}, integral_constant<int, 0xC>{}, v));
   return v;
+}
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  return wave_scan(v, 0, [](int a, int b) { return a + b; });
+}
+// The wave's total (or min / max): lane 63 of the inclusive scan, uniform.
+__device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
+__device__ __forceinline__ unsigned long long readlane64(unsigned long long u, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(u), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), l);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ long long lane63(long long v) {
+  return static_cast<long long>(readlane64(static_cast<unsigned long long>(v), 63));
 }
 
 // One workgroup. Thread t owns the contiguous sequences [t*per, (t+1)*per);
@@ -262,6 +343,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
   __shared__ int s_long[PLAN_WAVES], s_tail[PLAN_WAVES], s_slots[PLAN_WAVES], s_flag[PLAN_WAVES];
   // one sequence per thread: inclusive scan of long items and first slot per sequence
   __shared__ int s_inc_long[PLAN_THREADS], s_slot0[PLAN_THREADS];
+  __shared__ int s_n[PLAN_THREADS], s_chunk_len[PLAN_THREADS];   // the sequence's split
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
 
   int clamped = 0;
@@ -283,13 +365,12 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     lmin = min(lmin, s_len[b]);
     lmax = max(lmax, s_len[b]);
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {   // four independent reductions per step
-    work += __shfl_xor(work, off);
-    keys += __shfl_xor(keys, off);
-    lmin = min(lmin, __shfl_xor(lmin, off));
-    lmax = max(lmax, __shfl_xor(lmax, off));
-  }
+  // four independent scans per step; lane 63 holds the wave's totals
+  auto add64 = [](long long a, long long b) { return a + b; };
+  work = lane63(wave_scan(work, 0LL, add64));
+  keys = lane63(wave_scan(keys, 0LL, add64));
+  lmin = lane63(wave_scan(lmin, INT32_MAX, [](int a, int b) { return min(a, b); }));
+  lmax = lane63(wave_scan(lmax, 0, [](int a, int b) { return max(a, b); }));
   const int any_clamped = __any(clamped);
   if (lane == 0) {
     s_work[wv] = work;
@@ -323,45 +404,72 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     {
       const int k = tid / TPC, sub = tid % TPC;
       const int c = chunk_candidate(cr, step, k);
+      // four sequences per iteration: independent division chains overlap
+      const double c64 = c / NT, rc = rcp_refined(c64);
       int cnt = 0, mx = 0;
-      for (int b = sub; b < p.batch; b += TPC) {
+      int b = sub;
+      for (; b + 3 * TPC < p.batch; b += 4 * TPC) {
+        int n[4], len[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) seq_split_dev(s_len[b + u * TPC], c64, rc, &n[u], &len[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          cnt += n[u];
+          mx = max(mx, min(len[u], s_len[b + u * TPC]));
+        }
+      }
+      for (; b < p.batch; b += TPC) {
         int n, len;
-        seq_split(s_len[b], c, &n, &len);
+        seq_split_dev(s_len[b], c64, rc, &n, &len);
         cnt += n;
         mx = max(mx, min(len, s_len[b]));
       }
-#pragma unroll
-      for (int off = 1; off < TPC; off <<= 1) {
-        cnt += __shfl_xor(cnt, off);
-        mx = max(mx, __shfl_xor(mx, off));
-      }
+      // sums over the 8 lanes of a candidate: lane ^ 1, lane ^ 2, then the
+      // other quad of the half row
+      static_assert(TPC == 8, "the three DPP steps below cover 8 lanes");
+      cnt += dpp_move<0xB1, 0xF>(0, cnt);
+      mx = max(mx, dpp_move<0xB1, 0xF>(0, mx));
+      cnt += dpp_move<0x4E, 0xF>(0, cnt);
+      mx = max(mx, dpp_move<0x4E, 0xF>(0, mx));
+      cnt += dpp_move<0x141, 0xF>(0, cnt);
+      mx = max(mx, dpp_move<0x141, 0xF>(0, mx));
       if (sub == 0) {
         s_cnt[k] = cnt;
         s_mx[k] = mx;
       }
     }
     __syncthreads();
-    // argmin over the candidates in one wave (ties: the larger k)
-    unsigned long long cost = ~0ull;
-    int kb = lane;
+    // argmin over the candidates (ties: the larger k) as the minimum of
+    // cost * 32 + (31 - k): a search runs for fewer than SEARCH_MAX_PAIRS
+    // pairs, so the work is below 2^40 keys and every cost below 2^34
+    static_assert(CHUNK_CANDIDATES == 32, "five bits of candidate index");
+    unsigned long long key = ~0ull;
     if (lane < CHUNK_CANDIDATES)
-      cost = plan_cost((unsigned long long)s_cnt[lane] * p.nrg, s_mx[lane], total_keys, p.overhead);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const unsigned long long oc = __shfl_xor(cost, off);
-      const int ok = __shfl_xor(kb, off);
-      if (oc < cost || (oc == cost && ok > kb)) {
-        cost = oc;
-        kb = ok;
-      }
-    }
-    chunk = chunk_candidate(cr, step, kb);
+      key = (plan_cost((unsigned long long)s_cnt[lane] * p.nrg, s_mx[lane], total_keys, p.overhead) << 5) |
+            static_cast<unsigned long long>(CHUNK_CANDIDATES - 1 - lane);
+    auto kmin = [](unsigned long long a, long long b) {
+      const unsigned long long ub = static_cast<unsigned long long>(b);
+      return a < ub ? a : ub;
+    };
+    key = kmin(key, dpp_move64<0xB1, 0xF>(-1LL, static_cast<long long>(key)));
+    key = kmin(key, dpp_move64<0x4E, 0xF>(-1LL, static_cast<long long>(key)));
+    key = kmin(key, dpp_move64<0x141, 0xF>(-1LL, static_cast<long long>(key)));
+    key = kmin(key, dpp_move64<0x140, 0xF>(-1LL, static_cast<long long>(key)));
+    // lanes 0 and 16 hold the minima of candidates 0..15 and 16..31
+    const unsigned long long k0 = readlane64(key, 0), k1 = readlane64(key, 16);
+    const unsigned long long best = k0 < k1 ? k0 : k1;
+    chunk = chunk_candidate(cr, step, CHUNK_CANDIDATES - 1 - static_cast<int>(best & 31));
   }
 
+  const double chunk64 = chunk / NT, rchunk = rcp_refined(chunk64);
   int my_long = 0, my_tail = 0, my_slots = 0;
   for (int b = b0; b < b1; ++b) {
     int n, len;
-    seq_split(s_len[b], chunk, &n, &len);
+    seq_split_dev(s_len[b], chunk64, rchunk, &n, &len);
+    if (per == 1) {
+      s_n[tid] = n;
+      s_chunk_len[tid] = len;
+    }
     my_long += p.nrg * (n - 1);
     my_tail += p.nrg;
     if (n > 1) my_slots += p.nrg * n;
@@ -414,6 +522,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     s_slot0[tid] = slot;
     __syncthreads();
     const int n_long = overflow ? 0 : tot_long;
+    const double dnrg = p.nrg, rnrg = rcp_refined(dnrg);
     for (int i = tid; i < n_long; i += PLAN_THREADS) {
       // the sequence of long item i: the first b with inclusive scan > i
       int lo = 0, hi = p.batch - 1;
@@ -422,18 +531,19 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
         if (s_inc_long[mid] > i) hi = mid; else lo = mid + 1;
       }
       const int b = lo, L = s_len[b];
-      int n, len;
-      seq_split(L, chunk, &n, &len);
+      const int n = s_n[b], len = s_chunk_len[b];
       const int local = i - (s_inc_long[b] - p.nrg * (n - 1));
-      const int s = local / p.nrg;
-      write_item(i, b, local - s * p.nrg, s, n, len, L, s_slot0[b]);
+      double rg;
+      const int s = floor_div_dev(local, dnrg, rnrg, &rg);
+      write_item(i, b, static_cast<int>(rg), s, n, len, L, s_slot0[b]);
     }
     const int n_tail = p.batch * p.nrg;
     for (int i = tid; i < n_tail; i += PLAN_THREADS) {
       // last chunks: nrg per sequence, in sequence order; also the pair entry
-      const int b = i / p.nrg, rg = i - b * p.nrg, L = s_len[b];
-      int n, len;
-      seq_split(L, chunk, &n, &len);
+      double drg;
+      const int b = floor_div_dev(i, dnrg, rnrg, &drg), rg = static_cast<int>(drg), L = s_len[b];
+      int n = s_n[b];
+      const int len = s_chunk_len[b];
       if (overflow) n = 1;
       write_item(n_long + i, b, rg, n - 1, n, len, L, s_slot0[b]);
       p.pairs[2 * i] = n > 1 ? s_slot0[b] + rg * n : -1;
@@ -443,7 +553,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(PlanParams p) {
     for (int b = b0; b < b1; ++b) {
       const int L = s_len[b];
       int n, len;
-      seq_split(L, chunk, &n, &len);
+      seq_split_dev(L, chunk64, rchunk, &n, &len);
       if (overflow) n = 1;
       for (int rg = 0; rg < p.nrg; ++rg) {
         p.pairs[2 * (b * p.nrg + rg)] = n > 1 ? slot + rg * n : -1;

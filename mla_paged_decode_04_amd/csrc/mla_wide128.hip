@@ -98,7 +98,6 @@ __device__ __forceinline__ void qk_done(f32x16_t& s) {
 // keys' codes as stored and q split per row into q * 2^e = hi + lo (below).
 // Same chain rules as the bf16 forms; VALU reads of the result wait for the
 // 16 passes of the last MFMA (qk8_done).
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ void qk8_first(f32x16_t& s, const i32x8_t& a, const i32x8_t& b) {
   asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
 }
@@ -113,38 +112,6 @@ __device__ __forceinline__ void qk8_next_v(f32x16_t& s, const i32x8_t& a, const 
 }
 __device__ __forceinline__ void qk8_done(f32x16_t& s) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
-}
-
-// Four float32 values x (|x| < 256) -> e4m3fn codes of hi = nearest(x) and
-// lo = nearest(x - hi), packed four to a dword. For x = q * 2^e with q a bf16
-// value (8 significant bits) the residual x - hi is a multiple of q's last
-// place with at most 4 significant bits, so lo is exact and hi + lo = x
-// whenever that place is at least e4m3fn's smallest step 2^-9 (elements down
-// to 2^-10 of a row maximum scaled to [128, 256); smaller ones lose bits
-// below 2^-18 of the row maximum).
-typedef short s16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void split_fp8x4(float x0, float x1, float x2, float x3, uint32_t& hi,
-                                            uint32_t& lo) {
-  s16x2_t h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2_t{0, 0}, x0, x1, 1.0f, false);
-  h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x2, x3, 1.0f, true);
-  hi = __builtin_bit_cast(uint32_t, h);
-  const uint32_t d01 = fp8x2_to_bf16x2(hi, false), d23 = fp8x2_to_bf16x2(hi, true);   // exact
-  const float r0 = x0 - __builtin_bit_cast(float, d01 << 16);
-  const float r1 = x1 - __builtin_bit_cast(float, d01 & 0xFFFF0000u);
-  const float r2 = x2 - __builtin_bit_cast(float, d23 << 16);
-  const float r3 = x3 - __builtin_bit_cast(float, d23 & 0xFFFF0000u);
-  s16x2_t l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2_t{0, 0}, r0, r1, 1.0f, false);
-  l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, r2, r3, 1.0f, true);
-  lo = __builtin_bit_cast(uint32_t, l);
-}
-
-// 8 bf16 (one uint4) times 2^e -> hi and lo codes, two dwords each.
-__device__ __forceinline__ void split_fp8x8(uint4 v, float mul, uint32_t* hi, uint32_t* lo) {
-  auto f = [](uint32_t w, bool upper) {
-    return __builtin_bit_cast(float, upper ? (w & 0xFFFF0000u) : (w << 16));
-  };
-  split_fp8x4(f(v.x, false) * mul, f(v.x, true) * mul, f(v.y, false) * mul, f(v.y, true) * mul, hi[0], lo[0]);
-  split_fp8x4(f(v.z, false) * mul, f(v.z, true) * mul, f(v.w, false) * mul, f(v.w, true) * mul, hi[1], lo[1]);
 }
 
 // LDS reads by 32-bit LDS byte address. The per-lane operand offsets are
