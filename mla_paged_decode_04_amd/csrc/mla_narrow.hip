@@ -119,7 +119,9 @@ __device__ __forceinline__ void merge_and_store(const FwdParams& p, char* smem,
 // tile): while it computes tile j, tile j+4 is in flight. Tile layout in LDS:
 // [9 column groups of 128 B][16 keys][8 x 16-byte chunks], chunk position
 // XOR-swizzled by key & 7; the DMA lanes pick their global chunk so the LDS
-// side is always 64 consecutive 16-byte slots.
+// side is always 64 consecutive 16-byte slots. bf16 caches run S^T and O^T on
+// bf16 MFMAs; fp8 caches (32-key tiles) run S^T on the fp8 MFMA with q split
+// into exact e4m3fn hi/lo codes, and convert only the V operand to bf16.
 
 constexpr int H16_KT = 16;                      // keys per wave tile
 constexpr int H16_TILE = H16_KT * D * 2;        // 18432 bytes (bf16)
@@ -129,7 +131,7 @@ constexpr int H16_GSTRIDE = H16_KT * 128;       // bytes per 128-byte column gro
 // fp8 tiles: 32 keys x 576 bytes = 18432 bytes, laid out as
 // [9 column groups of 64 B][32 keys][4 x 16-byte chunks] with the chunk
 // position XOR-swizzled by f(key) = ((key >> 2) + (key >> 4)) & 3, which keeps
-// both the 8-byte K reads and the 8-bit transposed V reads spread over banks.
+// both the 16-byte K reads and the 8-bit transposed V reads spread over banks.
 constexpr int F8_KT = 32;
 constexpr int F8_GSTRIDE = F8_KT * 64;
 
@@ -195,7 +197,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
   const bool row_ok = row < p.rows;
   int limit = 0;   // keys this row sees, set once the first tile is in flight
 
-  bf16x8_t qb[D / 32];   // loaded below, after this wave's first tile was requested
+  // q operands, loaded below (bf16: after this wave's first tile was
+  // requested; fp8: staged in LDS ahead of it). bf16 caches: qb[s] holds dims
+  // 32s + 8g .. +7 of row c16 (16x16x32 bf16 MFMA). fp8 caches: S^T runs on the 16x16x128 f8f6f4 MFMA with both
+  // operands e4m3fn: the keys' codes as stored, and the row q * 2^qe split
+  // into hi + lo codes; q8h/q8l[s] hold dims 128s + 32g .. +31, q8r holds
+  // rope dims 32(g & 1) .. +31 as hi codes (g < 2) or lo codes (g >= 2), so
+  // one MFMA takes both halves of the 64 rope dims.
+  constexpr int QB = F8 ? 1 : D / 32;
+  bf16x8_t qb[QB];
+  i32x8_t q8h[4], q8l[4], q8r;
+  float scale_row = p.scale_log2;   // fp8: times 2^-qe
 
   f32x4_t o[DV / 16];
 #pragma unroll
@@ -205,7 +217,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
 
   // ---- lane constants (LDS byte offsets inside a tile, DMA source offsets) ----
   uint32_t dma_lane[2];
-  int kb[2][2];   // K operand: [M tile][s & 1], add (s >> 1) * column-group stride
+  int kb[2][2];   // K operand: bf16 [M tile][s & 1], add (s >> 1) * column-group stride;
+                  // fp8 [M tile][chunk h], add the column-group offset
   int vt[4];      // V^T operand: [dt & 3], add (dt >> 2) * column-group stride
   if constexpr (!F8) {
     dma_lane[0] = dma_lane[1] = (lane >> 3) * ROWB + (((lane & 7) ^ (lane >> 3)) << 4);
@@ -223,13 +236,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       dma_lane[h] = (lane >> 2) * ROWB + (((lane & 3) ^ (((lane >> 4) + h) & 3)) << 4);
-    // K: key 16*mi + c16, bytes 32*s + 8*g -> chunk 2*s + (g >> 1), half g & 1
+    // K: key 16*mi + c16, bytes 32*g .. +31 of a 128-byte step -> column
+    // group 2*step + (g >> 1), chunks 2*(g & 1) + h (h = 0, 1); the rope step
+    // reads column group 8 from every g. The 16 lanes of one quarter-wave hit
+    // 16 different 16-byte bank groups.
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        kb[mi][h] = (16 * mi + c16) * 64 +
-                    (((2 * h + (g >> 1)) ^ f8_swz(16 * mi + c16)) << 4) + (g & 1) * 8;
+        kb[mi][h] = (16 * mi + c16) * 64 + (((2 * (g & 1) + h) ^ f8_swz(16 * mi + c16)) << 4);
     // V^T: lane s = 2*jj + q supplies V[key_jj][16*dt + 8*q ..+7] with key_jj =
     // 4g + jj (jj < 4) or 16 + 4g + jj - 4, so ds_read_b64_tr_b8 hands lane
     // c16 the 8 values V[key_0..7][16*dt + c16].
@@ -312,17 +327,40 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
     f32x4_t sacc[MT];
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) sacc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (!F8) {
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
+      for (int s = 0; s < D / 32; ++s) {
 #pragma unroll
-      for (int mi = 0; mi < MT; ++mi) {
-        bf16x8_t a;
-        if constexpr (!F8)
-          a = *reinterpret_cast<const bf16x8_t*>(cur + kb[mi][s & 1] + (s >> 1) * GSTRIDE);
-        else
-          a = fp8x8_to_bf16x8_v(*reinterpret_cast<const uint2*>(cur + kb[mi][s & 1] + (s >> 1) * GSTRIDE));
-        sacc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc[mi], 0, 0, 0);
+        for (int mi = 0; mi < MT; ++mi) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(cur + kb[mi][s & 1] + (s >> 1) * GSTRIDE);
+          sacc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], sacc[mi], 0, 0, 0);
+        }
       }
+    } else {
+      // 32 consecutive key bytes per lane: two 16-byte chunks of one key row
+      auto k8 = [&](const char* base, int mi) {
+        const uint4 x = *reinterpret_cast<const uint4*>(base + kb[mi][0]);
+        const uint4 y = *reinterpret_cast<const uint4*>(base + kb[mi][1]);
+        return i32x8_t{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      };
+      const char* kg = cur + (g >> 1) * GSTRIDE;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        i32x8_t a[MT];
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) a[mi] = k8(kg + 2 * s * GSTRIDE, mi);
+        // hi of both M tiles, then lo: no MFMA waits on the one before it
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+          sacc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mi], q8h[s], sacc[mi], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+          sacc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mi], q8l[s], sacc[mi], 0, 0, 0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi)
+        sacc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k8(cur + 8 * GSTRIDE, mi), q8r, sacc[mi], 0, 0,
+                                                                    0, 0, 0, 0);
     }
 
     float x[MT][4];
@@ -332,7 +370,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int key = ts + 16 * mi + 4 * g + jj;
-        float v = sacc[mi][jj] * p.scale_log2;
+        float v = sacc[mi][jj] * scale_row;
         v = key < limit && tile_ok ? v : -INFINITY;
         x[mi][jj] = v;
         tmax = fmaxf(tmax, v);
@@ -388,6 +426,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
 
   int j = w, itn = 0;
   const char* cur = nullptr;
+  if constexpr (F8) {
+    // q reaches LDS by DMA, into this wave's second tile buffer (free until
+    // tile j + 4 is requested), ahead of tile 0: the wait for it below leaves
+    // tile 0 in flight, and the split into e4m3fn codes overlaps that. Layout
+    // [18 blocks of 32 dims][16 rows][64 bytes]; rows past the end read the
+    // last valid row (their values are replaced by zeros below).
+    const int qr = min(lane >> 2, p.rows - 1);
+    const char* qsrc = uniform_ptr(reinterpret_cast<const char*>(p.q + (size_t)b * p.rows * D));
+    const uint32_t ql = lds_addr(wbuf + H16_TILE);
+    const uint32_t qoff = qr * (D * 2) + (lane & 3) * 16;
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) lds_dma16(qsrc + n * 64, qoff, ql + n * 1024);
+  }
   if (w < ntiles) issue(w, wbuf);
   const int L = min(max(L_raw, 0), p.max_keys);
   if (row_ok) {
@@ -395,11 +446,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
     const int vis = p.causal ? L - p.s_q + 1 + tok : L;
     limit = min(vis, t1);
   }
-  // q is loaded while the first tile is in flight. Its loads are consumed
-  // here, so the compiler's own vmcnt wait for them (which also covers the
-  // older tile transfers) sits before the tile loop, not inside it (it cannot
-  // see the DMAs).
-  {
+  // bf16: q is loaded while the first tile is in flight. Its loads are
+  // consumed here, so the compiler's own vmcnt wait for them (which also
+  // covers the older tile transfers) sits before the tile loop, not inside it
+  // (it cannot see the DMAs).
+  if constexpr (!F8) {
     const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
@@ -407,9 +458,63 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
                        : make_uint4(0, 0, 0, 0);
       qb[s] = __builtin_bit_cast(bf16x8_t, v);
     }
-  }
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s) asm volatile("" ::"v"(qb[s]));
+    for (int s = 0; s < D / 32; ++s) asm volatile("" ::"v"(qb[s]));
+  } else {
+    // q's transfers are the oldest: with tile 0's NDMA behind them in flight
+    mem_fence_compiler();
+    if (w < ntiles)
+      wait_vmcnt<NDMA>();
+    else
+      wait_vmcnt<0>();
+    mem_fence_compiler();
+    const char* qs = wbuf + H16_TILE;
+    // dims 128s + 32g + 8c (s < 4) and rope dims 512 + 32(g & 1) + 8c (s = 4):
+    // 32-dim block 4s + g (or 16 + (g & 1)), 16-byte chunk c of row c16
+    uint4 v[5][4];
+    float qmax = 0.f;
+#pragma unroll
+    for (int s = 0; s < 5; ++s)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int blk = s < 4 ? 4 * s + g : 16 + (g & 1);
+        v[s][c] = row_ok ? *reinterpret_cast<const uint4*>(qs + blk * 1024 + c16 * 64 + c * 16)
+                         : make_uint4(0, 0, 0, 0);
+        const uint32_t w4[4] = {v[s][c].x, v[s][c].y, v[s][c].z, v[s][c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          qmax = fmaxf(qmax, fmaxf(fabsf(__builtin_bit_cast(float, w4[i] << 16)),
+                                   fabsf(__builtin_bit_cast(float, w4[i] & 0xFFFF0000u))));
+      }
+    // row scale 2^qe puts the row's largest |q| in [128, 256); scores are then
+    // sums of products of exact e4m3fn values, and 2^-qe joins the score scale
+    qmax = wave_max_across_groups(qmax);
+    const int qe = qmax > 0.f && qmax < INFINITY ? 8 - __builtin_amdgcn_frexp_expf(qmax) : 0;
+    const float qmul = __builtin_ldexpf(1.f, qe);
+    scale_row = p.scale_log2 * __builtin_ldexpf(1.f, -qe);
+#pragma unroll
+    for (int s = 0; s < 5; ++s) {
+      uint32_t h8[8], l8[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) split_fp8x8(v[s][c], qmul, h8 + 2 * c, l8 + 2 * c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (s < 4) {
+          q8h[s < 4 ? s : 0][i] = static_cast<int>(h8[i]);
+          q8l[s < 4 ? s : 0][i] = static_cast<int>(l8[i]);
+        } else {
+          q8r[i] = static_cast<int>(g < 2 ? h8[i] : l8[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // per dword: a 256-bit operand would be an x86 register class in the host pass
+#pragma unroll
+      for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(q8h[s][i]), "v"(q8l[s][i]));
+      asm volatile("" ::"v"(q8r[i]));
+    }
+  }
   for (; j < ntiles; j += 4, ++itn) {
     cur = prepare(j, itn);
     if (!compute(cur, t0 + KT * j, std::false_type{})) break;
