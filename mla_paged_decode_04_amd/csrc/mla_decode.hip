@@ -10,15 +10,16 @@
 //   1. mla_plan_kernel     one workgroup turns device seq_lens into a list of
 //                          work items (sequence, row group, key range)
 //   2. decode kernel       one workgroup per item, S^T = K Q^T and
-//                          O^T += V^T P^T on bf16 MFMA with a base-2 online
+//                          O^T += V^T P^T on MFMA with a base-2 online
 //                          softmax; writes the final rows or a split partial
-//                          (fp32 normalised o, base-2 lse):
+//                          (fp16 normalised o * 2^k, base-2 lse):
 //        mla_decode_narrow   <= 16 query rows per sequence (HBM-bound): every
 //                            wave streams its own key tiles HBM -> LDS
 //        mla_decode_wide     17..64 rows: 64-row items, 16 rows per wave on
 //                            16x16x32 MFMA, the waves share the key tiles
-//        mla_decode_wide128  > 64 rows: 128-row items, 32 rows per wave on
-//                            32x32x16 MFMA
+//        mla_decode_wide128  > 64 rows: 128-row items on 8 waves of 16 rows
+//                            (two waves per SIMD), the waves share the key
+//                            tiles
 //   3. mla_combine_kernel  merges the partials of split (sequence, row group)
 //                          pairs with log-sum-exp weights
 #include <algorithm>
@@ -42,8 +43,8 @@ constexpr int HEADER_BYTES = 256;
 // ---------------------------------------------------------------------------
 
 // Row grouping: kind 0 = narrow kernel (<= 16 rows), kind 1 = wide kernel
-// with 16 rows per wave (64-row items, up to 64 rows), kind 2 = wide kernel
-// with 32 rows per wave on 32x32 MFMAs (128-row items, more than 64 rows).
+// with 16 rows per wave (64-row items, up to 64 rows), kind 2 = 128-row
+// kernel with 8 waves of 16 rows (128-row items, more than 64 rows).
 struct RowCfg {
   int kind;
   int rgs;       // query rows per work item
@@ -58,7 +59,7 @@ __host__ __device__ inline RowCfg row_config(int rows) {
   c.rgs = c.kind == 0 ? 16 : c.kind == 1 ? 64 : 128;
   c.nrg = (rows + c.rgs - 1) / c.rgs;
   c.target = TARGET_ITEMS;
-  // A 128-row item also loads 147 KB of q and writes a 256 KB fp32 partial
+  // A 128-row item also loads 147 KB of q and writes a 128 KB fp16 partial
   // that the combine reads back: several times the narrow kernel's overhead.
   c.overhead = c.kind == 2 ? ITEM_OVERHEAD_WIDE128 : ITEM_OVERHEAD;
   return c;

@@ -130,12 +130,15 @@ constexpr int H16_GSTRIDE = H16_KT * 128;       // bytes per 128-byte column gro
 
 // fp8 tiles: 32 keys x 576 bytes = 18432 bytes, laid out as
 // [9 column groups of 64 B][32 keys][4 x 16-byte chunks] with the chunk
-// position XOR-swizzled by f(key) = ((key >> 2) + (key >> 4)) & 3, which keeps
-// both the 16-byte K reads and the 8-bit transposed V reads spread over banks.
+// position XOR-swizzled by f(key) = key bit 2 + 2 * key bit 4. With it the
+// 16-byte K reads and the 8-byte transposed V reads below are free of LDS
+// bank conflicts (measured on MI355X with the bank-conflict counter on each
+// access pattern alone; the swizzle ((key >> 2) + (key >> 4)) & 3 doubled the
+// LDS cycles of both).
 constexpr int F8_KT = 32;
 constexpr int F8_GSTRIDE = F8_KT * 64;
 
-__device__ __forceinline__ int f8_swz(int key) { return ((key >> 2) + (key >> 4)) & 3; }
+__device__ __forceinline__ int f8_swz(int key) { return ((key >> 2) & 1) | (((key >> 4) & 1) << 1); }
 
 // 8 e4m3fn codes -> 8 bf16 (exact).
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8_v(uint2 w) {
@@ -232,10 +235,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
     for (int c = 0; c < 4; ++c) vt[c] = (4 * g + j) * 128 + (((2 * c) ^ lanex) << 4) + (q & 1) * 8;
   } else {
     // DMA transfer n: column group n >> 1, keys 16*(n & 1) + (lane >> 2), chunk
-    // position lane & 3; f(key) = ((lane >> 4) + (n & 1)) & 3.
+    // position lane & 3; f(key) = ((lane >> 4) & 1) + 2 (n & 1).
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      dma_lane[h] = (lane >> 2) * ROWB + (((lane & 3) ^ (((lane >> 4) + h) & 3)) << 4);
+      dma_lane[h] = (lane >> 2) * ROWB + (((lane & 3) ^ (((lane >> 4) & 1) | (2 * h))) << 4);
     // K: key 16*mi + c16, bytes 32*g .. +31 of a 128-byte step -> column
     // group 2*step + (g >> 1), chunks 2*(g & 1) + h (h = 0, 1); the rope step
     // reads column group 8 from every g. The 16 lanes of one quarter-wave hit

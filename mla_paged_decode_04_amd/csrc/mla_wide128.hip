@@ -1,12 +1,13 @@
 // Paged MLA decode, > 64 query rows per sequence (the 128-head cases):
 // decode attention of MLA in its MQA form ("[WIP][Attention] FlashAttn MLA",
-// description) with 128 query rows per work item, 32 per wave, on gfx950's
-// 32x32x16 bf16 MFMA. A 32-row MFMA tile feeds each LDS byte of K or V to 32
-// rows (twice the 16-row tiles), and issues at full rate with one wave per
-// SIMD. With fp8 e4m3fn caches ("[Attention] Blackwell FP8 MLA support with
-// CUTLASS_MLA backend", Test Plan) the scores run on the 32x32x64 fp8 MFMA
-// against an exact two-term fp8 split of q, and V is widened to bf16 in
-// registers right before each PV MFMA.
+// description) with 128 query rows per work item on 8 waves of 16 rows, two
+// waves per SIMD. A wave's output rows (16 x 512 fp32) take 128 registers,
+// which leaves room for a second wave on every SIMD: while one wave waits for
+// LDS or runs its softmax, the other keeps the matrix core busy. All 8 waves
+// share the key tiles streamed HBM -> LDS. With fp8 e4m3fn caches
+// ("[Attention] Blackwell FP8 MLA support with CUTLASS_MLA backend", Test
+// Plan) the scores run on the 16x16x128 fp8 MFMA against an exact two-term
+// fp8 split of q, and V is widened to bf16 in registers before each PV MFMA.
 #include <type_traits>
 
 #include "mla_internal.h"
@@ -15,143 +16,79 @@ using namespace mla_detail;
 
 namespace {
 
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-// The ring: 4 slots of 36864 bytes (32 bf16 keys or 64 fp8 keys of 576
-// dims), three in flight while one is computed, one workgroup barrier per
-// slot. Each wave issues 9 of the 36 wave-wide 1 KB transfers of a slot.
-constexpr int X_TILE = 36864;
-constexpr int X_SLOTS = 4;
-constexpr int X_NDMA = 9;
-constexpr int X_GSTRIDE = 4096;   // bytes per 64-dim column group (both layouts)
-constexpr int X_RGS = 128;        // query rows per work item
-constexpr int X_STEP = 32;        // keys per compute step (one 32x32 S block)
-#ifndef QK_AHEAD
-#define QK_AHEAD 4                // k-steps whose K reads are issued ahead
-#endif
-#ifndef PV_AHEAD
-#define PV_AHEAD 8                // PV MFMAs whose V^T reads are issued ahead
+constexpr int Y_WAVES = 8;
+constexpr int Y_THREADS = 64 * Y_WAVES;
+constexpr int Y_RGS = 16 * Y_WAVES;   // query rows per work item
+constexpr int Y_SLOT = 36864;         // ring slot: 32 bf16 keys or 64 fp8 keys of 576 dims
+constexpr int Y_SLOTS = 4;            // three slots in flight while one is computed
+constexpr int Y_DMA_WAVES = 4;        // waves 0-3 issue a slot's 36 transfers
+constexpr int Y_NDMA = 9;             // 1 KB transfers per DMA wave per slot
+constexpr int BF_GS = 32 * 128;       // bf16 slot: bytes per 128-byte column group
+constexpr int F8_TILE = 32 * D;       // fp8 slot: two tiles of 32 keys
+constexpr int F8_GS = 32 * 64;        // fp8 tile: bytes per 64-byte column group
+#ifndef KV_AHEAD
+#define KV_AHEAD 4                    // K (QK) and V^T (PV) operand reads kept in flight
 #endif
 
-// bf16 slot layout: [9 column groups][32 keys][8 x 16-byte chunks], chunk c of
-// key k at position c ^ swz16(k). The swizzle is a bijection of key bits 1-3
-// (for either parity of bit 0), so the 16-byte K reads of 16 consecutive keys
-// hit 16 distinct bank groups; and it flips bit 2 between keys k and k + 2, so
-// the transposed V reads (4 keys x 32 dims per 32 lanes) are conflict-free too.
-__device__ __forceinline__ int swz16(int k) {
-  return (((k >> 1) & 1) << 2) | (((k >> 3) & 1) << 1) | ((k >> 2) & 1);
-}
-// fp8 slot layout: [9 column groups][64 keys][4 x 16-byte chunks], chunk c of
-// key k at position c ^ ((k >> 2) & 3).
-__device__ __forceinline__ int swz8(int k) { return (k >> 2) & 3; }
+// fp8 tile layout: [9 column groups of 64 B][32 keys][4 x 16 B chunks], chunk
+// c of key k at position c ^ swz8(k), swz8(k) = k bit 2 + 2 * k bit 4. With
+// it the K reads (16 bytes per lane, keys 16 mi + (lane & 15)) and the
+// transposed V reads (8 bytes per lane, keys 4g + 0..3 and 16 + 4g + 0..3)
+// are free of LDS bank conflicts; the earlier swizzle ((k >> 2) + (k >> 4)) & 3
+// doubled the LDS cycles of both (measured on MI355X with the bank-conflict
+// counter on each access pattern in isolation).
+__device__ __forceinline__ int swz8(int key) { return ((key >> 2) & 1) | (((key >> 4) & 1) << 1); }
 
-// Lanes l and l ^ 32 hold the two halves of one row's 32 scores: combine them
-// with gfx950's v_permlane32_swap (see the wide kernel for why inline asm).
-__device__ __forceinline__ float halves_max(float v) {
+// Max over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) with
+// gfx950's row-swap permutes, issued from inline asm (through the builtins
+// the compiler folds max(swap result 0, swap result 1) to result 0).
+__device__ __forceinline__ float max4_groups(float v) {
   float y = v;
   asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(v), "+v"(y));
+  v = fmaxf(v, y);
+  y = v;
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(v), "+v"(y));
   return fmaxf(v, y);
-}
-__device__ __forceinline__ float halves_sum(float v) {
-  float y = v;
-  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(v), "+v"(y));
-  return v + y;
 }
 
 // The lane id, read afresh where it is used: an opaque asm the compiler can
 // neither merge with other reads nor hoist out of the loop. Lane constants
-// derived from it are recomputed at each use (a few VALU instructions that
-// run under the MFMAs) rather than kept live across the tile loop, where the
-// register pressure would send them to scratch, and the wait for a scratch
-// reload would also wait for every tile transfer in flight.
+// derived from it are recomputed at each use (a few VALU instructions)
+// rather than kept live across the tile loop, where the register pressure
+// would send them to scratch, and the wait for a scratch reload would also
+// wait for every tile transfer in flight.
 __device__ __forceinline__ int fresh_lane() {
   int l;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
   return l;
 }
 
-// The S^T accumulation chain is issued from inline asm so that S lives in
-// VGPRs: through the builtin the compiler gives every MFMA accumulator an
-// AGPR, and S (16) next to O (256) overflows the 256 AGPRs into spills. The
-// asm carries the hazard waits the compiler would otherwise add: a chained
-// MFMA reading exactly the previous one's result needs none; an operand
-// written by a VALU instruction needs 2 wait states before the MFMA reads it
-// (the _v forms); and VALU reads of the result wait for the last MFMA's
-// passes (qk_done, which also orders those reads after it).
-__device__ __forceinline__ void qk_first(f32x16_t& s, const bf16x8_t& a, const bf16x8_t& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void qk_next(f32x16_t& s, const bf16x8_t& a, const bf16x8_t& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void qk_first_v(f32x16_t& s, const bf16x8_t& a, const bf16x8_t& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void qk_next_v(f32x16_t& s, const bf16x8_t& a, const bf16x8_t& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void qk_done(f32x16_t& s) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
-}
-
-// fp8 caches: S^T on gfx950's 32x32x64 MFMA with both operands e4m3fn, the
-// keys' codes as stored and q split per row into q * 2^e = hi + lo (below).
-// Same chain rules as the bf16 forms; VALU reads of the result wait for the
-// 16 passes of the last MFMA (qk8_done).
-__device__ __forceinline__ void qk8_first(f32x16_t& s, const i32x8_t& a, const i32x8_t& b) {
-  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void qk8_next(f32x16_t& s, const i32x8_t& a, const i32x8_t& b) {
-  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void qk8_first_v(f32x16_t& s, const i32x8_t& a, const i32x8_t& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void qk8_next_v(f32x16_t& s, const i32x8_t& a, const i32x8_t& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void qk8_done(f32x16_t& s) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
-}
-
-// LDS reads by 32-bit LDS byte address. The per-lane operand offsets are
-// formed as (slot base + lane offset) ^ (swizzle flip): the slot base is a
-// multiple of 1024, so the XOR only touches the lane offset's chunk bits, and
-// the result changes every step, which keeps the compiler from hoisting the
-// flipped variants out of the loop as extra live registers.
-__device__ __forceinline__ bf16x8_t lds_b128(uint32_t a) {
-  return *(const __attribute__((address_space(3))) bf16x8_t*)(a);
-}
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x4_t lds_u128(uint32_t a) {
-  return *(const __attribute__((address_space(3))) u32x4_t*)(a);
+__device__ __forceinline__ u32x4_t lds_u128(const char* a) {
+  return *reinterpret_cast<const u32x4_t*>(a);
 }
-__device__ __forceinline__ s16x4_t lds_tr16(uint32_t a) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a));
-}
-__device__ __forceinline__ uint2 lds_tr8(uint32_t a) {
+__device__ __forceinline__ uint2 lds_tr8(const char* a) {
   return __builtin_bit_cast(
       uint2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(a)));
 }
 
-// MFMA operand layouts (32x32x16): A[m][k] and B[k][n] put m (or n) = lane & 31
-// and k = 8 * (lane >> 5) + i in element i; C[m][n] puts n = lane & 31 and
-// m = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3) in element e.
-//   S^T (32 keys x 32 rows) = K (A, from LDS) . Q^T (B, registers)
-//   O^T (512 dims x 32 rows) += V^T (A, transposed LDS reads) . P^T (B)
-// The C layout of S^T gives lane (row n, half h) the keys 8q + 4h + r; packed
-// in that order they are exactly the P^T operand of the two 16-key PV steps
-// once the V^T operand of step s takes keys 16s + 4h + (0..3) and
-// 16s + 8 + 4h + (0..3), which two 4-key transposed reads deliver.
+// MFMA operand layouts (16x16, k = 32 bf16 or 128 fp8 per lane group):
+// A[m][k] and B[k][n] put m (or n) = lane & 15 and k = (k per lane) * (lane
+// >> 4) + i in element i; C[m][n] puts n = lane & 15 and m = 4 (lane >> 4) + e.
+//   S^T (16 keys x 16 rows) = K (A, from LDS) . Q^T (B, registers)
+//   O^T (16 dims x 16 rows) += V^T (A, transposed LDS reads) . P^T (B)
+// Lane (row c16, group g) thus holds the scores of keys 4g + e of each 16-key
+// block, and P^T's k-slot 8g + i is key 4g + i (i < 4) of block 0 or
+// 16 + 4g + i - 4 of block 1; the V^T reads deliver the same key order.
 template <int KVT>
-__global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
+__global__ __launch_bounds__(Y_THREADS, 1) void mla_decode_wide128(FwdParams p) {
   constexpr bool F8 = KVT == MLA_DTYPE_FP8_E4M3FN;
-  constexpr int KT = F8 ? 64 : 32;                  // keys per ring slot
-  constexpr int ROWB = F8 ? D : D * 2;              // bytes per cached row
-  __shared__ __attribute__((aligned(1024))) char smem[X_SLOTS * X_TILE];   // 147456 bytes
-  // the rope part of Q (the last 4 k-steps), 128 rows x 128 bytes: in LDS
-  // rather than in registers, which keeps the fast loop free of spills
-  __shared__ __attribute__((aligned(1024))) char qrope[X_RGS * 128];        // 16384 bytes
+  constexpr int KT = F8 ? 64 : 32;       // keys per ring slot
+  constexpr int ROWB = F8 ? D : 2 * D;   // bytes per cached row
+  constexpr int R = KV_AHEAD;
+  __shared__ __attribute__((aligned(1024))) char smem[Y_SLOTS * Y_SLOT];   // 147456 bytes
+  // the rope part of q, per wave in its operand layout (2 KB per wave)
+  __shared__ __attribute__((aligned(1024))) char qlds[Y_WAVES * 2048];     // 16384 bytes
 
   // XCD-aware item order (consecutive workgroups go to different XCDs): each
   // XCD takes a contiguous run of items. The grid is a multiple of 8.
@@ -167,7 +104,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   const int t0 = __builtin_amdgcn_readfirstlane(it[2]);
   const int t1 = __builtin_amdgcn_readfirstlane(it[3]);
   const int slot = __builtin_amdgcn_readfirstlane(it[4]);
-  if (!item_in_range(p, X_RGS, b, rg, t0, t1, slot)) {
+  if (!item_in_range(p, Y_RGS, b, rg, t0, t1, slot)) {
     flag_bad_item(p.flags);
     return;
   }
@@ -175,17 +112,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int n32 = lane & 31;
-  const int hi = lane >> 5;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
   const int L = __builtin_amdgcn_readfirstlane(min(max(p.seq_lens[b], 0), p.max_keys));
   // a cache read by one row group only streams past the caches; with several
   // row groups per sequence the other groups re-read it from L2
-  const bool stream_once = p.rows <= X_RGS;
+  const bool stream_once = p.rows <= Y_RGS;
+  const bool dma_wave = w < Y_DMA_WAVES;
 
-  const int row_local = 32 * w + n32;
-  const int row = rg * X_RGS + row_local;
+  const int row_local = 16 * w + c16;
+  const int row = rg * Y_RGS + row_local;
   const bool row_ok = row < p.rows;
-  const bool wave_active = rg * X_RGS + 32 * w < p.rows;   // wave-uniform
+  const bool wave_active = rg * Y_RGS + 16 * w < p.rows;   // wave-uniform
   int limit = 0;
   if (row_ok) {
     const int tok = row / p.heads;
@@ -193,564 +131,426 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
     limit = min(vis, t1);
   }
 
-  // ---- lane constants (byte offsets) ----
-  // K operand (key n32), bf16 k-step t: (slot + kb0) ^ ((t & 3) << 5), plus
-  // (t >> 2) * X_GSTRIDE; fp8 k-step pair u: (slot + kb0) ^ ((u & 1) << 5),
-  // plus (u >> 1) * X_GSTRIDE + 2048 * (32-key half of the slot)
-  // (kb0, computed at each use from a fresh lane id)
-  auto kb0_of = [](int ln) -> uint32_t {
-    const int n = ln & 31, h = (ln >> 5) & 1;
-    if constexpr (!F8)
-      return n * 128 + ((h ^ swz16(n)) << 4);
-    else
-      return n * 64 + (((2 * h) ^ swz8(n)) << 4);
-  };
-  // V^T operand, bf16 dim block db, 16-key step s, 4-key read x:
-  // (slot + vt0) ^ (64 (db & 1) + 32 x), plus (db >> 1) * X_GSTRIDE + 2048 s
-  // + 1024 x; fp8: (slot + vt0) ^ (32 (db & 1)), plus (db >> 1) * X_GSTRIDE
-  // + 2048 * half + 1024 s (computed at each use from a fresh lane id)
-  auto vt0_of = [](int ln) -> uint32_t {
-    const int g16 = (ln >> 4) & 1, ig = ln & 15, h = (ln >> 5) & 1;
-    if constexpr (!F8) {
-      const int j = ig >> 2, r = ig & 3;
-      return (4 * h + j) * 128 + (((2 * g16 + (r >> 1)) ^ swz16(4 * h + j)) << 4) + 8 * (r & 1);
-    } else {
-      const int jj = ig >> 1, q = ig & 1;
-      const int key = 4 * h + (jj & 3) + 8 * (jj >> 2);
-      return key * 64 + ((g16 ^ swz8(key)) << 4) + 8 * q;
-    }
-  };
-
   typedef const __attribute__((address_space(4))) int32_t const_i32;
   const_i32* bt = (const_i32*)(p.block_table + (size_t)b * p.max_blocks);
   // the block size is 64 or 128 (checked on the host): page and row offset
-  // are a shift and a mask
+  // are a shift and a mask; a slot never crosses a page (items start on
+  // 64-key boundaries)
   const int bsh = p.bs == 128 ? 7 : 6;
-  const int nsteps = (t1 - t0 + X_STEP - 1) / X_STEP;
   const int ntiles = (t1 - t0 + KT - 1) / KT;
 
-  // Issue this wave's X_NDMA transfers of slot-tile j (exactly X_NDMA VMEM
-  // instructions; the vmcnt arithmetic relies on it). A tile never crosses a
-  // page: items start on 64-key boundaries and pages hold 64 or 128 keys.
-  // Lane l of transfer n lands at slot byte n * 1024 + 16 l. bf16: column
-  // group n >> 2, key 8(n & 3) + (l >> 3), position l & 7; fp8: column group
-  // n >> 2, key 16(n & 3) + (l >> 2), position l & 3. The lane fetches the
-  // global chunk that belongs at that position.
+  // Issue this wave's Y_NDMA transfers of slot j (DMA waves only; exactly
+  // Y_NDMA VMEM instructions, which the vmcnt arithmetic relies on). Lane l
+  // of transfer n lands at slot byte n * 1024 + 16 l.
+  // bf16: transfer n = column group n >> 2, key 8 (n & 3) + (l >> 3),
+  //   position l & 7 of the key's 8 chunks (chunk c sits at c ^ (key & 7)).
+  // fp8: transfers 0-17 fill the tile of keys 0-31, 18-35 that of keys 32-63;
+  //   transfer m of a tile = column group m >> 1, key 16 (m & 1) + (l >> 2),
+  //   position l & 3 (chunk c at c ^ swz8(key)).
+  // The lane fetches the global chunk that belongs at its position.
   auto issue = [&](int j) {
     const int ts = t0 + KT * j;
     int page = bt[ts >> bsh];
     if (page < 0 || page >= p.num_blocks) page = 0;
     const char* src = reinterpret_cast<const char*>(p.kv) + ((size_t)page * p.bs + (ts & (p.bs - 1))) * ROWB;
-    const uint32_t l0 = lds_addr(smem + (j & 3) * X_TILE);
+    const uint32_t l0 = lds_addr(smem + (j & 3) * Y_SLOT);
     const int ln = fresh_lane();
-    uint32_t dma_lane[2];
-    if constexpr (!F8) {
+    auto all = [&](auto nt_tag) {
+      auto one = [&](const char* gsrc, uint32_t voff, uint32_t lds) {
+        if constexpr (decltype(nt_tag)::value)
+          lds_dma16_nt(gsrc, voff, lds);
+        else
+          lds_dma16(gsrc, voff, lds);
+      };
+      if constexpr (!F8) {
+        const uint32_t dl = (ln >> 3) * ROWB + (((ln & 7) ^ (ln >> 3)) << 4);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int key = 8 * h + (ln >> 3);   // key bits 1..3 as in transfer parity h
-        dma_lane[h] = (ln >> 3) * ROWB + (((ln & 7) ^ swz16(key)) << 4);
+        for (int i = 0; i < Y_NDMA; ++i) {
+          const int n = Y_NDMA * w + i;
+          one(src + (n & 3) * 8 * ROWB + (n >> 2) * 128, dl, l0 + n * 1024);
+        }
+      } else {
+        const int th = w >> 1;   // which 32-key tile of the slot this wave fills
+        const char* s2 = src + th * 32 * ROWB;
+        const uint32_t l2 = l0 + th * F8_TILE;
+        // transfer m's key half h = m & 1 alternates with i; wave parity
+        // decides the phase
+        uint32_t dl[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          dl[h] = (ln >> 2) * ROWB + (((ln & 3) ^ (((ln >> 4) & 1) | (2 * h))) << 4);
+        const bool odd = w & 1;
+#pragma unroll
+        for (int i = 0; i < Y_NDMA; ++i) {
+          const int m = Y_NDMA * (w & 1) + i;
+          const uint32_t voff = odd ? dl[(i + 1) & 1] : dl[i & 1];
+          one(s2 + (m & 1) * 16 * ROWB + (m >> 1) * 64, voff, l2 + m * 1024);
+        }
       }
-    } else {
-      dma_lane[0] = dma_lane[1] = (ln >> 2) * ROWB + (((ln & 3) ^ ((ln >> 4) & 3)) << 4);
-    }
-    auto one = [&](int i, auto nt_tag) {
-      const int n = w * X_NDMA + i;
-      const char* g = F8 ? src + (n & 3) * 16 * ROWB + (n >> 2) * 64 : src + (n & 3) * 8 * ROWB + (n >> 2) * 128;
-      const uint32_t v = F8 ? dma_lane[0] : dma_lane[n & 1];
-      if constexpr (decltype(nt_tag)::value)
-        lds_dma16_nt(g, v, l0 + n * 1024);
-      else
-        lds_dma16(g, v, l0 + n * 1024);
     };
-    if (stream_once) {
-#pragma unroll
-      for (int i = 0; i < X_NDMA; ++i) one(i, std::true_type{});
-    } else {
-#pragma unroll
-      for (int i = 0; i < X_NDMA; ++i) one(i, std::false_type{});
-    }
+    if (stream_once)
+      all(std::true_type{});
+    else
+      all(std::false_type{});
   };
-  // keys of slot-tile j that hold data; -1 when its page id is out of range
-  // (the tile is then zeroed and every key masked)
+  // keys of slot j that hold data; -1 when its page id is out of range (the
+  // slot is then zeroed and every key masked)
   auto valid_keys = [&](int j) {
     const int ts = t0 + KT * j;
     int page = bt[ts >> bsh];
     if (page < 0 || page >= p.num_blocks) return -1;
     return min(KT, t1 - ts);
   };
-  bool bad_page = false;
+  bool bad_page = false, tile_bad = false;
 
-  // Tile 0 is requested before q is loaded, so its latency overlaps the q
-  // loads (the compiler's own wait for q below also covers it: it was issued
-  // first); tile 1 goes out once q is resident, so that wait does not include
-  // it while every workgroup starts at once.
-  if (ntiles > 0) issue(0);
+  // Slot 0 is requested before q is loaded, so the compiler's own wait for
+  // the q loads (it cannot see the DMAs) also covers it; slots 1 and 2 go
+  // out once q is resident.
+  if (dma_wave && ntiles > 0) issue(0);
 
-  // Q^T operand: k-step t holds dims 16t + 8h .. +7 (bf16), or for fp8 (whose
-  // K reads take 16 dims per lane at once) 32(t >> 1) + 16h + 8(t & 1) .. +7.
-  // Any fixed assignment of dims to k-steps gives the same dot products.
-  // k-steps 32..35 (dims 512..575 either way) go to qrope: chunk 2(t - 32) + h
-  // of row r at position (2(t - 32) + h) ^ swz16(r) of its 128 bytes. Each
-  // wave writes and reads only its own rows.
-  // bf16 caches: k-steps 0..31 in registers (qb), 32..35 in qrope.
-  // fp8 caches: the 64-dim blocks 0..7 as hi/lo e4m3fn operands in registers
-  // (q8h, q8l: lane (row n, half h) byte j is dim 64 blk + 32 h + j, the same
-  // bijection as the K operand read below; A and B of the 32x32x64 MFMA pair
-  // their bytes by lane half and byte), block 8 (the rope dims) in qrope as
-  // chunks 4 part + 2 h + (j >> 4), part 0 = hi, 1 = lo.
-  constexpr int QREG = F8 ? 1 : D / 16 - 4;
-  bf16x8_t qb[QREG];
-  constexpr int Q8 = F8 ? 8 : 1;
-  i32x8_t q8h[Q8], q8l[Q8];
-  const int qr_off = row_local * 128;
-  const int qr_swz = swz16(row_local);
-  const uint16_t* qrow_g = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
-  // fp8: row scale 2^qe puts the row's largest |q| in [128, 256); scores are
-  // then sums of products of exact e4m3fn values, and 2^-qe is folded into
-  // this row's score scale
-  float qmul = 1.f, scale_row = p.scale_log2;
+  // ---- q operands ----
+  // bf16: qb[s] = dims 32 s + 8 g .. +7 of this lane's row for s < 16; the
+  // rope steps s = 16, 17 sit in qlds at (s - 16) * 1024 + 16 lane.
+  // fp8: the row q * 2^qe (largest |q| in [128, 256)) split into e4m3fn hi +
+  // lo codes; q8h/q8l[s] = dims 128 s + 32 g .. +31 for s < 4; the rope
+  // operand (dims 512 + 32 (g & 1) .. +31 as hi codes for g < 2, lo codes for
+  // g >= 2, so one MFMA takes both terms) sits in qlds as two 16-byte halves
+  // at hh * 1024 + 16 lane.
+  constexpr int QB = F8 ? 1 : 16;
+  bf16x8_t qb[QB];
+  i32x8_t q8h[F8 ? 4 : 1], q8l[F8 ? 4 : 1];
+  char* const qw = qlds + w * 2048;
+  float scale_row = p.scale_log2;   // fp8: times 2^-qe
+  const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
   if constexpr (!F8) {
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      const int d = 16 * t + 8 * hi;
-      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow_g + d) : make_uint4(0, 0, 0, 0);
-      if (t < QREG)
-        qb[t] = __builtin_bit_cast(bf16x8_t, v);
+    for (int s = 0; s < 18; ++s) {
+      const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
+      if (s < 16)
+        qb[s < 16 ? s : 0] = __builtin_bit_cast(bf16x8_t, v);
       else
-        *reinterpret_cast<uint4*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4)) = v;
+        *reinterpret_cast<uint4*>(qw + (s - 16) * 1024 + 16 * lane) = v;
     }
+#pragma unroll
+    for (int s = 0; s < QB; ++s) asm volatile("" ::"v"(qb[s]));
   } else {
+    uint4 v[5][4];
     float qmax = 0.f;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow_g + 64 * (c >> 2) + 32 * hi + 8 * (c & 3))
-                             : make_uint4(0, 0, 0, 0);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        qmax = fmaxf(qmax, fmaxf(fabsf(__builtin_bit_cast(float, w[i] << 16)),
-                                 fabsf(__builtin_bit_cast(float, w[i] & 0xFFFF0000u))));
-    }
-    qmax = halves_max(qmax);
-    const int qe = qmax > 0.f && qmax < INFINITY ? 8 - __builtin_amdgcn_frexp_expf(qmax) : 0;
-    qmul = __builtin_ldexpf(1.f, qe);
-    scale_row = p.scale_log2 * __builtin_ldexpf(1.f, -qe);
-#pragma unroll
-    for (int blk = 0; blk < 9; ++blk) {
-      uint32_t h8[8], l8[8];
+    for (int s = 0; s < 5; ++s)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow_g + 64 * blk + 32 * hi + 8 * c)
-                               : make_uint4(0, 0, 0, 0);
-        split_fp8x8(v, qmul, h8 + 2 * c, l8 + 2 * c);
+        const int d = s < 4 ? 128 * s + 32 * g + 8 * c : 512 + 32 * (g & 1) + 8 * c;
+        v[s][c] = row_ok ? *reinterpret_cast<const uint4*>(qrow + d) : make_uint4(0, 0, 0, 0);
+        const uint32_t w4[4] = {v[s][c].x, v[s][c].y, v[s][c].z, v[s][c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          qmax = fmaxf(qmax, fmaxf(fabsf(__builtin_bit_cast(float, w4[i] << 16)),
+                                   fabsf(__builtin_bit_cast(float, w4[i] & 0xFFFF0000u))));
       }
-      if (blk < 8) {
+    qmax = wave_max_across_groups(qmax);
+    const int qe = qmax > 0.f && qmax < INFINITY ? 8 - __builtin_amdgcn_frexp_expf(qmax) : 0;
+    const float qmul = __builtin_ldexpf(1.f, qe);
+    scale_row = p.scale_log2 * __builtin_ldexpf(1.f, -qe);
+#pragma unroll
+    for (int s = 0; s < 5; ++s) {
+      uint32_t h8[8], l8[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) split_fp8x8(v[s][c], qmul, h8 + 2 * c, l8 + 2 * c);
+      if (s < 4) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          q8h[blk < Q8 ? blk : 0][i] = static_cast<int>(h8[i]);
-          q8l[blk < Q8 ? blk : 0][i] = static_cast<int>(l8[i]);
+          q8h[s < 4 ? s : 0][i] = static_cast<int>(h8[i]);
+          q8l[s < 4 ? s : 0][i] = static_cast<int>(l8[i]);
         }
       } else {
-#pragma unroll
-        for (int part = 0; part < 2; ++part)
-#pragma unroll
-          for (int half16 = 0; half16 < 2; ++half16) {
-            const uint32_t* src = (part ? l8 : h8) + 4 * half16;
-            *reinterpret_cast<uint4*>(qrope + qr_off + (((4 * part + 2 * hi + half16) ^ qr_swz) << 4)) =
-                make_uint4(src[0], src[1], src[2], src[3]);
-          }
+        const uint32_t* r = g < 2 ? h8 : l8;
+        *reinterpret_cast<uint4*>(qw + 16 * lane) = make_uint4(r[0], r[1], r[2], r[3]);
+        *reinterpret_cast<uint4*>(qw + 1024 + 16 * lane) = make_uint4(r[4], r[5], r[6], r[7]);
       }
     }
-  }
-  // q loads (and with them tile 0, issued before) complete here, so the
-  // compiler places no wait for them inside the tile loop (it cannot see the
-  // DMAs)
-  if constexpr (!F8) {
 #pragma unroll
-    for (int t = 0; t < QREG; ++t) asm volatile("" ::"v"(qb[t]));
-  } else {
-#pragma unroll
-    for (int t = 0; t < Q8; ++t)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       // per dword: a 256-bit operand would be an x86 register class in the host pass
-      for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(q8h[t][i]), "v"(q8l[t][i]));
+      for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(q8h[s][i]), "v"(q8l[s][i]));
   }
-  // tile 1 goes out once q and tile 0 are resident
-  if (ntiles > 1) issue(1);
-  auto q_operand = [&](int t) -> bf16x8_t {
-    if (t < QREG) return qb[t];
-    return *reinterpret_cast<const bf16x8_t*>(qrope + qr_off + (((2 * (t - QREG) + hi) ^ qr_swz) << 4));
-  };
-  // The slow loop reads the register part of q from memory at every use, so
-  // the q registers die at the fast loop's exit instead of being saved to
-  // scratch there for a loop that rarely runs.
-  auto q_operand_mem = [&](int t) -> bf16x8_t {
-    if (t < QREG) {
-      const int d = 16 * t + 8 * hi;
-      const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow_g + d) : make_uint4(0, 0, 0, 0);
-      return __builtin_bit_cast(bf16x8_t, v);
-    }
-    return q_operand(t);
-  };
-  // fp8 operands of block blk: registers (blocks 0..7 in the fast loop),
-  // recomputed from memory (blocks 0..7 in the rescaling loop), or qrope
-  auto q8_rope = [&](int part) -> i32x8_t {
-    const uint4 a = *reinterpret_cast<const uint4*>(qrope + qr_off + (((4 * part + 2 * hi) ^ qr_swz) << 4));
-    const uint4 c = *reinterpret_cast<const uint4*>(qrope + qr_off + (((4 * part + 2 * hi + 1) ^ qr_swz) << 4));
-    return i32x8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z, (int)c.w};
-  };
-  auto q8_mem = [&](int blk, i32x8_t& h, i32x8_t& l) {
-    uint32_t h8[8], l8[8];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow_g + 64 * blk + 32 * hi + 8 * c)
-                             : make_uint4(0, 0, 0, 0);
-      split_fp8x8(v, qmul, h8 + 2 * c, l8 + 2 * c);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      h[i] = static_cast<int>(h8[i]);
-      l[i] = static_cast<int>(l8[i]);
-    }
-  };
+  if (dma_wave) {
+    if (ntiles > 1) issue(1);
+    if (ntiles > 2) issue(2);
+  }
 
-  f32x16_t o[DV / 32];
+  f32x4_t o[DV / 16];
 #pragma unroll
-  for (int d = 0; d < DV / 32; ++d)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
+  for (int d = 0; d < DV / 16; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-
-  // The ring runs two tiles ahead. prepare(j) makes tile j resident for
-  // every wave (wait for this wave's transfers, zero its slots of keys past
-  // the end, barrier), then issues tile j + 2 into the slot of tile j - 2,
-  // which every wave has finished with once it is past the barrier: while
-  // step k's PV reads tile(k) and step k + 1's QK reads tile(k + 1), the two
-  // tiles after them are in flight. Bit (j & 3) of bad_slots records whether
-  // tile j's page id was out of range.
-  int bad_slots = 0;
-  auto prepare = [&](int j) {
-    mem_fence_compiler();
-    if (j + 1 < ntiles)
-      wait_vmcnt<X_NDMA>();
-    else
-      wait_vmcnt<0>();
-    mem_fence_compiler();
-    char* t = smem + (j & 3) * X_TILE;
-    const int nv = valid_keys(j);
-    const bool bad = nv < 0;
-    bad_page |= bad;
-    bad_slots = (bad_slots & ~(1 << (j & 3))) | (bad ? 1 << (j & 3) : 0);
-    if (nv < KT) {
-      const int ln = fresh_lane();
-      const int lk = F8 ? (ln >> 2) : (ln >> 3);   // key within the transfer
-#pragma unroll
-      for (int i = 0; i < X_NDMA; ++i) {
-        const int n = w * X_NDMA + i;
-        if (lk >= nv - (F8 ? 16 : 8) * (n & 3))
-          *reinterpret_cast<uint4*>(t + n * 1024 + ln * 16) = make_uint4(0, 0, 0, 0);
-      }
-    }
-    __syncthreads();
-    if (j + 2 < ntiles) issue(j + 2);
-  };
-  auto tile_of = [&](int k) -> const char* { return smem + ((F8 ? k >> 1 : k) & 3) * X_TILE; };
-  // Element e of step k's scores (C layout) is a visible key iff
-  // 8(e >> 2) + (e & 3) < rel_of(k); a tile whose page id was out of range
-  // has none.
-  auto rel_of = [&](int k) -> int {
-    const int j = F8 ? k >> 1 : k;
-    return (bad_slots >> (j & 3)) & 1 ? -64 : limit - (t0 + X_STEP * k) - 4 * hi;
-  };
-
-  // S^T of step k (32 keys x this wave's 32 rows) from tile `tile`, with the
-  // operands that need no wait states (q from registers or qrope, K from
-  // LDS). between(g) runs after the MFMAs of each of the 9 groups of 64 dims:
-  // a wave issues in order and an MFMA occupies the matrix core for 32
-  // (bf16) or 64 (fp8) cycles, so VALU work placed there executes meanwhile.
-  // The K reads are software-pipelined by hand: the asm MFMAs look cheap to
-  // the scheduler, which would otherwise issue each read just before its use
-  // and expose the LDS latency every time.
-  auto qk = [&](const char* tile, int k, f32x16_t& sacc, auto&& between) {
-    const uint32_t kbase = lds_addr(tile) + kb0_of(fresh_lane());
+  // ---- lane operand offsets inside a tile ----
+  // K, bf16: key 16 mi + c16, dims 32 s + 8 g: chunk 4 (s & 1) + g of column
+  //   group s >> 1; fp8: key 16 mi + c16, bytes 32 g .. +31 of 128-dim step s:
+  //   column group 2 s + (g >> 1), chunks 2 (g & 1) + h (h = 0, 1); the rope
+  //   step reads column group 8 for every g.
+  // V^T, bf16: two 4-key transposed reads per 16 dims; fp8: one 8-key read.
+  // (computed from a fresh lane id at each use, see fresh_lane)
+  auto k_offsets = [](int ln, int (&kb)[2][2]) {
+    const int c = ln & 15, gg = ln >> 4;
     if constexpr (!F8) {
-      auto kaddr = [&](int t) { return (kbase ^ ((t & 3) << 5)) + (t >> 2) * X_GSTRIDE; };
-      bf16x8_t kr[QK_AHEAD];
 #pragma unroll
-      for (int t = 0; t < QK_AHEAD; ++t) kr[t] = lds_b128(kaddr(t));
+      for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const bf16x8_t a = kr[t % QK_AHEAD];
-        if (t + QK_AHEAD < D / 16) kr[t % QK_AHEAD] = lds_b128(kaddr(t + QK_AHEAD));
-        if (t == 0)
-          qk_first(sacc, a, q_operand(t));
-        else
-          qk_next(sacc, a, q_operand(t));
-        if ((t & 3) == 3) {
-          between(t >> 2);
-          __builtin_amdgcn_sched_barrier(0);
+        for (int par = 0; par < 2; ++par) kb[mi][par] = (16 * mi + c) * 128 + (((4 * par + gg) ^ (c & 7)) << 4);
+    } else {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          kb[mi][h] = (16 * mi + c) * 64 + (((2 * (gg & 1) + h) ^ swz8(16 * mi + c)) << 4);
+    }
+  };
+  auto v_offsets = [](int ln, int (&vt)[4]) {
+    const int c = ln & 15, gg = ln >> 4;
+    if constexpr (!F8) {
+      const int j = c >> 2, q = c & 3;
+      const int lanex = (q >> 1) ^ ((gg & 1) << 2) ^ j;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) vt[x] = (4 * gg + j) * 128 + (((2 * x) ^ lanex) << 4) + (q & 1) * 8;
+    } else {
+      const int jj = c >> 1, q = c & 1;
+      const int key = jj < 4 ? 4 * gg + jj : 16 + 4 * gg + (jj - 4);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) vt[x] = key * 64 + ((x ^ swz8(key)) << 4) + q * 8;
+    }
+  };
+
+  // S^T of 32 keys (two 16-key blocks) x this wave's 16 rows, with the K
+  // operand reads kept R MFMAs ahead of their use.
+  auto qk = [&](const char* tile, f32x4_t (&sacc)[2]) {
+    const int ln = fresh_lane();
+    int kb[2][2];
+    k_offsets(ln, kb);
+    if constexpr (!F8) {
+      constexpr int N = 36;   // MFMA i: k-step i >> 1, block i & 1
+      auto kread = [&](int i) -> bf16x8_t {
+        const int s = i >> 1, mi = i & 1;
+        return *reinterpret_cast<const bf16x8_t*>(tile + kb[mi][s & 1] + (s >> 1) * BF_GS);
+      };
+      bf16x8_t kr[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) kr[i] = kread(i);
+      bf16x8_t qr[2];
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const bf16x8_t a = kr[i % R];
+        if (i + R < N) kr[i % R] = kread(i + R);
+        if (i == 24) {
+          qr[0] = *reinterpret_cast<const bf16x8_t*>(qw + 16 * ln);
+          qr[1] = *reinterpret_cast<const bf16x8_t*>(qw + 1024 + 16 * ln);
         }
+        const int s = i >> 1;
+        const bf16x8_t bq = s < 16 ? qb[s < 16 ? s : 0] : qr[s - 16 < 0 ? 0 : s - 16];
+        sacc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, i < 2 ? f32x4_t{0.f, 0.f, 0.f, 0.f}
+                                                                           : sacc[i & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      // K operand of 64-dim block blk: key 32 half + n32, chunks 2h and
-      // 2h + 1 (dims 64 blk + 32 h .. + 31), as stored
-      auto kaddr = [&](int blk) { return kbase + blk * X_GSTRIDE + 2048 * (k & 1); };
-      auto kread = [&](int blk) -> i32x8_t {
-        const u32x4_t a = lds_u128(kaddr(blk)), c = lds_u128(kaddr(blk) ^ 16);
-        return i32x8_t{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+      // read pair i (two 16-byte chunks): 128-dim step i >> 1 (4 = rope), block i & 1
+      constexpr int N = 10;
+      constexpr int R8 = R / 2 > 0 ? R / 2 : 1;
+      const char* kg = tile + ((ln >> 5) & 1) * F8_GS;
+      auto kread = [&](int i) -> i32x8_t {
+        const int s = i >> 1, mi = i & 1;
+        const char* base = s < 4 ? kg + 2 * s * F8_GS : tile + 8 * F8_GS;
+        const u32x4_t x = lds_u128(base + kb[mi][0]), y = lds_u128(base + kb[mi][1]);
+        return i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
       };
-      i32x8_t kr = kread(0);
+      i32x8_t kr[R8];
 #pragma unroll
-      for (int blk = 0; blk < 9; ++blk) {
-        const i32x8_t a = kr;
-        if (blk + 1 < 9) kr = kread(blk + 1);
-        if (blk == 8) {
-          qk8_next(sacc, a, q8_rope(0));
-          qk8_next(sacc, a, q8_rope(1));
-        } else {
-          if (blk == 0)
-            qk8_first(sacc, a, q8h[blk]);
-          else
-            qk8_next(sacc, a, q8h[blk]);
-          qk8_next(sacc, a, q8l[blk]);
+      for (int i = 0; i < R8; ++i) kr[i] = kread(i);
+      i32x8_t qr;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const i32x8_t a = kr[i % R8];
+        if (i + R8 < N) kr[i % R8] = kread(i + R8);
+        if (i == 6) {
+          const u32x4_t x = lds_u128(qw + 16 * ln), y = lds_u128(qw + 1024 + 16 * ln);
+          qr = i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
         }
-        between(blk);
+        const int s = i >> 1, mi = i & 1;
+        if (s < 4) {
+          sacc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a, q8h[s < 4 ? s : 0], s == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : sacc[mi], 0, 0, 0, 0, 0, 0);
+          sacc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, q8l[s < 4 ? s : 0], sacc[mi], 0, 0, 0, 0,
+                                                                      0, 0);
+        } else {
+          sacc[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qr, sacc[mi], 0, 0, 0, 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
-  auto qk_wait = [&](f32x16_t& sacc) {
-    if constexpr (F8)
-      qk8_done(sacc);
-    else
-      qk_done(sacc);
-  };
 
-  // O^T += V^T P^T over step k's two 16-key halves (tile `tile`): 32 MFMAs,
-  // MFMA i on dim block i & 15 of half i >> 4. The V^T reads run PV_AHEAD
-  // MFMAs ahead through a ring of raw operands, and the operand of MFMA i + 1
-  // is assembled (widened, for fp8) right after MFMA i issues, in its shadow.
-  // The order is fixed per MFMA: left to the scheduler, the reads sink to
-  // their uses under the loop's register pressure and each MFMA waits for a
-  // full LDS round trip.
-  auto pv = [&](const char* tile, int k, const bf16x8_t* pb) {
-    const int half = F8 ? (k & 1) : 0;   // fp8: which 32 keys of the 64-key slot
-    const uint32_t vbase = lds_addr(tile) + vt0_of(fresh_lane());
-    constexpr int NPV = 2 * (DV / 32);
-    typedef std::conditional_t<F8, uint2, uint4> raw_t;
-    auto vread = [&](int i) -> raw_t {
-      const int s = i >> 4, db = i & 15;
-      if constexpr (!F8) {
-        const uint32_t off = (db >> 1) * X_GSTRIDE + 2048 * s;
-        const uint2 a0 = __builtin_bit_cast(uint2, lds_tr16((vbase ^ (64 * (db & 1))) + off));
-        const uint2 a1 = __builtin_bit_cast(uint2, lds_tr16((vbase ^ (64 * (db & 1) + 32)) + off + 1024));
-        return make_uint4(a0.x, a0.y, a1.x, a1.y);
-      } else {
-        return lds_tr8((vbase ^ (32 * (db & 1))) + (db >> 1) * X_GSTRIDE + 2048 * half + 1024 * s);
-      }
-    };
-    auto operand = [&](const raw_t& r) -> bf16x8_t {
-      if constexpr (!F8)
-        return __builtin_bit_cast(bf16x8_t, r);
-      else
-        return __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(r.x, r.y));
-    };
-    raw_t vr[PV_AHEAD];
-#pragma unroll
-    for (int i = 0; i < PV_AHEAD; ++i) vr[i] = vread(i);
-    bf16x8_t a = operand(vr[0]);
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      o[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[i >> 4], o[i & 15], 0, 0, 0);
-      if (i + PV_AHEAD < NPV) vr[i % PV_AHEAD] = vread(i + PV_AHEAD);
-      if (i + 1 < NPV) a = operand(vr[(i + 1) % PV_AHEAD]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // Online softmax of one step's raw scores (the scale is folded into the
-  // max and the FMA), in 8 stages so that the fast loop can spread it over
-  // the next step's QK MFMAs; each stage pins its results (an empty asm that
-  // takes them as operands), which keeps the compiler from sinking the work
-  // past the QK chain to where it is used. Stage 2 decides whether the step
-  // stays on the fast path: no row's max more than BIG_SLACK above its
-  // reference (which a row's first keys set). The stages leave m_run, l_run
-  // and O alone otherwise; the caller adds lsum to l_run once the step is
-  // accepted.
-  float sx[16], tmax = 0.f, neg_m = 0.f, lsum = 0.f;
-  bool jump = false;
-  bf16x8_t pb[2];
-  auto pin = [](float& v) { asm volatile("" : "+v"(v)); };
-  auto smx = [&](int st, const f32x16_t& sc, int rel) {
-    if (st == 0) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sx[e] = sc[e];
-      // keys past a row's limit or on a bad page (rare: a uniform branch)
-      if (__builtin_amdgcn_ballot_w64(rel < 28)) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sx[e] = 8 * (e >> 2) + (e & 3) < rel ? sx[e] : -INFINITY;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) pin(sx[e]);
-    } else if (st == 1) {
-      tmax = fmaxf(fmaxf(fmaxf(sx[0], sx[1]), fmaxf(sx[2], sx[3])), fmaxf(fmaxf(sx[4], sx[5]), fmaxf(sx[6], sx[7])));
-      tmax = fmaxf(tmax, fmaxf(fmaxf(fmaxf(sx[8], sx[9]), fmaxf(sx[10], sx[11])),
-                               fmaxf(fmaxf(sx[12], sx[13]), fmaxf(sx[14], sx[15]))));
-      pin(tmax);
-    } else if (st == 2) {
-      tmax = halves_max(tmax) * scale_row;
-      if (m_run == -INFINITY) m_run = tmax;   // o and l of this row are still zero
-      jump = __builtin_amdgcn_ballot_w64(tmax > m_run + BIG_SLACK) != 0;
-      // rows without any key so far keep m = -inf: a finite stand-in makes
-      // their masked scores give exp2(-inf) = 0, never NaN
-      neg_m = -fmaxf(m_run, -1e30f);
-      lsum = 0.f;
-      pin(m_run);
-      pin(neg_m);
-    } else if (st <= 6) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * (st - 3) + i;
-        sx[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[e], scale_row, neg_m));
-        lsum += sx[e];
-        pin(sx[e]);
-      }
-      pin(lsum);
-    } else if (st == 7) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        pb[s] = __builtin_bit_cast(
-            bf16x8_t, make_uint4(pack_bf16x2(sx[8 * s], sx[8 * s + 1]), pack_bf16x2(sx[8 * s + 2], sx[8 * s + 3]),
-                                 pack_bf16x2(sx[8 * s + 4], sx[8 * s + 5]),
-                                 pack_bf16x2(sx[8 * s + 6], sx[8 * s + 7])));
-        asm volatile("" : "+v"(pb[s]));
-      }
-    }
-  };
-
-  // One step with rescaling (the rare path after a row's max jumped): the q
-  // operands are re-read from memory (so q's registers die at the fast
-  // loop's exit instead of being saved to scratch for a loop that rarely
-  // runs) and reach the MFMAs through VALU code, hence the forms with wait
-  // states; every row is rescaled by alpha = 2^(m_old - m_new) (1 for rows
-  // whose max did not move: a conditional rescale merges two versions of O
-  // and makes the compiler hold all of O in VGPRs).
-  auto compute_slow = [&](const char* tile, int k, int rel) {
-    f32x16_t sacc;
-    const uint32_t kbase = lds_addr(tile) + kb0_of(fresh_lane());
+  // O^T += V^T P^T over 32 keys: 32 MFMAs (16 dims each), the V^T reads R
+  // MFMAs ahead; an fp8 operand is widened right after the previous MFMA
+  // issues.
+  auto pv = [&](const char* tile, const bf16x8_t& pb) {
+    int vt[4];
+    v_offsets(fresh_lane(), vt);
     if constexpr (!F8) {
-      auto kaddr = [&](int t) { return (kbase ^ ((t & 3) << 5)) + (t >> 2) * X_GSTRIDE; };
-      bf16x8_t kr[QK_AHEAD];
+      auto vread = [&](int dt) -> uint4 {
+        const char* src = tile + vt[dt & 3] + (dt >> 2) * BF_GS;
+        const uint2 a0 = __builtin_bit_cast(uint2, read_vt(src));
+        const uint2 a1 = __builtin_bit_cast(uint2, read_vt(src + 16 * 128));
+        return make_uint4(a0.x, a0.y, a1.x, a1.y);
+      };
+      uint4 vr[R];
 #pragma unroll
-      for (int t = 0; t < QK_AHEAD; ++t) kr[t] = lds_b128(kaddr(t));
+      for (int i = 0; i < R; ++i) vr[i] = vread(i);
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const bf16x8_t a = kr[t % QK_AHEAD];
-        if (t + QK_AHEAD < D / 16) kr[t % QK_AHEAD] = lds_b128(kaddr(t + QK_AHEAD));
-        const bf16x8_t qv = q_operand_mem(t);
-        if (t == 0)
-          qk_first_v(sacc, a, qv);
-        else
-          qk_next_v(sacc, a, qv);
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, vr[dt % R]);
+        if (dt + R < DV / 16) vr[dt % R] = vread(dt + R);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      auto kaddr = [&](int blk) { return kbase + blk * X_GSTRIDE + 2048 * (k & 1); };
-      auto kread = [&](int blk) -> i32x8_t {
-        const u32x4_t a = lds_u128(kaddr(blk)), c = lds_u128(kaddr(blk) ^ 16);
-        return i32x8_t{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
-      };
+      auto vread = [&](int dt) -> uint2 { return lds_tr8(tile + vt[dt & 3] + (dt >> 2) * F8_GS); };
+      uint2 vr[R];
 #pragma unroll
-      for (int blk = 0; blk < 9; ++blk) {
-        const i32x8_t a = kread(blk);
-        i32x8_t h, l;
-        if (blk == 8) {
-          h = q8_rope(0);
-          l = q8_rope(1);
-        } else {
-          q8_mem(blk, h, l);
-        }
-        if (blk == 0)
-          qk8_first_v(sacc, a, h);
-        else
-          qk8_next_v(sacc, a, h);
-        qk8_next_v(sacc, a, l);
+      for (int i = 0; i < R; ++i) vr[i] = vread(i);
+      bf16x8_t a = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(vr[0].x, vr[0].y));
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
+        if (dt + R < DV / 16) vr[dt % R] = vread(dt + R);
+        if (dt + 1 < DV / 16)
+          a = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(vr[(dt + 1) % R].x, vr[(dt + 1) % R].y));
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    qk_wait(sacc);
-    smx(0, sacc, rel);
-    smx(1, sacc, rel);
-    tmax = halves_max(tmax) * scale_row;
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);   // m_run = -inf gives 0
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int d = 0; d < DV / 32; ++d) {
-      o[d] *= alpha;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    neg_m = -fmaxf(m_run, -1e30f);
-    lsum = 0.f;
-#pragma unroll
-    for (int st = 3; st < 8; ++st) smx(st, sacc, rel);
-    l_run += lsum;
-    __builtin_amdgcn_sched_barrier(0);
-    pv(tile, k, pb);
   };
 
-  // Fast loop, software-pipelined across steps: step k + 1's QK MFMAs are
-  // interleaved with step k's softmax, then step k's PV follows.
-  if (ntiles > 0) prepare(0);
-  int k = 0;
-  if (!wave_active) {
-    // rows past the end: no compute, but the same barriers and transfers
-    for (int j = 1; j < ntiles; ++j) prepare(j);
-    k = nsteps;
-  } else if (nsteps > 0) {
-    f32x16_t s_cur;
-    int rel_cur = rel_of(0);
-    qk(tile_of(0), 0, s_cur, [](int) {});
-    qk_wait(s_cur);
-    bool jumped = false;
-    for (; k + 1 < nsteps; ++k) {
-      if (!F8 || (k & 1)) prepare(F8 ? (k + 1) >> 1 : k + 1);
-      const int rel_nxt = rel_of(k + 1);
-      f32x16_t s_nxt;
-      qk(tile_of(k + 1), k + 1, s_nxt, [&](int g) { smx(g, s_cur, rel_cur); });
-      // the compiler may move or copy s_nxt (or reuse its registers when the
-      // step is dropped) right after the chain: wait for the last MFMA first
-      // (its wait states overlap that MFMA's own passes)
-      qk_wait(s_nxt);
-      if (jump) {
+  // One 32-key step. The fast variant never touches the accumulators with
+  // VALU code and returns false (before consuming the step) if a row's max
+  // jumped more than BIG_SLACK above its reference; the slow variant rescales.
+  auto compute = [&](const char* tile, int ts, auto slow_tag) -> bool {
+    constexpr bool SLOW = decltype(slow_tag)::value;
+    f32x4_t sacc[2];
+    qk(tile, sacc);
+    float x[2][4];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[mi][e] = sacc[mi][e];
+    // a step that reaches a row's limit, or whose page id was out of range
+    if (tile_bad || __builtin_amdgcn_ballot_w64(ts + 32 > limit)) {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = ts + 16 * mi + 4 * g + e;
+          x[mi][e] = key < limit && !tile_bad ? x[mi][e] : -INFINITY;
+        }
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+    tmax = max4_groups(tmax) * scale_row;
+    if constexpr (!SLOW) {
+      if (m_run == -INFINITY) m_run = tmax;   // o and l of this row are still zero
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + BIG_SLACK)) return false;
+    } else {
+      const bool need = tmax > m_run;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        float alpha = 1.f;
+        if (need) {
+          alpha = exp2f(m_run - tmax);   // m_run = -inf gives 0
+          m_run = tmax;
+        }
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DV / 16; ++d) o[d] *= alpha;
+      }
+    }
+    // a row without any key so far keeps m = -inf: a finite stand-in makes its
+    // masked scores (-inf) give exp2(-inf) = 0, never NaN
+    const float neg_m = -fmaxf(m_run, -1e30f);
+    float e[2][4];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        e[mi][jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[mi][jj], scale_row, neg_m));
+        l_run += e[mi][jj];
+      }
+    const bf16x8_t pb = __builtin_bit_cast(
+        bf16x8_t, make_uint4(pack_bf16x2(e[0][0], e[0][1]), pack_bf16x2(e[0][2], e[0][3]),
+                             pack_bf16x2(e[1][0], e[1][1]), pack_bf16x2(e[1][2], e[1][3])));
+    pv(tile, pb);
+    return true;
+  };
+
+  // Make slot j resident for every wave: wait for this wave's transfers of
+  // it (three slots are in flight at most), zero the keys past the end in
+  // this wave's transfers, barrier, then issue slot j + 3 into the slot every
+  // wave finished with before the barrier.
+  auto prepare = [&](int j) -> const char* {
+    char* cur = smem + (j & 3) * Y_SLOT;
+    if (dma_wave) {
+      mem_fence_compiler();
+      const int ahead = min(2, ntiles - 1 - j);
+      if (ahead >= 2)
+        wait_vmcnt<2 * Y_NDMA>();
+      else if (ahead == 1)
+        wait_vmcnt<Y_NDMA>();
+      else
+        wait_vmcnt<0>();
+      mem_fence_compiler();
+    }
+    const int nv = valid_keys(j);
+    tile_bad = nv < 0;
+    bad_page |= tile_bad;
+    if (dma_wave && nv < KT) {
+#pragma unroll
+      for (int i = 0; i < Y_NDMA; ++i) {
+        const int n = Y_NDMA * w + i;
+        const int key = F8 ? 32 * (n >= 18) + 16 * ((n - 18 * (n >= 18)) & 1) + (lane >> 2)
+                           : 8 * (n & 3) + (lane >> 3);
+        if (key >= nv) *reinterpret_cast<uint4*>(cur + n * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    if (dma_wave && j + 3 < ntiles) issue(j + 3);
+    return cur;
+  };
+
+  // tile of the sub-step u (fp8: two 32-key steps per slot)
+  auto step_tile = [&](const char* cur, int u) -> const char* { return F8 ? cur + u * F8_TILE : cur; };
+  constexpr int SUB = F8 ? 2 : 1;
+  int j = 0, u = 0;
+  const char* cur = nullptr;
+  bool jumped = false;
+  for (; j < ntiles; ++j) {
+    cur = prepare(j);
+    if (!wave_active) continue;
+    for (u = 0; u < SUB; ++u) {
+      const int ts = t0 + KT * j + 32 * u;
+      if (ts >= t1) break;
+      if (!compute(step_tile(cur, u), ts, std::false_type{})) {
         jumped = true;
         break;
       }
-      l_run += lsum;
-      pv(tile_of(k), k, pb);
-      s_cur = s_nxt;
-      rel_cur = rel_nxt;
     }
-    if (!jumped) {
-#pragma unroll
-      for (int g = 0; g < 8; ++g) smx(g, s_cur, rel_cur);
-      if (!jump) {
-        l_run += lsum;
-        pv(tile_of(k), k, pb);
-        ++k;
-      }
+    if (jumped) break;
+  }
+  if (jumped) {   // rare: finish with rescaling, from sub-step u of the resident slot j
+    for (; u < SUB; ++u) {
+      const int ts = t0 + KT * j + 32 * u;
+      if (ts < t1) compute(step_tile(cur, u), ts, std::true_type{});
     }
-    // rare: finish with rescaling, from step k, whose tile is resident (as
-    // is the next step's)
-    if (k < nsteps) {
-      int prepared = F8 ? min(k + 1, nsteps - 1) >> 1 : min(k + 1, nsteps - 1);
-      for (; k < nsteps; ++k) {
-        const int j = F8 ? k >> 1 : k;
-        if (j > prepared) {
-          prepare(j);
-          prepared = j;
-        }
-        compute_slow(tile_of(k), k, rel_of(k));
+    for (++j; j < ntiles; ++j) {
+      cur = prepare(j);
+      for (u = 0; u < SUB; ++u) {
+        const int ts = t0 + KT * j + 32 * u;
+        if (ts < t1) compute(step_tile(cur, u), ts, std::true_type{});
       }
     }
   }
@@ -758,70 +558,40 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide128(FwdParams p) {
   flag_bad_page(p.flags, bad_page);
 
   // ---- write this wave's rows: final (slot < 0) or split partial ----
-  // The rows leave through LDS (the ring is free once every wave is past its
-  // last step): a wave stages its 32 rows x 256 dims at a time, then writes
-  // whole row segments, so each store instruction covers 512 B of one row
-  // (bf16 out or fp16 partial) instead of scattered 16-byte pieces.
-  // Lane-derived values are derived afresh here, from the lane id, rather
-  // than kept from the prologue: kept, they stay live across the tile loop
-  // and come back as scratch reloads, each a memory round trip.
-  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  const int n32_e = lane_e & 31, hi_e = lane_e >> 5;
-  const int row_local_e = 32 * w + n32_e;
-  const int row_e = rg * X_RGS + row_local_e;
-  const bool row_ok_e = row_e < p.rows;
-  const float l_row = halves_sum(l_run);
+  const float l_row = wave_sum_across_groups(l_run);
   const bool empty = !(l_row > 0.f);
   const float inv = empty ? 0.f : p.out_scale / l_row;
-  const float lse2 = empty ? -INFINITY : m_run + log2f(l_row);
-  // A split partial row leaves as fp16 o * 2^k (partial_exponent). Here 2^k
-  // is folded into the normalisation factor, with k capped so that inv * 2^k
-  // stays finite (which only matters for rows whose values are all far below
-  // 2^-100).
-  int kexp = 0;
+  int kexp = 0;   // split partials: fp16 o * 2^k (partial_exponent)
   if (slot >= 0) {
     float amax = 0.f;
 #pragma unroll
-    for (int db = 0; db < DV / 32; ++db)
+    for (int dt = 0; dt < DV / 16; ++dt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[db][e]));
-    amax = halves_max(amax) * inv;   // this row's largest |o| after normalisation
-    kexp = min(partial_exponent(amax), 127 - __builtin_amdgcn_frexp_expf(inv));
+      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(o[dt][e]));
+    kexp = min(partial_exponent(wave_max_across_groups(amax) * inv), 127 - __builtin_amdgcn_frexp_expf(inv));
   }
-  const float fs = __builtin_ldexpf(inv, kexp);   // normalisation and 2^k in one factor
-  if (row_ok_e && hi_e == 0) {
+  if (row_ok) {
+    const float lse2 = empty ? -INFINITY : m_run + log2f(l_row);
+    const size_t orow = (size_t)b * p.rows + row;
+    const float fs = __builtin_ldexpf(inv, kexp);
     if (slot < 0) {
-      if (p.lse != nullptr) p.lse[(size_t)b * p.rows + row_e] = lse2 * LN2;
-    } else {
-      p.part_lse[(size_t)slot * X_RGS + row_local_e] = lse2;
-      p.part_scale[(size_t)slot * X_RGS + row_local_e] = kexp;
-    }
-  }
-  __syncthreads();   // every wave is done with the ring
-  constexpr int SROW = 260;   // floats per staged row: 256 + 4 (rows 16 bytes apart in the banks)
-  static_assert(4 * 32 * SROW * 4 <= X_SLOTS * X_TILE, "staging fits in the ring");
-  float* stage = reinterpret_cast<float*>(smem) + w * 32 * SROW;
-  const int nrow = min(32, p.rows - (rg * X_RGS + 32 * w));   // this wave's valid rows (wave-uniform)
+      uint16_t* dst = p.out + orow * DV + 4 * g;
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-    for (int db = 0; db < DV / 64; ++db)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x16_t& a = o[(DV / 64) * hf + db];
-        *reinterpret_cast<f32x4_t*>(stage + n32_e * SROW + 32 * db + 8 * q + 4 * hi_e) =
-            f32x4_t{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]} * fs;
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        const f32x4_t v = o[dt] * fs;
+        *reinterpret_cast<uint2*>(dst + 16 * dt) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
-    // a wave's LDS accesses complete in order: the reads below see the writes
-    for (int r = 0; r < nrow; ++r) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + r * SROW + 4 * lane_e);
-      const int rl = 32 * w + r;
-      if (slot < 0) {
-        uint16_t* dst = p.out + ((size_t)b * p.rows + rg * X_RGS + rl) * DV + (DV / 2) * hf + 4 * lane_e;
-        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      } else {
-        _Float16* dst = p.part_o + ((size_t)slot * X_RGS + rl) * DV + (DV / 2) * hf + 4 * lane_e;
-        *reinterpret_cast<f16x4_t*>(dst) = __builtin_convertvector(v, f16x4_t);
+      if (p.lse != nullptr && g == 0) p.lse[orow] = lse2 * LN2;
+    } else {
+      _Float16* dst = p.part_o + ((size_t)slot * Y_RGS + row_local) * DV + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        const f32x4_t v = o[dt] * fs;
+        *reinterpret_cast<f16x4_t*>(dst + 16 * dt) = __builtin_convertvector(v, f16x4_t);
+      }
+      if (g == 0) {
+        p.part_lse[(size_t)slot * Y_RGS + row_local] = lse2;
+        p.part_scale[(size_t)slot * Y_RGS + row_local] = kexp;
       }
     }
   }
@@ -833,9 +603,9 @@ namespace mla_detail {
 
 void launch_wide128(int kv_dtype, dim3 grid, hipStream_t st, const FwdParams& fp) {
   if (kv_dtype == MLA_DTYPE_BF16)
-    hipLaunchKernelGGL((mla_decode_wide128<MLA_DTYPE_BF16>), grid, dim3(NTHREADS), 0, st, fp);
+    hipLaunchKernelGGL((mla_decode_wide128<MLA_DTYPE_BF16>), grid, dim3(Y_THREADS), 0, st, fp);
   else
-    hipLaunchKernelGGL((mla_decode_wide128<MLA_DTYPE_FP8_E4M3FN>), grid, dim3(NTHREADS), 0, st, fp);
+    hipLaunchKernelGGL((mla_decode_wide128<MLA_DTYPE_FP8_E4M3FN>), grid, dim3(Y_THREADS), 0, st, fp);
 }
 
 }  // namespace mla_detail
