@@ -38,14 +38,11 @@ constexpr int G_TN_MAX = 512;                   // output columns per tile (at m
 #define ABSO_TPW 32
 #endif
 
-#ifndef RSQ_TPW
-#define RSQ_TPW 32
+#ifndef RSQ_WGS
+#define RSQ_WGS 256
 #endif
-#ifndef RSQ_AHT
-#define RSQ_AHT 4
-#endif
-#ifndef RSQ_NW
-#define RSQ_NW 8
+#ifndef RSQ_DEPTH
+#define RSQ_DEPTH 8
 #endif
 
 struct GemmParams {
@@ -282,41 +279,116 @@ __global__ __launch_bounds__(G_THREADS) void mla_bgemm_ws_kernel(GemmParams p) {
 // keeps its 16 * NTW-column slice of the head's B (all K rows) in VGPRs as
 // MFMA operands (NTW x K/32 fragments), so
 // the main loop reads only A and has no LDS traffic for B. A workgroup runs
-// RS_TPW tiles of 16 tokens; every tile is staged in LDS as complete output
-// rows (absorb_q: the 512 latent columns and the copied q_pe), which leave as
-// contiguous runs (1152 bytes per q row) instead of per-slice pieces.
-// B enters the registers through a per-wave LDS staging area, 32 rows at a
-// time, read back with the transposed reads (no workgroup barrier: each wave
-// stages and reads only its own area). One workgroup per (token group, head),
-// head fastest: workgroups that run together read neighbouring A rows and
-// write neighbouring output rows.
-constexpr int RS_TM = 16;        // tokens per tile
-template <int K, int NW, int NTW, int AHT, int TPW, bool PE>   // NW waves; AHT: tiles of A read ahead
-__global__ __launch_bounds__(NW * 64) void mla_bgemm_rs_kernel(GemmParams p) {
-  constexpr int NTH = NW * 64;
+// Byte range [base, base + bytes) as a buffer resource (gfx9 descriptor,
+// 32-bit data format, no stride, no swizzle). A buffer load whose offset lies
+// outside the range returns zeros and such a store is dropped, so every lane
+// of a wave can issue the same memory instructions: no branch around a load
+// or a store, and the compiler's count of outstanding memory operations stays
+// exact (a conditional load or a store loop of unknown length makes it wait
+// for all of them, stores included).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t byte_range(const void* base, long long bytes) {
+  const int n = bytes <= 0 ? 0 : static_cast<int>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+constexpr uint32_t OUT_OF_RANGE = 0x80000000u;   // an offset past every range built here
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, off, 0, 0);
+}
+
+// absorb_q with d_nope = 128: q[t, h, 0:512] = q_nope[t, h, :] . W_UK[h] and
+// q[t, h, 512:576] = q_pe[t, h, :]. One workgroup per (token range, head),
+// 9 waves in two roles:
+// - a loader wave copies each 16-token tile of q_nope (4 KB) and q_pe (2 KB)
+//   HBM -> LDS (global_load_lds_dwordx4, non-temporal) into a ring of D tile
+//   slots, D - 1 tiles ahead. It issues nothing else, so its vmcnt waits
+//   cover its own copies only.
+// - 8 compute waves each keep a 128 x 64 column slice of W_UK[h] in VGPRs as
+//   MFMA fragments (loaded once through a per-wave LDS staging area and the
+//   transposed LDS reads), read the tile's A fragments from the ring, and
+//   write results straight from the accumulators: two v_permlane16_swap per
+//   register pair turn the 4-column pieces of lanes g and g + 1 into 16-byte
+//   runs, so a wave writes its 128-byte slice of a row in two back-to-back
+//   stores. Wave w also copies q_pe rows 2w and 2w + 1 of the tile. These
+//   waves issue stores only and never wait for memory.
+// Vector memory operations of a wave retire in issue order; with loads and
+// stores in one wave, every load would also wait for the write
+// acknowledgements of the stores before it, and under a write-heavy stream
+// those arrive late. One barrier per tile hands a slot from the loader to the
+// compute waves and back. Rows past the last token: the copies read the last
+// valid row again and the buffer stores drop them.
+constexpr int RS_TM = 16;             // tokens per tile
+constexpr int RS_NW = 8;              // compute waves
+constexpr int RS_THREADS = (RS_NW + 1) * 64;
+constexpr int RS_ATILE = RS_TM * 256; // q_nope tile bytes (d_nope = 128)
+constexpr int RS_SLOT = RS_ATILE + RS_TM * 128;
+constexpr int RS_NDMA = RS_SLOT / 1024;   // loader transfers per tile
+template <int D>   // ring slots
+__global__ __launch_bounds__(RS_THREADS) void mla_absorb_q_rs_kernel(GemmParams p, int tpw) {
+  constexpr int K = 128, N = 512, NW = RS_NW;
+  constexpr int NTW = N / 16 / NW;               // 16-column blocks per wave
   constexpr int WCOL = 16 * NTW;                 // columns per wave
-  constexpr int N = NW * WCOL;                   // columns per workgroup (= p.N)
-  constexpr int SROW = WCOL * 2 + 8;             // staging row (bytes)
-  constexpr int OUTC = N + (PE ? 64 : 0);        // staged output columns
-  constexpr int CROW = OUTC * 2 + 16;            // LDS row of the staged tile
+  constexpr int SROW = WCOL * 2 + 8;             // staging row of B (bytes)
   constexpr int KS = K / G_TK;                   // k-steps
   constexpr int STG = NW * G_TK * SROW;
-  constexpr int CST = RS_TM * CROW;
-  constexpr int AH = AHT * KS;                   // ring slots: flat k-steps ahead
-  static_assert(TPW % AHT == 0, "the tile loop is unrolled by AHT");
-  __shared__ __attribute__((aligned(16))) char lds[STG > CST ? STG : CST];
+  static_assert(NTW == 4 && RS_TM == 2 * NW, "the output swaps assume 64 columns and 2 q_pe rows per wave");
+  static_assert(D >= 2 && RS_NDMA * (D - 1) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) char lds[STG + D * RS_SLOT];
+  char* const ring = lds + STG;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-  const int jj = (lane >> 2) & 3, qq = lane & 3;
-  const int tiles = (p.T + RS_TM - 1) / RS_TM;
-  const int groups = (tiles + TPW - 1) / TPW;
-  const int pair = blockIdx.x;   // (token group, head), head fastest
-  if (pair >= groups * p.H) return;
-  const int h = pair % p.H;
-  const int tile0 = (pair / p.H) * TPW;
-  const int ntile = min(TPW, tiles - tile0);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int h = blockIdx.x % p.H;
+  const int row0 = (blockIdx.x / p.H) * tpw * RS_TM;
+  if (row0 >= p.T) return;
+  const int rows = min(tpw * RS_TM, p.T - row0);
+  const int ntile = (rows + RS_TM - 1) / RS_TM;
+  const long long ra_row = (long long)p.H * p.lda * 2;   // bytes between consecutive tokens
+  const long long rc_row = (long long)p.H * p.ldc * 2;
+  const long long rp_row = (long long)p.H * 64 * 2;
+  const char* a0 = reinterpret_cast<const char*>(p.a + ((size_t)row0 * p.H + h) * p.lda);
+  const char* p0 = reinterpret_cast<const char*>(p.pe + ((size_t)row0 * p.H + h) * 64);
 
-  // ---- B slice of this wave into registers: frag[nt][s] ----
+  if (w == NW) {
+    // ---- loader. Slot layout: q_nope row r (256 B) at r * 256 with its
+    // 16-byte chunk c at position c ^ r (the compute waves' 16-byte reads
+    // are then free of bank conflicts); q_pe row r at RS_ATILE + r * 128.
+    // Transfer j, lane l fills slot bytes 1024 j + 16 l.
+    const uint32_t ring_lds = lds_addr(ring);
+    auto issue = [&](int u) {
+      const uint32_t sl = ring_lds + (u % D) * RS_SLOT;
+#pragma unroll
+      for (int j = 0; j < RS_NDMA; ++j) {
+        const int pos = 64 * j + lane;                  // 16-byte position in the slot
+        if (j < RS_ATILE / 1024) {
+          const int r = pos >> 4, c = (pos & 15) ^ r;
+          const int t = min(u * RS_TM + r, rows - 1);
+          lds_dma16_nt(a0, (uint32_t)(t * ra_row) + 16 * c, sl + 1024 * j);
+        } else {
+          const int q = pos - RS_ATILE / 16, r = q >> 3, c = q & 7;
+          const int t = min(u * RS_TM + r, rows - 1);
+          lds_dma16_nt(p0, (uint32_t)(t * rp_row) + 16 * c, sl + 1024 * j);
+        }
+      }
+    };
+    for (int u = 0; u < D - 1; ++u) issue(u);
+    for (int u = 0; u < ntile; ++u) {
+      wait_vmcnt<RS_NDMA * (D - 2)>();   // tile u has landed (tiles u+1 .. u+D-2 may be in flight)
+      __syncthreads();                  // slot u to the compute waves; slot u-1 is free again
+      issue(u + D - 1);                 // into slot (u - 1) % D
+    }
+    wait_vmcnt<0>();   // no copy may land after the workgroup's LDS is released
+    return;
+  }
+
+  // ---- compute waves: B slice of this wave into registers, frag[nt][s] ----
+  const int jj = (lane >> 2) & 3, qq = lane & 3;
   bf16x8_t frag[NTW][KS];
   {
     char* st = lds + w * G_TK * SROW;
@@ -341,73 +413,51 @@ __global__ __launch_bounds__(NW * 64) void mla_bgemm_rs_kernel(GemmParams p) {
       }
     }
   }
-  __syncthreads();   // the staging areas become the output tile
 
-  // A fragments, flat k-step f = u * KS + s, AH ahead in a register ring
-  const int total = ntile * KS;
-  auto load_a = [&](int f) {
-    const int u = f / KS, s = f - u * KS;
-    const int t = (tile0 + u) * RS_TM + c16;
-    if (t >= p.T) return make_uint4(0, 0, 0, 0);
-    return *reinterpret_cast<const uint4*>(p.a + ((size_t)t * p.H + h) * p.lda + s * G_TK + 8 * g);
-  };
-  uint4 ring[AH];
-#pragma unroll
-  for (int i = 0; i < AH; ++i) ring[i] = i < total ? load_a(i) : make_uint4(0, 0, 0, 0);
-  // absorb_q: q_pe chunk (row tid >> 3, 16 bytes tid & 7) of tile u, AHT tiles
-  // ahead as well (threads 0..127): a load issued within its own tile would
-  // hold every tile's barrier for a memory round trip
-  auto load_pe = [&](int u) {
-    const int t = (tile0 + u) * RS_TM + (tid >> 3);
-    if (!PE || tid >= RS_TM * 8 || u >= ntile || t >= p.T) return make_uint4(0, 0, 0, 0);
-    return *reinterpret_cast<const uint4*>(p.pe + ((size_t)t * p.H + h) * 64 + 8 * (tid & 7));
-  };
-  uint4 pe_ring[AHT];
-#pragma unroll
-  for (int i = 0; i < AHT; ++i) pe_ring[i] = load_pe(i);
-
-  // the tile loop is unrolled by AHT so that every ring slot is a constant:
-  // flat k-step (u0 + uu) * KS + s sits in slot uu * KS + s
-  for (int u0 = 0; u0 < ntile; u0 += AHT)
-#pragma unroll
-  for (int uu = 0; uu < AHT; ++uu) {
-    const int u = u0 + uu;
-    if (u >= ntile) break;
-    const int t0 = (tile0 + u) * RS_TM;
+  const char* c0 = reinterpret_cast<const char*>(p.c + ((size_t)row0 * p.H + h) * p.ldc);
+  // After the swaps lane (c16, g) holds the 16-byte runs of row c16 at
+  // columns w * 64 + {0, 16, 8, 24}[g] and + 32.
+  const uint32_t c_off = (uint32_t)(c16 * rc_row) + 2 * (w * WCOL + (g & 1) * 16 + (g >> 1) * 8);
+  const int prow = 2 * w + ((lane >> 3) & 1);      // q_pe: lanes 0..15 copy rows 2w, 2w + 1
+  const uint32_t pc_off = lane < 16 ? (uint32_t)(prow * rc_row) + 2 * N + 16 * (lane & 7) : OUT_OF_RANGE;
+  const int pe_lds = RS_ATILE + prow * 128 + 16 * (lane & 7);
+  for (int u = 0; u < ntile; ++u) {
+    __syncthreads();   // slot u % D holds tile u
+    const char* sl = ring + (u % D) * RS_SLOT;
     f32x4_t acc[NTW];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int f = u * KS + s;
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ring[uu * KS + s]);
-      if (f + AH < total) ring[uu * KS + s] = load_a(f + AH);
+      const bf16x8_t a = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(sl + c16 * 256 + (((4 * s + g) ^ c16) << 4)));
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag[nt][s], a, acc[nt], 0, 0, 0);
     }
-    // acc[nt] lane (c16 = token, g) holds C[t0 + c16][w * WCOL + 16nt + 4g + j]
-    {
-      char* crow = lds + c16 * CROW + (w * WCOL) * 2;
+    const uint4 pe = *reinterpret_cast<const uint4*>(sl + pe_lds);
+    // acc[nt] lane (c16 = token, g) holds C[c16][w * WCOL + 16nt + 4g + j]:
+    // pk[nt] = those 4 columns as bf16. permlane16_swap(x, y) exchanges the
+    // odd 16-lane rows of x with the even rows of y; on (pk[0], pk[1]) it
+    // leaves lane g with columns {0, 16, 8, 24}[g] .. + 7 in (pk[0], pk[1]).
+    uint32_t pk[NTW][2];
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt)
-        *reinterpret_cast<uint2*>(crow + (16 * nt + 4 * g) * 2) =
-            make_uint2(pack_bf16x2(acc[nt][0], acc[nt][1]), pack_bf16x2(acc[nt][2], acc[nt][3]));
+    for (int nt = 0; nt < NTW; ++nt) {
+      pk[nt][0] = pack_bf16x2(acc[nt][0], acc[nt][1]);
+      pk[nt][1] = pack_bf16x2(acc[nt][2], acc[nt][3]);
     }
-    if constexpr (PE) {   // q_pe (t, h, 0:64) -> columns N .. N + 63
-      if (tid < RS_TM * 8)
-        *reinterpret_cast<uint4*>(lds + (tid >> 3) * CROW + N * 2 + (tid & 7) * 16) = pe_ring[uu];
-      pe_ring[uu] = load_pe(u + AHT);
-    }
-    __syncthreads();
-    constexpr int CCH = OUTC / 8;                  // 16-byte chunks per output row
-    for (int i = tid; i < RS_TM * CCH; i += NTH) {
-      const int r = i / CCH, c = i % CCH;
-      const int tt = t0 + r;
-      if (tt < p.T)
-        *reinterpret_cast<uint4*>(p.c + ((size_t)tt * p.H + h) * p.ldc + 8 * c) =
-            *reinterpret_cast<const uint4*>(lds + r * CROW + c * 16);
-    }
-    __syncthreads();   // the tile buffer is rewritten by the next tile
+#pragma unroll
+    for (int pr = 0; pr < NTW; pr += 2)
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(pk[pr][d], pk[pr + 1][d], false, false);
+        pk[pr][d] = sw[0];
+        pk[pr + 1][d] = sw[1];
+      }
+    const int left = min(RS_TM, rows - u * RS_TM);   // valid rows of tile u
+    const rsrc_t rc = byte_range(c0 + (long long)u * RS_TM * rc_row, (long long)(left - 1) * rc_row + 2 * (N + 64));
+    buf_store16(rc, c_off, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
+    buf_store16(rc, c_off + 64, make_uint4(pk[2][0], pk[2][1], pk[3][0], pk[3][1]));
+    buf_store16(rc, pc_off, pe);
   }
 }
 
@@ -420,12 +470,15 @@ mla_status_t launch_bgemm(const GemmParams& gp, void* stream) {
   // many tokens: weight-stationary. Narrow column slices keep the LDS per
   // workgroup small enough for two or more workgroups per CU (measured faster
   // than wider slices, which read A fewer times).
-  // absorb_q, d_nope = 128, at least 256 tokens: whole rows, B in registers
+  // absorb_q, d_nope = 128, at least 256 tokens: whole rows, B in registers.
+  // About RSQ_WGS workgroups in all (one per CU at 256), each over a
+  // contiguous range of at most 4096 tokens of one head.
   const int tiles16 = (gp.T + RS_TM - 1) / RS_TM;
   if (tiles16 >= 16 && gp.K == 128 && gp.N == 512 && gp.pe != nullptr) {   // absorb_q
-    const unsigned n = (unsigned)(((tiles16 + RSQ_TPW - 1) / RSQ_TPW) * gp.H);
-    hipLaunchKernelGGL((mla_bgemm_rs_kernel<128, RSQ_NW, 512 / 16 / RSQ_NW, RSQ_AHT, RSQ_TPW, true>), dim3(n),
-                       dim3(64 * RSQ_NW), 0, st0, gp);
+    const int groups = std::max(1, RSQ_WGS / gp.H);
+    const int tpw = std::min(256, (tiles16 + groups - 1) / groups);
+    const unsigned n = (unsigned)(((tiles16 + tpw - 1) / tpw) * gp.H);
+    hipLaunchKernelGGL((mla_absorb_q_rs_kernel<RSQ_DEPTH>), dim3(n), dim3(RS_THREADS), 0, st0, gp, tpw);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
   }
   // one-dimensional XCD-aware grid: 8 x slices x ceil(pairs / 8) workgroups
