@@ -44,6 +44,9 @@ constexpr int G_TN_MAX = 512;                   // output columns per tile (at m
 #ifndef RSQ_DEPTH
 #define RSQ_DEPTH 8
 #endif
+#ifndef RSO_DEPTH
+#define RSO_DEPTH 5
+#endif
 
 struct GemmParams {
   const uint16_t* a;       // A(t, h, k) = a[(t * H + h) * lda + k]
@@ -275,10 +278,6 @@ __global__ __launch_bounds__(G_THREADS) void mla_bgemm_ws_kernel(GemmParams p) {
   }
 }
 
-// Register-stationary variant that writes whole rows: each of the NW waves
-// keeps its 16 * NTW-column slice of the head's B (all K rows) in VGPRs as
-// MFMA operands (NTW x K/32 fragments), so
-// the main loop reads only A and has no LDS traffic for B. A workgroup runs
 // Byte range [base, base + bytes) as a buffer resource (gfx9 descriptor,
 // 32-bit data format, no stride, no swizzle). A buffer load whose offset lies
 // outside the range returns zeros and such a store is dropped, so every lane
@@ -320,9 +319,25 @@ __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v) {
 // Vector memory operations of a wave retire in issue order; with loads and
 // stores in one wave, every load would also wait for the write
 // acknowledgements of the stores before it, and under a write-heavy stream
-// those arrive late. One barrier per tile hands a slot from the loader to the
-// compute waves and back. Rows past the last token: the copies read the last
-// valid row again and the buffer stores drop them.
+// those arrive late. Slots change hands through two LDS counters instead of a
+// barrier per tile (which would start every wave's stores at the same moment):
+// the loader publishes how many tiles have landed, and each compute wave
+// counts its completions of a slot, which the loader awaits before refilling
+// it. Compute waves may thus drift up to D - 1 tiles apart. Every wait on a
+// counter gives up after a fixed number of polls, so a broken handshake ends
+// the kernel with wrong output instead of a hang. Rows past the last token:
+// the copies read the last valid row again and the buffer stores drop them.
+// Poll an LDS counter until it reaches `target`, at most 2^22 times (tens of
+// milliseconds): the caller then goes on regardless. The compiler keeps the
+// LDS accesses after the call below the poll.
+__device__ __forceinline__ void lds_await(int* c, int target) {
+  for (int i = 0; i < (1 << 22); ++i) {
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
 constexpr int RS_TM = 16;             // tokens per tile
 constexpr int RS_NW = 8;              // compute waves
 constexpr int RS_THREADS = (RS_NW + 1) * 64;
@@ -340,6 +355,8 @@ __global__ __launch_bounds__(RS_THREADS) void mla_absorb_q_rs_kernel(GemmParams 
   static_assert(NTW == 4 && RS_TM == 2 * NW, "the output swaps assume 64 columns and 2 q_pe rows per wave");
   static_assert(D >= 2 && RS_NDMA * (D - 1) < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char lds[STG + D * RS_SLOT];
+  // cnt[0]: tiles landed in the ring; cnt[1 + s]: compute-wave completions of slot s
+  __shared__ int cnt[1 + D];
   char* const ring = lds + STG;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -354,6 +371,8 @@ __global__ __launch_bounds__(RS_THREADS) void mla_absorb_q_rs_kernel(GemmParams 
   const long long rp_row = (long long)p.H * 64 * 2;
   const char* a0 = reinterpret_cast<const char*>(p.a + ((size_t)row0 * p.H + h) * p.lda);
   const char* p0 = reinterpret_cast<const char*>(p.pe + ((size_t)row0 * p.H + h) * 64);
+  if (tid <= D) cnt[tid] = 0;
+  __syncthreads();   // the only barrier: the counters start at zero
 
   if (w == NW) {
     // ---- loader. Slot layout: q_nope row r (256 B) at r * 256 with its
@@ -380,8 +399,12 @@ __global__ __launch_bounds__(RS_THREADS) void mla_absorb_q_rs_kernel(GemmParams 
     for (int u = 0; u < D - 1; ++u) issue(u);
     for (int u = 0; u < ntile; ++u) {
       wait_vmcnt<RS_NDMA * (D - 2)>();   // tile u has landed (tiles u+1 .. u+D-2 may be in flight)
-      __syncthreads();                  // slot u to the compute waves; slot u-1 is free again
-      issue(u + D - 1);                 // into slot (u - 1) % D
+      __hip_atomic_store(&cnt[0], u + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (u > 0) {   // slot (u - 1) % D is refilled once every compute wave is done with tile u - 1
+        const int need = NW * ((u - 1) / D + 1);
+        lds_await(&cnt[1 + (u - 1) % D], need);
+      }
+      issue(u + D - 1);
     }
     wait_vmcnt<0>();   // no copy may land after the workgroup's LDS is released
     return;
@@ -422,7 +445,7 @@ __global__ __launch_bounds__(RS_THREADS) void mla_absorb_q_rs_kernel(GemmParams 
   const uint32_t pc_off = lane < 16 ? (uint32_t)(prow * rc_row) + 2 * N + 16 * (lane & 7) : OUT_OF_RANGE;
   const int pe_lds = RS_ATILE + prow * 128 + 16 * (lane & 7);
   for (int u = 0; u < ntile; ++u) {
-    __syncthreads();   // slot u % D holds tile u
+    lds_await(&cnt[0], u + 1);   // slot u % D holds tile u
     const char* sl = ring + (u % D) * RS_SLOT;
     f32x4_t acc[NTW];
 #pragma unroll
@@ -435,6 +458,9 @@ __global__ __launch_bounds__(RS_THREADS) void mla_absorb_q_rs_kernel(GemmParams 
       for (int nt = 0; nt < NTW; ++nt) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag[nt][s], a, acc[nt], 0, 0, 0);
     }
     const uint4 pe = *reinterpret_cast<const uint4*>(sl + pe_lds);
+    // LDS operations of a wave execute in order: the count follows the reads
+    asm volatile("" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(&cnt[1 + u % D], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     // acc[nt] lane (c16 = token, g) holds C[c16][w * WCOL + 16nt + 4g + j]:
     // pk[nt] = those 4 columns as bf16. permlane16_swap(x, y) exchanges the
     // odd 16-lane rows of x with the even rows of y; on (pk[0], pk[1]) it
@@ -458,6 +484,134 @@ __global__ __launch_bounds__(RS_THREADS) void mla_absorb_q_rs_kernel(GemmParams 
     buf_store16(rc, c_off, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
     buf_store16(rc, c_off + 64, make_uint4(pk[2][0], pk[2][1], pk[3][0], pk[3][1]));
     buf_store16(rc, pc_off, pe);
+  }
+}
+
+// absorb_out with 512 latent columns and d_v = 128: out[t, h, :] =
+// o[t, h, :] . W_UV[h]. The same two roles as absorb_q, 9 waves:
+// - the loader copies each 16-token tile of o (16 rows of 1 KB, one transfer
+//   per row) HBM -> LDS into a ring of D slots, D - 1 tiles ahead;
+// - 8 compute waves: wave w keeps the 512 x 32 column slice 32 * (w % 4) of
+//   W_UV[h] in VGPRs (two 16-column blocks x 16 k-steps of fragments) and
+//   takes the tiles u with u % 2 == w / 4, so each tile is read from LDS by
+//   4 waves and every SIMD runs two waves. After two v_permlane16_swap per
+//   register a lane holds a 16-byte run, and a wave writes its 64 bytes of
+//   the tile's 16 rows in one store.
+// Slot layout: token row r at r * 1024 with its 16-byte chunk c at position
+// (c & 48) | ((c ^ r) & 15), which keeps the compute waves' 16-byte reads
+// free of bank conflicts. The handshake is the one of absorb_q (LDS counters,
+// bounded polls).
+constexpr int RO_NW = 8;
+constexpr int RO_THREADS = (RO_NW + 1) * 64;
+constexpr int RO_SLOT = RS_TM * 1024;
+template <int D>
+__global__ __launch_bounds__(RO_THREADS) void mla_absorb_out_rs_kernel(GemmParams p, int tpw) {
+  constexpr int K = 512, N = 128, NTW = 2, WCOL = 32, KS = K / G_TK, NCG = N / WCOL;
+  constexpr int SROW = WCOL * 2 + 8;             // staging row of B (bytes)
+  constexpr int STG = RO_NW * G_TK * SROW;
+  constexpr int NDMA = RS_TM;                    // one 1 KB row per transfer
+  static_assert(NCG * 2 == RO_NW && D >= 2 && NDMA * (D - 2) < 64, "shape");
+  __shared__ __attribute__((aligned(16))) char lds[STG + D * RO_SLOT];
+  __shared__ int cnt[1 + D];   // [0]: tiles landed; [1 + s]: compute-wave completions of slot s
+  char* const ring = lds + STG;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int h = blockIdx.x % p.H;
+  const int row0 = (blockIdx.x / p.H) * tpw * RS_TM;
+  if (row0 >= p.T) return;
+  const int rows = min(tpw * RS_TM, p.T - row0);
+  const int ntile = (rows + RS_TM - 1) / RS_TM;
+  const long long ra_row = (long long)p.H * p.lda * 2;
+  const long long rc_row = (long long)p.H * p.ldc * 2;
+  const char* a0 = reinterpret_cast<const char*>(p.a + ((size_t)row0 * p.H + h) * p.lda);
+  if (tid <= D) cnt[tid] = 0;
+  __syncthreads();   // the only barrier: the counters start at zero
+
+  if (w == RO_NW) {   // ---- loader
+    const uint32_t ring_lds = lds_addr(ring);
+    const int chunk = (lane & 48);
+    auto issue = [&](int u) {
+      const uint32_t sl = ring_lds + (u % D) * RO_SLOT;
+#pragma unroll
+      for (int r = 0; r < NDMA; ++r) {
+        const int c = chunk | ((lane ^ r) & 15);
+        const int t = min(u * RS_TM + r, rows - 1);
+        lds_dma16_nt(a0, (uint32_t)(t * ra_row) + 16 * c, sl + 1024 * r);
+      }
+    };
+    for (int u = 0; u < D - 1; ++u) issue(u);
+    for (int u = 0; u < ntile; ++u) {
+      wait_vmcnt<NDMA * (D - 2)>();   // tile u has landed
+      __hip_atomic_store(&cnt[0], u + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (u > 0) lds_await(&cnt[1 + (u - 1) % D], 4 * ((u - 1) / D + 1));   // 4 waves read each tile
+      issue(u + D - 1);
+    }
+    wait_vmcnt<0>();   // no copy may land after the workgroup's LDS is released
+    return;
+  }
+
+  // ---- compute waves: column group cg, tiles of parity tp
+  const int cg = w % NCG, tp = w / NCG;
+  const int jj = (lane >> 2) & 3, qq = lane & 3;
+  bf16x8_t frag[NTW][KS];
+  {
+    char* st = lds + w * G_TK * SROW;
+    const uint16_t* bw = p.b + (size_t)h * K * N + cg * WCOL;
+    constexpr int CPR = WCOL / 8;                  // 16-byte chunks per staged row
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int i = lane; i < G_TK * CPR; i += 64) {
+        const int r = i / CPR, c = i % CPR;
+        *reinterpret_cast<uint4*>(st + r * SROW + c * 16) =
+            *reinterpret_cast<const uint4*>(bw + (size_t)(s * G_TK + r) * N + 8 * c);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const char* src = st + (8 * g + jj) * SROW + (16 * nt + 4 * qq) * 2;
+        const s16x4_t b0 = gemm_read_tr(src);
+        const s16x4_t b1 = gemm_read_tr(src + 4 * SROW);
+        frag[nt][s] = __builtin_bit_cast(
+            bf16x8_t, make_uint4(__builtin_bit_cast(uint2, b0).x, __builtin_bit_cast(uint2, b0).y,
+                                 __builtin_bit_cast(uint2, b1).x, __builtin_bit_cast(uint2, b1).y));
+      }
+    }
+  }
+  const char* c0 = reinterpret_cast<const char*>(p.c + ((size_t)row0 * p.H + h) * p.ldc);
+  const uint32_t c_off = (uint32_t)(c16 * rc_row) + 2 * (cg * WCOL + (g & 1) * 16 + (g >> 1) * 8);
+  for (int u = tp; u < ntile; u += 2) {
+    lds_await(&cnt[0], u + 1);   // slot u % D holds tile u
+    const char* sl = ring + (u % D) * RO_SLOT + c16 * 1024;
+    f32x4_t acc[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int c = 4 * s + g;
+      const bf16x8_t a = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(sl + (((c & 48) | ((c ^ c16) & 15)) << 4)));
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag[nt][s], a, acc[nt], 0, 0, 0);
+    }
+    // LDS operations of a wave execute in order: the count follows the reads
+    asm volatile("" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(&cnt[1 + u % D], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    uint32_t pk[NTW][2];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      pk[nt][0] = pack_bf16x2(acc[nt][0], acc[nt][1]);
+      pk[nt][1] = pack_bf16x2(acc[nt][2], acc[nt][3]);
+    }
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {   // lane g: columns {0, 16, 8, 24}[g] .. + 7 of the wave's 32
+      const auto sw = __builtin_amdgcn_permlane16_swap(pk[0][d], pk[1][d], false, false);
+      pk[0][d] = sw[0];
+      pk[1][d] = sw[1];
+    }
+    const int left = min(RS_TM, rows - u * RS_TM);
+    const rsrc_t rc = byte_range(c0 + (long long)u * RS_TM * rc_row, (long long)(left - 1) * rc_row + 2 * N);
+    buf_store16(rc, c_off, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
   }
 }
 
@@ -491,7 +645,14 @@ mla_status_t launch_bgemm(const GemmParams& gp, void* stream) {
                        dim3(G_THREADS), 0, st0, gp);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
   }
-  if (gp.K == 512 && gp.N % ABSO_TN == 0 && tiles >= 64) {   // absorb_out
+  if (tiles16 >= 16 && gp.K == 512 && gp.N == 128 && gp.pe == nullptr) {   // absorb_out, d_v = 128
+    const int groups = std::max(1, RSQ_WGS / gp.H);
+    const int tpw = std::min(256, (tiles16 + groups - 1) / groups);
+    const unsigned n = (unsigned)(((tiles16 + tpw - 1) / tpw) * gp.H);
+    hipLaunchKernelGGL((mla_absorb_out_rs_kernel<RSO_DEPTH>), dim3(n), dim3(RO_THREADS), 0, st0, gp, tpw);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
+  if (gp.K == 512 && gp.N % ABSO_TN == 0 && tiles >= 64) {   // absorb_out, other d_v
     hipLaunchKernelGGL((mla_bgemm_ws_kernel<ABSO_TN, 512, ABSO_AHEAD, ABSO_TPW>), ws_grid(ABSO_TN, ABSO_TPW),
                        dim3(G_THREADS), 0, st0, gp);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;

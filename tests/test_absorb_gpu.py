@@ -27,10 +27,13 @@ def dev(bits):
     return torch.from_numpy(bits.view(np.int16)).to("cuda:0").view(torch.bfloat16)
 
 
-# 2100 tokens: absorb_q takes the weight-stationary path (33 token tiles: 16 + 16 + 1,
-# the last one ragged); 4200 tokens do the same for absorb_out (66 tiles: 32 + 32 + 2)
+# From 241 tokens on, d = 128 takes the ring kernels: 256 / H workgroups per
+# head, each over a run of 16-token tiles. 600 tokens at H = 128 give each
+# workgroup 19 tiles (the last one ragged), so the LDS rings (8 and 5 slots)
+# wrap twice or more; 2100 tokens at H = 2 give 2 tiles per workgroup. Other
+# shapes take the streaming or weight-stationary kernels.
 @pytest.mark.parametrize("T,H,d", [(128, 16, 128), (64, 128, 128), (37, 3, 64), (1, 1, 32), (2100, 2, 128),
-                                   (256, 1, 128), (1000, 5, 128)])
+                                   (256, 1, 128), (1000, 5, 128), (600, 128, 128)])
 def test_absorb_q(mla, T, H, d):
     rng = np.random.default_rng(T * 1000 + H)
     qn, pe, w = bf16(rng, (T, H, d)), bf16(rng, (T, H, 64)), bf16(rng, (H, d, 512), d ** -0.5)
@@ -43,7 +46,8 @@ def test_absorb_q(mla, T, H, d):
 
 
 @pytest.mark.parametrize("T,H,dv", [(128, 16, 128), (64, 128, 128), (37, 3, 64), (5, 2, 192),
-                                    (4200, 2, 128), (4200, 3, 64), (256, 1, 128), (1000, 5, 128)])
+                                    (4200, 2, 128), (4200, 3, 64), (256, 1, 128), (1000, 5, 128),
+                                    (600, 128, 128)])
 def test_absorb_out(mla, T, H, dv):
     rng = np.random.default_rng(T * 1000 + H + 7)
     o, w = bf16(rng, (T, H, 512)), bf16(rng, (H, 512, dv), 512 ** -0.5)
