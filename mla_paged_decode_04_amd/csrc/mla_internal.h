@@ -146,6 +146,16 @@ __device__ __forceinline__ void lds_dma16_nt(const char* gbase, uint32_t voff, u
                : "memory");
 }
 
+// 16 bytes at p (always a valid address) if keep, else zeros: the load is
+// issued unconditionally and masked. A branch around a load leaves the
+// compiler without an exact count of the memory operations in flight, and
+// its next wait then drains all of them, the DMAs it cannot see included.
+__device__ __forceinline__ uint4 load16_masked(const void* p, bool keep) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t m = keep ? 0xFFFFFFFFu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));

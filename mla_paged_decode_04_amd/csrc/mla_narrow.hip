@@ -457,9 +457,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
     const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
-                       : make_uint4(0, 0, 0, 0);
-      qb[s] = __builtin_bit_cast(bf16x8_t, v);
+      qb[s] = __builtin_bit_cast(bf16x8_t, load16_masked(qrow + 32 * s + 8 * g, row_ok));
     }
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) asm volatile("" ::"v"(qb[s]));
@@ -481,8 +479,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_narrow(FwdParams p) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int blk = s < 4 ? 4 * s + g : 16 + (g & 1);
-        v[s][c] = row_ok ? *reinterpret_cast<const uint4*>(qs + blk * 1024 + c16 * 64 + c * 16)
-                         : make_uint4(0, 0, 0, 0);
+        v[s][c] = load16_masked(qs + blk * 1024 + c16 * 64 + c * 16, row_ok);
         const uint32_t w4[4] = {v[s][c].x, v[s][c].y, v[s][c].z, v[s][c].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)

@@ -103,9 +103,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mla_decode_wide(FwdParams p) {
     const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g)
-                       : make_uint4(0, 0, 0, 0);
-      qb[s] = __builtin_bit_cast(bf16x8_t, v);
+      qb[s] = __builtin_bit_cast(bf16x8_t, load16_masked(qrow + 32 * s + 8 * g, row_ok));
     }
   }
   // q loads complete here, before the first (compiler-invisible) DMA

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(Y_THREADS, 1) void mla_decode_wide128(FwdParams p) 
   if constexpr (!F8) {
 #pragma unroll
     for (int s = 0; s < 18; ++s) {
-      const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
+      const uint4 v = load16_masked(qrow + 32 * s + 8 * g, row_ok);
       if (s < 16)
         qb[s < 16 ? s : 0] = __builtin_bit_cast(bf16x8_t, v);
       else
@@ -236,12 +236,18 @@ __global__ __launch_bounds__(Y_THREADS, 1) void mla_decode_wide128(FwdParams p) 
   } else {
     uint4 v[5][4];
     float qmax = 0.f;
+    // all 20 loads first: one memory round trip (interleaved with the max
+    // below, the scheduler spreads them over several)
+#pragma unroll
+    for (int s = 0; s < 5; ++s)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        v[s][c] = load16_masked(qrow + (s < 4 ? 128 * s + 32 * g + 8 * c : 512 + 32 * (g & 1) + 8 * c), row_ok);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 5; ++s)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int d = s < 4 ? 128 * s + 32 * g + 8 * c : 512 + 32 * (g & 1) + 8 * c;
-        v[s][c] = row_ok ? *reinterpret_cast<const uint4*>(qrow + d) : make_uint4(0, 0, 0, 0);
         const uint32_t w4[4] = {v[s][c].x, v[s][c].y, v[s][c].z, v[s][c].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
