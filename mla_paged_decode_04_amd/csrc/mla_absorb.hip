@@ -441,10 +441,8 @@ __global__ __launch_bounds__(RS_THREADS) void mla_absorb_q_rs_kernel(GemmParams 
   }
 
   const char* c0 = reinterpret_cast<const char*>(p.c + ((size_t)row0 * p.H + h) * p.ldc);
-  // Stores (see the tile loop): lane (c16, g) writes the 16-byte run at
-  // columns w * 64 + {0, 16, 8, 24}[g] (+ 32 for c16 >= 8) of rows c16 & 7
-  // and (c16 & 7) + 8.
-  const uint32_t c_col = 2 * (w * WCOL + (g & 1) * 16 + (g >> 1) * 8) + (c16 < 8 ? 0 : 64);
+  // lane (c16, g) stores into rows c16 & 7 and (c16 & 7) + 8 of each tile
+  const uint32_t c_col = 2 * w * WCOL + whole_row_col(c16, g);
   const uint32_t c_off_lo = (uint32_t)((c16 & 7) * rc_row) + c_col;
   const uint32_t c_off_hi = (uint32_t)(((c16 & 7) + 8) * rc_row) + c_col;
   const int prow = 2 * w + ((lane >> 3) & 1);      // q_pe: lanes 0..15 copy rows 2w, 2w + 1
@@ -467,47 +465,23 @@ __global__ __launch_bounds__(RS_THREADS) void mla_absorb_q_rs_kernel(GemmParams 
     // LDS operations of a wave execute in order: the count follows the reads
     asm volatile("" ::: "memory");
     if (lane == 0) __hip_atomic_fetch_add(&cnt[1 + u % D], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    // acc[nt] lane (c16 = token, g) holds C[c16][w * WCOL + 16nt + 4g + j]:
-    // pk[nt] = those 4 columns as bf16. permlane16_swap(x, y) exchanges the
-    // odd 16-lane rows of x with the even rows of y; on (pk[0], pk[1]) it
-    // leaves lane g with columns {0, 16, 8, 24}[g] .. + 7 in (pk[0], pk[1]).
+    // acc[nt] lane (c16 = token, g) holds C[c16][w * WCOL + 16nt + 4g + j];
+    // each of the two stores covers 8 whole rows of the wave's 128-byte
+    // slice (whole_row_runs). Non-temporal: the 604 MB of q at 4096 tokens x
+    // 128 heads would otherwise sit dirty in the caches and be written back
+    // during the next kernel (absorb_q then absorb_out: 303 -> 290 us).
     uint32_t pk[NTW][2];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       pk[nt][0] = pack_bf16x2(acc[nt][0], acc[nt][1]);
       pk[nt][1] = pack_bf16x2(acc[nt][2], acc[nt][3]);
     }
-#pragma unroll
-    for (int pr = 0; pr < NTW; pr += 2)
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const auto sw = __builtin_amdgcn_permlane16_swap(pk[pr][d], pk[pr + 1][d], false, false);
-        pk[pr][d] = sw[0];
-        pk[pr + 1][d] = sw[1];
-      }
+    uint4 rows_lo, rows_hi;
+    whole_row_runs(pk, c16, rows_lo, rows_hi);
     const int left = min(RS_TM, rows - u * RS_TM);   // valid rows of tile u
     const rsrc_t rc = byte_range(c0 + (long long)u * RS_TM * rc_row, (long long)(left - 1) * rc_row + 2 * (N + 64));
-    // Lane (c16, g) now holds runs A (columns cA = {0, 16, 8, 24}[g]) and B
-    // (cA + 32) of row c16. A row-rotate by 8 inside each 16-lane row swaps
-    // B of rows 0..7 with A of rows 8..15, so each store covers 8 whole rows
-    // of the wave's slice: 8 cache lines per instruction instead of 16 half
-    // lines (absorb_q 177 -> 157 us). Non-temporal: the 604 MB of q at 4096
-    // tokens x 128 heads would otherwise sit dirty in the caches and be
-    // written back during the next kernel (absorb_q then absorb_out: 303 ->
-    // 290 us).
-    {
-      const uint4 ra = make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]);
-      const uint4 rb = make_uint4(pk[2][0], pk[2][1], pk[3][0], pk[3][1]);
-      const bool lo = c16 < 8;
-      const uint4 x = lo ? rb : ra;
-      constexpr int ROW_ROR8 = 0x128;   // DPP row_ror:8 (lane l of a 16-lane row reads lane l ^ 8)
-      const uint4 y = make_uint4((uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.x, ROW_ROR8, 0xF, 0xF, false),
-                                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.y, ROW_ROR8, 0xF, 0xF, false),
-                                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.z, ROW_ROR8, 0xF, 0xF, false),
-                                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.w, ROW_ROR8, 0xF, 0xF, false));
-      buf_store16<ST_NT>(rc, c_off_lo, lo ? ra : y);   // rows 0..7
-      buf_store16<ST_NT>(rc, c_off_hi, lo ? y : rb);   // rows 8..15
-    }
+    buf_store16<ST_NT>(rc, c_off_lo, rows_lo);
+    buf_store16<ST_NT>(rc, c_off_hi, rows_hi);
     buf_store16<ST_NT>(rc, pc_off, pe);
   }
 }

@@ -156,6 +156,42 @@ __device__ __forceinline__ uint4 load16_masked(const void* p, bool keep) {
   return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
+// Store layout for four MFMA result fragments of a 16-row tile, packed to
+// 16-bit values: pk[i][0..1] of lane (c16, g) hold columns 16 i + 4 g .. + 3
+// of row c16. Rearranged across lanes so that two 16-byte stores per lane
+// write 8 whole rows of the tile's 64 columns each (128 bytes, one cache
+// line per row): `lo` for rows 0..7, `hi` for rows 8..15, lane (c16, g)
+// writing row (c16 & 7) (+ 8) at byte whole_row_col(c16, g) of the row's
+// slice. Two v_permlane16_swap per fragment pair turn the 4-column pieces
+// of lanes g and g + 1 into 8-column runs (columns {0, 16, 8, 24}[g] and
+// + 32 of the 64); a DPP row rotate by 8 then swaps the second run of rows
+// 0..7 with the first run of rows 8..15. Every lane of the wave must take
+// part. (Half- or quarter-line stores keep fewer writes in flight.)
+__device__ __forceinline__ void whole_row_runs(uint32_t (&pk)[4][2], int c16, uint4& lo, uint4& hi) {
+#pragma unroll
+  for (int pr = 0; pr < 4; pr += 2)
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(pk[pr][d], pk[pr + 1][d], false, false);
+      pk[pr][d] = sw[0];
+      pk[pr + 1][d] = sw[1];
+    }
+  const uint4 ra = make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]);
+  const uint4 rb = make_uint4(pk[2][0], pk[2][1], pk[3][0], pk[3][1]);
+  const bool low = c16 < 8;
+  const uint4 x = low ? rb : ra;
+  constexpr int ROW_ROR8 = 0x128;   // DPP row_ror:8: lane l of a 16-lane row reads lane l ^ 8
+  const uint4 y = make_uint4(static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x.x), ROW_ROR8, 0xF, 0xF, false)),
+                             static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x.y), ROW_ROR8, 0xF, 0xF, false)),
+                             static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x.z), ROW_ROR8, 0xF, 0xF, false)),
+                             static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x.w), ROW_ROR8, 0xF, 0xF, false)));
+  lo = low ? ra : y;
+  hi = low ? y : rb;
+}
+__device__ __forceinline__ int whole_row_col(int c16, int g) {
+  return 2 * ((g & 1) * 16 + (g >> 1) * 8) + (c16 < 8 ? 0 : 64);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));

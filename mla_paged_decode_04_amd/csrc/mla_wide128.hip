@@ -576,29 +576,50 @@ __global__ __launch_bounds__(Y_THREADS, 1) void mla_decode_wide128(FwdParams p) 
       for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(o[dt][e]));
     kexp = min(partial_exponent(wave_max_across_groups(amax) * inv), 127 - __builtin_amdgcn_frexp_expf(inv));
   }
-  if (row_ok) {
+  // The wave's 16 rows leave in 8 groups of 64 dims; each store covers 8
+  // whole rows of a group (whole_row_runs), so every lane takes part in the
+  // exchange and a store goes out only for a row of the sequence.
+  const float fs = __builtin_ldexpf(inv, kexp);
+  const int r_lo = 16 * w + (c16 & 7), r_hi = r_lo + 8;   // item rows of the two stores
+  const bool ok_lo = rg * Y_RGS + r_lo < p.rows, ok_hi = rg * Y_RGS + r_hi < p.rows;
+  char* dst_lo;
+  char* dst_hi;
+  if (slot < 0) {
+    const size_t orow0 = (size_t)b * p.rows + rg * Y_RGS;
+    dst_lo = reinterpret_cast<char*>(p.out + (orow0 + r_lo) * DV);
+    dst_hi = reinterpret_cast<char*>(p.out + (orow0 + r_hi) * DV);
+  } else {
+    dst_lo = reinterpret_cast<char*>(p.part_o + ((size_t)slot * Y_RGS + r_lo) * DV);
+    dst_hi = reinterpret_cast<char*>(p.part_o + ((size_t)slot * Y_RGS + r_hi) * DV);
+  }
+  const int col = whole_row_col(c16, g);
+#pragma unroll
+  for (int k = 0; k < DV / 64; ++k) {
+    uint32_t pk[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4_t v = o[4 * k + i] * fs;
+      if (slot < 0) {
+        pk[i][0] = pack_bf16x2(v[0], v[1]);
+        pk[i][1] = pack_bf16x2(v[2], v[3]);
+      } else {
+        const uint2 h = __builtin_bit_cast(uint2, __builtin_convertvector(v, f16x4_t));
+        pk[i][0] = h.x;
+        pk[i][1] = h.y;
+      }
+    }
+    uint4 lo, hi;
+    whole_row_runs(pk, c16, lo, hi);
+    if (ok_lo) *reinterpret_cast<uint4*>(dst_lo + 128 * k + col) = lo;
+    if (ok_hi) *reinterpret_cast<uint4*>(dst_hi + 128 * k + col) = hi;
+  }
+  if (row_ok && g == 0) {
     const float lse2 = empty ? -INFINITY : m_run + log2f(l_row);
-    const size_t orow = (size_t)b * p.rows + row;
-    const float fs = __builtin_ldexpf(inv, kexp);
     if (slot < 0) {
-      uint16_t* dst = p.out + orow * DV + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) {
-        const f32x4_t v = o[dt] * fs;
-        *reinterpret_cast<uint2*>(dst + 16 * dt) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      }
-      if (p.lse != nullptr && g == 0) p.lse[orow] = lse2 * LN2;
+      if (p.lse != nullptr) p.lse[(size_t)b * p.rows + row] = lse2 * LN2;
     } else {
-      _Float16* dst = p.part_o + ((size_t)slot * Y_RGS + row_local) * DV + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) {
-        const f32x4_t v = o[dt] * fs;
-        *reinterpret_cast<f16x4_t*>(dst + 16 * dt) = __builtin_convertvector(v, f16x4_t);
-      }
-      if (g == 0) {
-        p.part_lse[(size_t)slot * Y_RGS + row_local] = lse2;
-        p.part_scale[(size_t)slot * Y_RGS + row_local] = kexp;
-      }
+      p.part_lse[(size_t)slot * Y_RGS + row_local] = lse2;
+      p.part_scale[(size_t)slot * Y_RGS + row_local] = kexp;
     }
   }
 }
