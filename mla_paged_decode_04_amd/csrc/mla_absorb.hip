@@ -15,19 +15,9 @@ namespace {
 constexpr int G_THREADS = 256;                  // 4 waves
 constexpr int G_TM = 64;                        // tokens per tile (16 per wave)
 constexpr int G_TK = 32;                        // k per step
-constexpr int G_TN_MAX = 512;                   // output columns per tile (at most)
 
-// Weight-stationary shapes (column slice, A read-ahead in k-steps, token
-// tiles per workgroup) of the two projections; tuning knobs.
-#ifndef ABSQ_TN
-#define ABSQ_TN 128
-#endif
-#ifndef ABSQ_AHEAD
-#define ABSQ_AHEAD 4
-#endif
-#ifndef ABSQ_TPW
-#define ABSQ_TPW 16
-#endif
+// Weight-stationary shape of absorb_out with d_v other than 128 (column
+// slice, A read-ahead in k-steps, token tiles per workgroup); tuning knobs.
 #ifndef ABSO_TN
 #define ABSO_TN 64
 #endif
@@ -38,6 +28,8 @@ constexpr int G_TN_MAX = 512;                   // output columns per tile (at m
 #define ABSO_TPW 32
 #endif
 
+// Ring kernels: workgroups per launch (about), LDS ring slots of absorb_q
+// and absorb_out.
 #ifndef RSQ_WGS
 #define RSQ_WGS 256
 #endif
@@ -618,49 +610,39 @@ bool al(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % 
 
 mla_status_t launch_bgemm(const GemmParams& gp, void* stream) {
   if (gp.T == 0) return MLA_OK;
-  hipStream_t st0 = static_cast<hipStream_t>(stream);
-  const int tiles = (gp.T + G_TM - 1) / G_TM;
-  // many tokens: weight-stationary. Narrow column slices keep the LDS per
-  // workgroup small enough for two or more workgroups per CU (measured faster
-  // than wider slices, which read A fewer times).
-  // absorb_q, d_nope = 128, at least 256 tokens: whole rows, B in registers.
-  // About RSQ_WGS workgroups in all (one per CU at 256), each over a
-  // contiguous range of at most 4096 tokens of one head.
-  const int tiles16 = (gp.T + RS_TM - 1) / RS_TM;
-  if (tiles16 >= 16 && gp.K == 128 && gp.N == 512 && gp.pe != nullptr) {   // absorb_q
-    const int groups = std::max(1, RSQ_WGS / gp.H);
-    const int tpw = std::min(256, (tiles16 + groups - 1) / groups);
-    const unsigned n = (unsigned)(((tiles16 + tpw - 1) / tpw) * gp.H);
-    hipLaunchKernelGGL((mla_absorb_q_rs_kernel<RSQ_DEPTH>), dim3(n), dim3(RS_THREADS), 0, st0, gp, tpw);
-    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
-  }
-  // one-dimensional XCD-aware grid: 8 x slices x ceil(pairs / 8) workgroups
-  auto ws_grid = [&](int tn, int tpw) {
-    const long long pairs = (long long)((tiles + tpw - 1) / tpw) * gp.H;
-    return dim3(static_cast<unsigned>(8LL * (gp.N / tn) * ((pairs + 7) / 8)));
-  };
-  if (gp.N == 512 && gp.K == 128 && tiles >= 32) {   // absorb_q, d_nope = 128
-    hipLaunchKernelGGL((mla_bgemm_ws_kernel<ABSQ_TN, 128, ABSQ_AHEAD, ABSQ_TPW>), ws_grid(ABSQ_TN, ABSQ_TPW),
-                       dim3(G_THREADS), 0, st0, gp);
-    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
-  }
-  if (tiles16 >= 16 && gp.K == 512 && gp.N == 128 && gp.pe == nullptr) {   // absorb_out, d_v = 128
-    const int groups = std::max(1, RSQ_WGS / gp.H);
-    const int tpw = std::min(256, (tiles16 + groups - 1) / groups);
-    const unsigned n = (unsigned)(((tiles16 + tpw - 1) / tpw) * gp.H);
-    hipLaunchKernelGGL((mla_absorb_out_rs_kernel<RSO_DEPTH>), dim3(n), dim3(RO_THREADS), 0, st0, gp, tpw);
-    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
-  }
-  if (gp.K == 512 && gp.N % ABSO_TN == 0 && tiles >= 64) {   // absorb_out, other d_v
-    hipLaunchKernelGGL((mla_bgemm_ws_kernel<ABSO_TN, 512, ABSO_AHEAD, ABSO_TPW>), ws_grid(ABSO_TN, ABSO_TPW),
-                       dim3(G_THREADS), 0, st0, gp);
-    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
-  }
-  // absorb_q (N = 512, K = d_nope): whole 512-column rows per tile; otherwise
-  // 64-column tiles, which keep more workgroups in flight over the long K
-  const int tn = gp.N == 512 && tiles * gp.H >= 512 ? 512 : 64;
-  const dim3 grid(gp.N / tn, (gp.T + G_TM - 1) / G_TM, gp.H);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const int tiles = (gp.T + G_TM - 1) / G_TM;     // 64-token tiles
+  const int tiles16 = (gp.T + RS_TM - 1) / RS_TM;  // 16-token tiles
+  // Ring kernels (at least 16 tiles of 16 tokens; absorb_q with d_nope = 128,
+  // absorb_out with d_v = 128): about RSQ_WGS workgroups in all (one per CU
+  // at 256), each over a contiguous range of at most 4096 tokens of one head.
+  const bool q_ring = gp.K == 128 && gp.N == 512 && gp.pe != nullptr;
+  const bool out_ring = gp.K == 512 && gp.N == 128 && gp.pe == nullptr;
+  if (tiles16 >= 16 && (q_ring || out_ring)) {
+    const int groups = std::max(1, RSQ_WGS / gp.H);
+    const int tpw = std::min(256, (tiles16 + groups - 1) / groups);
+    const unsigned n = (unsigned)(((tiles16 + tpw - 1) / tpw) * gp.H);
+    if (q_ring)
+      hipLaunchKernelGGL((mla_absorb_q_rs_kernel<RSQ_DEPTH>), dim3(n), dim3(RS_THREADS), 0, st, gp, tpw);
+    else
+      hipLaunchKernelGGL((mla_absorb_out_rs_kernel<RSO_DEPTH>), dim3(n), dim3(RO_THREADS), 0, st, gp, tpw);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
+  // absorb_out with another d_v and many tokens: weight-stationary, on a
+  // one-dimensional XCD-aware grid of 8 x slices x ceil(pairs / 8)
+  // workgroups. Narrow column slices keep the LDS per workgroup small enough
+  // for two or more workgroups per CU.
+  if (gp.K == 512 && gp.N % ABSO_TN == 0 && tiles >= 64) {
+    const long long pairs = (long long)((tiles + ABSO_TPW - 1) / ABSO_TPW) * gp.H;
+    const dim3 grid(static_cast<unsigned>(8LL * (gp.N / ABSO_TN) * ((pairs + 7) / 8)));
+    hipLaunchKernelGGL((mla_bgemm_ws_kernel<ABSO_TN, 512, ABSO_AHEAD, ABSO_TPW>), grid, dim3(G_THREADS), 0, st, gp);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
+  // everything else (few tokens, other shapes): streaming. absorb_q (N = 512)
+  // takes whole 512-column rows per tile when there are enough tiles;
+  // otherwise 64-column tiles keep more workgroups in flight over the long K
+  const int tn = gp.N == 512 && tiles * gp.H >= 512 ? 512 : 64;
+  const dim3 grid(gp.N / tn, tiles, gp.H);
   switch (tn) {
     case 512: hipLaunchKernelGGL(mla_bgemm_kernel<512>, grid, dim3(G_THREADS), 0, st, gp); break;
     default: hipLaunchKernelGGL(mla_bgemm_kernel<64>, grid, dim3(G_THREADS), 0, st, gp); break;
