@@ -271,23 +271,18 @@ __global__ __launch_bounds__(G_THREADS) void mla_bgemm_ws_kernel(GemmParams p) {
 }
 
 // Byte range [base, base + bytes) as a buffer resource (gfx9 descriptor,
-// 32-bit data format, no stride, no swizzle). A buffer load whose offset lies
-// outside the range returns zeros and such a store is dropped, so every lane
-// of a wave can issue the same memory instructions: no branch around a load
-// or a store, and the compiler's count of outstanding memory operations stays
-// exact (a conditional load or a store loop of unknown length makes it wait
-// for all of them, stores included).
+// 32-bit data format, no stride, no swizzle; bytes < 2^31: the ring kernels
+// build one per 16-row tile). A buffer store whose offset lies outside the
+// range is dropped, so every lane of a wave issues the same stores and rows
+// past the last token need no branch (a store under a branch, or in a loop
+// of unknown length, leaves the compiler's count of memory operations in
+// flight inexact, and its next wait then drains all of them).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t byte_range(const void* base, long long bytes) {
   const int n = bytes <= 0 ? 0 : static_cast<int>(bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 constexpr uint32_t OUT_OF_RANGE = 0x80000000u;   // an offset past every range built here
-__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
 // AUX: cache-policy bits of the store; 2 = nt (non-temporal, streaming).
 template <int AUX = 0>
 __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v) {
@@ -295,6 +290,18 @@ __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, off, 0, AUX);
 }
 constexpr int ST_NT = 2;
+
+// Poll an LDS counter until it reaches `target`, at most 2^22 times (with
+// s_sleep 1 between polls, about a tenth of a second): the caller then goes
+// on regardless. The compiler keeps the LDS accesses after the call below
+// the poll.
+__device__ __forceinline__ void lds_await(int* c, int target) {
+  for (int i = 0; i < (1 << 22); ++i) {
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
 
 // absorb_q with d_nope = 128: q[t, h, 0:512] = q_nope[t, h, :] . W_UK[h] and
 // q[t, h, 512:576] = q_pe[t, h, :]. One workgroup per (token range, head),
@@ -322,17 +329,6 @@ constexpr int ST_NT = 2;
 // counter gives up after a fixed number of polls, so a broken handshake ends
 // the kernel with wrong output instead of a hang. Rows past the last token:
 // the copies read the last valid row again and the buffer stores drop them.
-// Poll an LDS counter until it reaches `target`, at most 2^22 times (tens of
-// milliseconds): the caller then goes on regardless. The compiler keeps the
-// LDS accesses after the call below the poll.
-__device__ __forceinline__ void lds_await(int* c, int target) {
-  for (int i = 0; i < (1 << 22); ++i) {
-    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  asm volatile("" ::: "memory");
-}
-
 constexpr int RS_TM = 16;             // tokens per tile
 constexpr int RS_NW = 8;              // compute waves
 constexpr int RS_THREADS = (RS_NW + 1) * 64;
