@@ -83,3 +83,42 @@ def test_absorbed_decode_chain(mla, kv_dtype):
                               inp.kv_scale, wl.kv_dtype, True)
     ref = np.einsum("thn,hnv->thv", o_ref.reshape(B, H, 512), orc.bf16_bits_to_f64(w_uv))
     assert orc.rel_fro(out.float().cpu().double().numpy(), ref) <= 1e-2
+
+
+def test_absorb_beyond_4gib(mla):
+    # 33000 tokens x 128 heads: q (576 wide) is 4.9 GB and o 4.3 GB, so
+    # element offsets pass 2^32 bytes; 9 token ranges per head, the last one
+    # ragged. Sampled rows against the oracle (the full products take the
+    # oracle minutes): the first, middle and last tokens of several ranges,
+    # over several heads.
+    T, H, d = 33000, 128, 128
+    assert T * H * 576 * 2 > 2 ** 32 and T * H * 512 * 2 > 2 ** 32
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(4242)
+    qn = torch.randn((T, H, d), device="cuda:0", generator=g).bfloat16()
+    pe = torch.randn((T, H, 64), device="cuda:0", generator=g).bfloat16()
+    w_uk = (torch.randn((H, d, 512), device="cuda:0", generator=g) * d ** -0.5).bfloat16()
+    o = torch.randn((T, H, 512), device="cuda:0", generator=g).bfloat16()
+    w_uv = (torch.randn((H, 512, d), device="cuda:0", generator=g) * 512 ** -0.5).bfloat16()
+    q = mla.mla_absorb_q(qn, pe, w_uk)
+    y = mla.mla_absorb_out(o, w_uv)
+    torch.cuda.synchronize()
+    toks = torch.tensor([0, 1, 15, 16, 4095, 4096, 16383, 16400, 29999, 32767, 32768, 32990, 32999])
+    heads = torch.tensor([0, 1, 63, 64, 127])
+    tt, hh = torch.meshgrid(toks, heads, indexing="ij")
+    tt, hh = tt.reshape(-1), hh.reshape(-1)
+    bits = lambda x: x.cpu().view(torch.int16).numpy()   # noqa: E731
+    w_uk_b, w_uv_b = bits(w_uk), bits(w_uv)
+    got_q = q[tt, hh].float().cpu().double().numpy()
+    got_y = y[tt, hh].float().cpu().double().numpy()
+    ref_q = np.stack([orc.absorb_q(bits(qn[t:t + 1, h:h + 1]), bits(pe[t:t + 1, h:h + 1]),
+                                   w_uk_b[h:h + 1])[0, 0] for t, h in zip(tt.tolist(), hh.tolist())])
+    ref_y = np.stack([orc.absorb_out(bits(o[t:t + 1, h:h + 1]), w_uv_b[h:h + 1])[0, 0]
+                      for t, h in zip(tt.tolist(), hh.tolist())])
+    assert orc.rel_fro(got_q[:, :512], ref_q[:, :512]) <= 5e-3
+    np.testing.assert_array_equal(got_q[:, 512:], ref_q[:, 512:])
+    assert orc.rel_fro(got_y, ref_y) <= 5e-3
+    # every sampled row individually as well (a misplaced row would be off by ~1)
+    for i in range(len(tt)):
+        assert orc.rel_fro(got_q[i, :512], ref_q[i, :512]) <= 1e-2
+        assert orc.rel_fro(got_y[i], ref_y[i]) <= 1e-2
