@@ -529,3 +529,34 @@ def test_stale_plan_items_are_skipped_and_flagged(mla, case):
     r = run_oracle(inp)
     assert_parity(out[:4].float().cpu().double().numpy(), lse[:4].cpu().double().numpy(), r[0][:4], r[1][:4],
                   dtype, f"after stale plan {tag}", vabs=r.vabs[:4])
+
+
+# ---------------------------------------------------------------------------
+# a latent cache larger than 4 GiB
+# ---------------------------------------------------------------------------
+
+# The sequences' pages are moved above the 4 GiB offset of a cache of about
+# 4.3 GB, so every row address needs 64-bit arithmetic. One case per decode
+# kernel (16, 32 and 128 query rows per sequence), split items included (a
+# few short sequences over 256 items). The oracle reads the same pages from
+# the compact cache through the original block table.
+@pytest.mark.parametrize("heads,s_q,bs,kv_dtype", [(16, 1, 64, "bf16"), (32, 1, 64, "fp8"),
+                                                   (128, 1, 128, "bf16"), (16, 4, 128, "fp8")])
+def test_cache_beyond_4gib(mla, heads, s_q, bs, kv_dtype):
+    import dataclasses
+    wl = dataclasses.replace(mi.WORKLOADS["tiny"], name=f"big_cache_h{heads}_sq{s_q}_{kv_dtype}", batch=3,
+                             s_q=s_q, heads=heads, block_size=bs, kv_dtype=kv_dtype,
+                             lens="fixed", lens_arg=(1000, 77, 640), seed=heads + s_q)
+    inp = mi.make_inputs(wl)
+    print(f"[{wl.name}] cache rows past 4 GiB", flush=True)
+    q, kv, bt, sl = to_device(inp)
+    page_bytes = bs * 576 * (2 if kv_dtype == "bf16" else 1)
+    base = (2 ** 32) // page_bytes + 1                 # first page id past 4 GiB
+    n_small = kv.shape[0]
+    big = torch.empty((base + n_small,) + tuple(kv.shape[1:]), dtype=kv.dtype, device=kv.device)
+    assert big.numel() * big.element_size() > 2 ** 32
+    big[base:] = kv
+    bt_big = torch.where(bt >= 0, bt + base, bt)
+    o, l = run_gpu(mla, inp, dev_inputs=(q, big, bt_big, sl))
+    ro = run_oracle(inp)
+    assert_parity(o, l, ro[0], ro[1], kv_dtype, tag=wl.name, vabs=ro.vabs)
