@@ -114,3 +114,32 @@ def test_append_last_token_then_decode(mla, name):
     tol = 5e-3 if wl.kv_dtype == "bf16" else 1e-2
     assert orc.rel_fro(o, ro) <= tol
     assert np.abs(lse.cpu().double().numpy() - rl).max() <= 1e-3
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_kv_append_beyond_4gib(mla, kv_dtype):
+    # slots above the 4 GiB offset of a cache of about 4.3 GB: the row address
+    # needs 64-bit arithmetic. The written region against the oracle's encoder
+    # on a compact copy of it, byte for byte.
+    rng = np.random.default_rng(13 if kv_dtype == "bf16" else 14)
+    bs, nb, n = 64, 7, 300
+    row_bytes = 576 * (2 if kv_dtype == "bf16" else 1)
+    base_page = (2 ** 32) // (bs * row_bytes) + 1
+    scale = 1.0 if kv_dtype == "bf16" else 0.0213
+    rows = rows_with_edge_values(rng, n, scale, kv_dtype == "fp8")
+    slots = rng.permutation(nb * bs)[:n].astype(np.int32)
+    dt = np.uint16 if kv_dtype == "bf16" else np.uint8
+    kv0 = rng.integers(0, 1 << (16 if kv_dtype == "bf16" else 8), size=(nb, bs, 576)).astype(dt)
+    ref = orc.kv_append(kv0, rows, slots, scale, kv_dtype)
+
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if kv_dtype == "bf16" else torch.float8_e4m3fn
+    big = torch.empty((base_page + nb, bs, 576), dtype=tdt, device=dev)
+    assert big.numel() * big.element_size() > 2 ** 32
+    big[base_page:] = torch.from_numpy(kv0.view(np.int16) if kv_dtype == "bf16" else kv0).to(dev).view(tdt)
+    r = torch.from_numpy(rows.view(np.int16)).to(dev).view(torch.bfloat16)
+    s = torch.from_numpy(slots + base_page * bs).to(dev)
+    mla.mla_kv_append(r, s, big, scale)
+    torch.cuda.synchronize()
+    got = big[base_page:].view(torch.int16 if kv_dtype == "bf16" else torch.uint8).cpu().numpy().view(dt)
+    np.testing.assert_array_equal(got, ref)
