@@ -449,11 +449,16 @@ __global__ __launch_bounds__(Y_THREADS, 1) void mla_decode_wide128(FwdParams p) 
       for (int e = 0; e < 4; ++e) x[mi][e] = sacc[mi][e];
     // a step that reaches a row's limit, or whose page id was out of range
     if (tile_bad || __builtin_amdgcn_ballot_w64(ts + 32 > limit)) {
+      // bf16: the lane group read afresh, which shortens the tile loop's
+      // schedule (3% at 64 x 128 heads, 1-2k keys); for fp8 the same change
+      // lengthens it (2% at 32 x 4 x 128 rows, 0.5-16k keys), so fp8 keeps
+      // the value held from the prologue
+      const int gk = 4 * (F8 ? g : fresh_lane() >> 4);
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int key = ts + 16 * mi + 4 * g + e;
+          const int key = ts + 16 * mi + gk + e;
           x[mi][e] = key < limit && !tile_bad ? x[mi][e] : -INFINITY;
         }
     }
@@ -578,9 +583,12 @@ __global__ __launch_bounds__(Y_THREADS, 1) void mla_decode_wide128(FwdParams p) 
   }
   // The wave's 16 rows leave in 8 groups of 64 dims; each store covers 8
   // whole rows of a group (whole_row_runs), so every lane takes part in the
-  // exchange and a store goes out only for a row of the sequence.
+  // exchange and a store goes out only for a row of the sequence. Lane
+  // values are derived afresh here, so that nothing computed for the
+  // epilogue is held (and spilled) across the tile loop.
   const float fs = __builtin_ldexpf(inv, kexp);
-  const int r_lo = 16 * w + (c16 & 7), r_hi = r_lo + 8;   // item rows of the two stores
+  const int ln_e = fresh_lane(), c16e = ln_e & 15, ge = ln_e >> 4;
+  const int r_lo = 16 * w + (c16e & 7), r_hi = r_lo + 8;   // item rows of the two stores
   const bool ok_lo = rg * Y_RGS + r_lo < p.rows, ok_hi = rg * Y_RGS + r_hi < p.rows;
   char* dst_lo;
   char* dst_hi;
@@ -592,7 +600,7 @@ __global__ __launch_bounds__(Y_THREADS, 1) void mla_decode_wide128(FwdParams p) 
     dst_lo = reinterpret_cast<char*>(p.part_o + ((size_t)slot * Y_RGS + r_lo) * DV);
     dst_hi = reinterpret_cast<char*>(p.part_o + ((size_t)slot * Y_RGS + r_hi) * DV);
   }
-  const int col = whole_row_col(c16, g);
+  const int col = whole_row_col(c16e, ge);
 #pragma unroll
   for (int k = 0; k < DV / 64; ++k) {
     uint32_t pk[4][2];
@@ -609,17 +617,18 @@ __global__ __launch_bounds__(Y_THREADS, 1) void mla_decode_wide128(FwdParams p) 
       }
     }
     uint4 lo, hi;
-    whole_row_runs(pk, c16, lo, hi);
+    whole_row_runs(pk, c16e, lo, hi);
     if (ok_lo) *reinterpret_cast<uint4*>(dst_lo + 128 * k + col) = lo;
     if (ok_hi) *reinterpret_cast<uint4*>(dst_hi + 128 * k + col) = hi;
   }
-  if (row_ok && g == 0) {
+  const int row_e = rg * Y_RGS + 16 * w + c16e;   // this lane's own row
+  if (row_e < p.rows && ge == 0) {
     const float lse2 = empty ? -INFINITY : m_run + log2f(l_row);
     if (slot < 0) {
-      if (p.lse != nullptr) p.lse[(size_t)b * p.rows + row] = lse2 * LN2;
+      if (p.lse != nullptr) p.lse[(size_t)b * p.rows + row_e] = lse2 * LN2;
     } else {
-      p.part_lse[(size_t)slot * Y_RGS + row_local] = lse2;
-      p.part_scale[(size_t)slot * Y_RGS + row_local] = kexp;
+      p.part_lse[(size_t)slot * Y_RGS + 16 * w + c16e] = lse2;
+      p.part_scale[(size_t)slot * Y_RGS + 16 * w + c16e] = kexp;
     }
   }
 }
