@@ -205,7 +205,7 @@ __global__ __launch_bounds__(Y_THREADS, 1) void mla_decode_wide128(FwdParams p) 
 
   // Slot 0 is requested before q is loaded, so the compiler's own wait for
   // the q loads (it cannot see the DMAs) also covers it; slots 1 and 2 go
-  // out once q is resident.
+  // out behind the q loads (bf16) or once q is converted (fp8).
   if (dma_wave && ntiles > 0) issue(0);
 
   // ---- q operands ----
@@ -223,13 +223,26 @@ __global__ __launch_bounds__(Y_THREADS, 1) void mla_decode_wide128(FwdParams p) 
   float scale_row = p.scale_log2;   // fp8: times 2^-qe
   const uint16_t* qrow = p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * D;
   if constexpr (!F8) {
+    // slots 1 and 2 go out right behind the q loads, so the memory pipe
+    // stays full while q lands; the wait for q then covers them too (in
+    // order), and the first steps find their tiles resident (3 % at 64 x
+    // 128 heads, 1-2k keys). The fp8 path requests them after its q
+    // conversion instead, which overlaps their arrival.
+    uint4 v[18];
+#pragma unroll
+    for (int s = 0; s < 18; ++s) v[s] = load16_masked(qrow + 32 * s + 8 * g, row_ok);
+    __builtin_amdgcn_sched_barrier(0);
+    if (dma_wave) {
+      if (ntiles > 1) issue(1);
+      if (ntiles > 2) issue(2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 18; ++s) {
-      const uint4 v = load16_masked(qrow + 32 * s + 8 * g, row_ok);
       if (s < 16)
-        qb[s < 16 ? s : 0] = __builtin_bit_cast(bf16x8_t, v);
+        qb[s < 16 ? s : 0] = __builtin_bit_cast(bf16x8_t, v[s]);
       else
-        *reinterpret_cast<uint4*>(qw + (s - 16) * 1024 + 16 * lane) = v;
+        *reinterpret_cast<uint4*>(qw + (s - 16) * 1024 + 16 * lane) = v[s];
     }
 #pragma unroll
     for (int s = 0; s < QB; ++s) asm volatile("" ::"v"(qb[s]));
@@ -281,7 +294,7 @@ __global__ __launch_bounds__(Y_THREADS, 1) void mla_decode_wide128(FwdParams p) 
       // per dword: a 256-bit operand would be an x86 register class in the host pass
       for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(q8h[s][i]), "v"(q8l[s][i]));
   }
-  if (dma_wave) {
+  if (F8 && dma_wave) {
     if (ntiles > 1) issue(1);
     if (ntiles > 2) issue(2);
   }
