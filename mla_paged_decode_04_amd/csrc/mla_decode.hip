@@ -597,6 +597,7 @@ struct CombineParams {
 // lse = log2(sum_s 2^lse_s), out = sum_s 2^(lse_s - lse) o_s, where the
 // partial rows hold fp16 values of o_s * 2^k_s with a per-row exponent k_s.
 constexpr int COMBINE_SLICES = DV / 8;   // 64 threads per row
+static_assert(COMBINE_SLICES == 64, "one wave per row: the combine reads the row index as wave-uniform");
 
 __global__ __launch_bounds__(NTHREADS) void mla_combine_kernel(CombineParams p) {
   const int pair = blockIdx.x;
@@ -607,9 +608,11 @@ __global__ __launch_bounds__(NTHREADS) void mla_combine_kernel(CombineParams p) 
     flag_bad_item(p.flags);
     return;
   }
-  const int idx = blockIdx.y * NTHREADS + threadIdx.x;
-  const int rr = idx / COMBINE_SLICES;
-  const int d0 = (idx % COMBINE_SLICES) * 8;
+  // one wave per row: the row index is wave-uniform, so the per-split lse
+  // and exponent loads are scalar (C3 combine 9.8 -> 9.4 us, C4 16.2 -> 15.9)
+  const int rr = __builtin_amdgcn_readfirstlane(blockIdx.y * (NTHREADS / COMBINE_SLICES) +
+                                                (int)(threadIdx.x / COMBINE_SLICES));
+  const int d0 = (threadIdx.x % COMBINE_SLICES) * 8;
   const int b = pair / p.nrg, rg = pair % p.nrg;
   const int grow = rg * p.rgs + rr;
   if (rr >= p.rgs || grow >= p.rows) return;
