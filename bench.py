@@ -474,6 +474,57 @@ def copy_calibration(mib: int = 1024, reps: int = 3):
                                            "bytes_written_per_copy": n * 4, "copies": reps}}))
 
 
+def peaks(reps: int = 5):
+    """Achievable rates on this chip, as context for the roofline fractions
+    (which stay against the published peaks): the MFMA probe for the shapes
+    the kernels use, and torch's device fill and copy over 1 GiB. Times are HIP events around each launch on the launch stream;
+    the median of `reps` after one untimed launch."""
+    import torch
+    import mla_paged_decode_04_amd as mla
+    dev = torch.device("cuda:0")
+    lib = mla.probe_library()
+    published = {mla.PROBE_MFMA_16X16X32_BF16: 2.5e15, mla.PROBE_MFMA_32X32X16_BF16: 2.5e15,
+                 mla.PROBE_MFMA_16X16X128_FP8: 5.0e15}
+    names = {mla.PROBE_MFMA_16X16X32_BF16: "mfma_f32_16x16x32_bf16",
+             mla.PROBE_MFMA_32X32X16_BF16: "mfma_f32_32x32x16_bf16",
+             mla.PROBE_MFMA_16X16X128_FP8: "mfma_scale_f32_16x16x128_f8f6f4"}
+    wgs, iters, x = 1024, 2048, 0.0625
+    out = torch.empty(wgs * mla.PROBE_THREADS, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    res = {"workgroups": wgs, "waves_per_workgroup": 8, "iters": iters}
+    for shape, name in names.items():
+        t = timed(lambda: mla.mla_probe_mfma(shape, wgs, iters, x, out))
+        want = lib.mla_probe_mfma_expected(shape, iters, x)
+        ok = bool(torch.all(out == want).item())
+        flops = lib.mla_probe_mfma_flops(shape, wgs, iters)
+        res[name] = {"tflops": round(flops / t / 1e12, 1), "frac_of_published": round(flops / t / published[shape], 3),
+                     "us": round(t * 1e6, 1), "result_exact": ok}
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    gib = float(n * 4)
+    res["hbm"] = {
+        "fill_gbs": round(gib / timed(lambda: b.fill_(1.0)) / 1e9, 1),
+        "copy_gbs_read_plus_written": round(2 * gib / timed(lambda: b.copy_(a)) / 1e9, 1),
+        "bytes": int(gib), "published_gbs": 8000.0,
+    }
+    return {"peaks": res, "n_gpus": 1, "data": "synthetic"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,6 +538,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the timings with the 256 MB Infinity Cache evicted before each call")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure achievable MFMA and device-memory rates (context)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration)")
     ap.add_argument("--absorb", action="store_true",
@@ -500,6 +553,9 @@ def main():
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.peaks:
+        print(json.dumps(peaks()), flush=True)
         return
     if a.absorb:
         for T, H in ((4096, 128),) if a.only else ((128, 16), (64, 128), (4096, 128)):

@@ -20,6 +20,7 @@ __all__ = ["mla_decode", "mla_decode_plan", "mla_decode_with_plan", "mla_decode_
 D_QK = 576
 D_V = 512
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_decode.so")
+PROBE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_probe.so")
 
 MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP8_E4M3FN = 1
@@ -88,6 +89,44 @@ def library() -> ctypes.CDLL:
     lib.mla_abi_version.restype = i32
     _lib = lib
     return lib
+
+
+_probe_lib: Optional[ctypes.CDLL] = None
+
+PROBE_MFMA_16X16X32_BF16, PROBE_MFMA_32X32X16_BF16, PROBE_MFMA_16X16X128_FP8 = 0, 1, 2
+PROBE_THREADS = 512
+
+
+def probe_library() -> ctypes.CDLL:
+    """Load the in-tree achievable-peak probe (include/mla_probe.h)."""
+    global _probe_lib
+    if _probe_lib is not None:
+        return _probe_lib
+    if not os.path.exists(PROBE_LIB_PATH):
+        raise RuntimeError(
+            f"{PROBE_LIB_PATH} is missing: build it with `python -m mla_paged_decode_04_amd.build`")
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    i32, f32 = ctypes.c_int32, ctypes.c_float
+    lib.mla_probe_mfma_flops.argtypes = [i32, i32, i32]
+    lib.mla_probe_mfma_flops.restype = ctypes.c_double
+    lib.mla_probe_mfma_expected.argtypes = [i32, i32, f32]
+    lib.mla_probe_mfma_expected.restype = ctypes.c_double
+    lib.mla_probe_mfma.argtypes = [i32, i32, i32, f32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mla_probe_mfma.restype = i32
+    _probe_lib = lib
+    return lib
+
+
+def mla_probe_mfma(shape: int, workgroups: int, iters: int, x: float, out: torch.Tensor) -> None:
+    """Launch the MFMA probe on the current torch stream; out is float32 with
+    workgroups * PROBE_THREADS elements on the GPU."""
+    _check(out, "out", torch.float32, 1)
+    if out.numel() < workgroups * PROBE_THREADS:
+        raise ValueError(f"out needs {workgroups * PROBE_THREADS} elements")
+    st = probe_library().mla_probe_mfma(shape, workgroups, iters, float(x), out.data_ptr(),
+                                        torch.cuda.current_stream(out.device).cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"mla_probe_mfma returned {st}")
 
 
 def _status_string(status: int) -> str:

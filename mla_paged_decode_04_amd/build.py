@@ -1,9 +1,10 @@
-"""Build step: compile the HIP sources for gfx950 into an in-tree shared library.
+"""Build step: compile the HIP sources for gfx950 into in-tree shared libraries.
 
     python -m mla_paged_decode_04_amd.build
 
 produces ``mla_paged_decode_04_amd/libmla_decode.so`` (host C ABI + device
-code objects for gfx950). hipcc cross-compiles without a GPU present.
+code objects for gfx950) and ``libmla_probe.so`` (the achievable-peak probe,
+include/mla_probe.h). hipcc cross-compiles without a GPU present.
 """
 from __future__ import annotations
 
@@ -20,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 SRCS = [os.path.join(CSRC, f) for f in ("mla_decode.hip", "mla_narrow.hip", "mla_wide.hip", "mla_wide128.hip", "mla_append.hip",
                                         "mla_absorb.hip")]
 LIB = os.path.join(PKG, "libmla_decode.so")
+PROBE_SRCS = [os.path.join(CSRC, "mla_probe.hip")]
+PROBE_LIB = os.path.join(PKG, "libmla_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -41,17 +44,23 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (expected /opt/rocm/bin/hipcc)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always; a stale build is never reused)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SRCS, "-o", tmp]
+def _compile(srcs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile both libraries (always; a stale build is never reused).
+    Returns the decode library's path."""
+    _compile(SRCS, LIB, verbose)
+    _compile(PROBE_SRCS, PROBE_LIB, verbose)
     return LIB
 
 

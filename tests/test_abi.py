@@ -313,3 +313,44 @@ def test_noalloc_entry_checks_arguments_on_the_host():
     # a forced 64-key split of 128-row items over long contexts needs far more
     # than 64 MiB of partials: refused
     assert call_na(desc(batch=64, num_heads=128, max_blocks_per_seq=256, split_keys=64), s_q=4) == WS_SMALL
+
+
+# ---------------------------------------------------------------------------
+# the achievable-peak probe library (include/mla_probe.h)
+# ---------------------------------------------------------------------------
+
+PROBE_HEADER = os.path.join(ROOT, "include", "mla_probe.h")
+
+
+def test_probe_library_exports_every_declared_function():
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"^\s*[\w\s\*]+?\b(mla_probe_\w+)\s*\(", text, flags=re.M)))
+    assert declared == ["mla_probe_mfma", "mla_probe_mfma_expected", "mla_probe_mfma_flops"]
+    lib = mla.probe_library()
+    for fn in declared:
+        assert hasattr(lib, fn), fn
+
+
+def test_probe_flop_and_result_formulas():
+    lib = mla.probe_library()
+    # workgroups x 8 waves x iters x 8 chains x 2 M N K
+    assert lib.mla_probe_mfma_flops(0, 1024, 2048) == 1024 * 8 * 2048 * 8 * 2 * 16 * 16 * 32
+    assert lib.mla_probe_mfma_flops(1, 3, 5) == 3 * 8 * 5 * 8 * 2 * 32 * 32 * 16
+    assert lib.mla_probe_mfma_flops(2, 1, 1) == 8 * 8 * 2 * 16 * 16 * 128
+    assert lib.mla_probe_mfma_flops(3, 1, 1) == 0 and lib.mla_probe_mfma_flops(0, 0, 1) == 0
+    # per thread: 8 chains x elements per lane x iters x K x x^2 (x = 1/16)
+    assert lib.mla_probe_mfma_expected(0, 16, 0.0625) == 8 * 4 * 16 * 32 / 256
+    assert lib.mla_probe_mfma_expected(1, 16, 0.0625) == 8 * 16 * 16 * 16 / 256
+    assert lib.mla_probe_mfma_expected(2, 16, 0.0625) == 8 * 4 * 16 * 128 / 256
+    assert lib.mla_probe_mfma_expected(-1, 16, 0.0625) == 0
+
+
+@pytest.mark.parametrize("args", [(3, 8, 16), (-1, 8, 16), (0, 0, 16), (0, 8, 0), (0, (1 << 20) + 1, 1),
+                                  (0, 1, (1 << 24) + 1)])
+def test_probe_rejects_bad_arguments_without_launching(args):
+    shape, wgs, iters = args
+    assert mla.probe_library().mla_probe_mfma(shape, wgs, iters, 0.0625, FAKE, None) == 1
+
+
+def test_probe_rejects_null_output():
+    assert mla.probe_library().mla_probe_mfma(0, 8, 16, 0.0625, None, None) == 1
